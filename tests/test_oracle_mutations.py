@@ -1,0 +1,103 @@
+"""The oracle's pins have teeth: plausible mistakes planted in a copy of the
+oracle (on the CPU) must each be caught by at least one pin."""
+import math
+import types
+
+import numpy as np
+import pytest
+
+import oracle.fp2_oracle as ref_mod
+from test_oracle import brute_force, _rand_seq, _torch_sdpa
+
+
+def _mutant(old: str, new: str):
+    import inspect
+    src = inspect.getsource(ref_mod)
+    assert src.count(old) >= 1, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def pin_brute(mod):
+    rng = np.random.default_rng(5)
+    T, n, Hq, Hkv, d, B = 100, 68, 2, 1, 8, 16
+    Q, K, V = _rand_seq(rng, T, n, Hq, Hkv, d)
+    for j in range(-(-T // B)):
+        K[j * B:(j + 1) * B] += rng.standard_normal((1, Hkv, d)) * 0.7
+    res = mod.run_batch([(Q, K, V)], B, 0.1, True)
+    ref, keep_ref = brute_force(Q, K, V, B, 0.1, True)
+    for (g, i), js in keep_ref.items():
+        assert list(np.nonzero(res["keep"][0][g, i])[0]) == js
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+
+
+def pin_dense(mod):
+    rng = np.random.default_rng(3)
+    Q, K, V = _rand_seq(rng, 200, 72, 8, 2, 8)
+    res = mod.run_batch([(Q, K, V)], 32, float("inf"), True)
+    np.testing.assert_allclose(res["out"], _torch_sdpa(Q, K, V), rtol=0, atol=1e-12)
+
+
+def pin_identical_keys(mod):
+    rng = np.random.default_rng(8)
+    B, n, P = 16, 192, 64
+    T = P + n
+    Q, K, V = _rand_seq(rng, T, n, 4, 2, 16)
+    for j in range(-(-T // B)):
+        K[j * B:(j + 1) * B] = rng.standard_normal((1, 2, 16))
+    res = mod.run_batch([(Q, K, V)], B, 0.0, True)
+    np.testing.assert_allclose(res["out"], mod.dense(Q, K, V)[0], rtol=0, atol=1e-12)
+
+
+def pin_tau_zero(mod):
+    rng = np.random.default_rng(13)
+    B, T, n = 16, 320, 256
+    Q, K, V = _rand_seq(rng, T, n, 4, 2, 16)
+    p0 = mod.plan_batch([(Q, K, V)], B, 0.0)
+    for g in range(2):
+        for i in range(n // B):
+            diag = (T - n) // B + i
+            row = p0["s"][0][g, i, :diag + 1]
+            assert set(np.nonzero(p0["keep"][0][g, i])[0]) == {0, diag, int(np.argmax(row))}
+
+
+def pin_prefix(mod):
+    rng = np.random.default_rng(16)
+    Qf, K, V = _rand_seq(rng, 224, 224, 4, 2, 16)
+    full = mod.run_batch([(Qf, K, V)], 32, 0.1, True)
+    part = mod.run_batch([(Qf[96:], K, V)], 32, 0.1, True)
+    np.testing.assert_allclose(part["out"], full["out"][96:], rtol=0, atol=1e-12)
+
+
+PINS = [pin_brute, pin_dense, pin_identical_keys, pin_tau_zero, pin_prefix]
+
+MUTATIONS = [
+    ("surrogate weight 1 instead of B", "* c + logB", "* c"),
+    ("causal mask off by one", "keys[None, :] <= qpos[:, None]", "keys[None, :] < qpos[:, None] + 1 - 1"),
+    ("kept blocks also corrected", "for j in range(1, diag) if not keep[g, i, j]", "for j in range(1, diag) if True"),
+    ("strict threshold", "keep = s >= thr[:, :, None]", "keep = s > thr[:, :, None]"),
+    ("score scale dropped", "full = (q32[:, g, :] @ k32[:, g, :].T) * c", "full = (q32[:, g, :] @ k32[:, g, :].T)"),
+    ("diag ignores prefix in attend", "        diag = P // B + i\n        kept", "        diag = i\n        kept"),
+    ("pooled over tokens only", "out[i] = blk.mean(axis=(0, 2))", "out[i] = blk[:, :, 0].mean(axis=0)"),
+    ("value mean taken from keys", "kbar, vbar = block_means(K, B), block_means(V, B)\n        O, lse",
+     "kbar, vbar = block_means(K, B), block_means(K, B)\n        O, lse"),
+    ("exp base 2", "w = np.exp(L - m)", "w = np.exp2(L - m)"),
+]
+
+
+def test_reference_passes_every_pin():
+    for pin in PINS:
+        pin(ref_mod)
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(name, old, new):
+    mod = _mutant(old, new)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(mod)
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught: {name}"
