@@ -1,0 +1,131 @@
+// C ABI of the library: host-side checks, then kernel launches on the
+// caller's stream.  No allocation, no synchronisation, no state besides the
+// per-thread error text.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "fp2.h"
+#include "fp2_internal.h"
+
+namespace fp2 {
+hipError_t launch_block_stats(const fp2_batch* b, const fp2_kv* kv, const BatchInfo& info,
+                              float* kbar, float* vbar, hipStream_t stream);
+hipError_t launch_plan(const fp2_batch* b, const fp2_q* q, int hkv, const BatchInfo& info,
+                       const float* kbar, float tau, int32_t* row_ptr, int32_t* col_idx,
+                       int32_t* nnz, float* scores, void* workspace, hipStream_t stream);
+hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, const BatchInfo& info,
+                          const int32_t* row_ptr, const int32_t* col_idx, const float* kbar,
+                          const float* vbar, int correction, float softmax_scale, int out_f32,
+                          void* out, void* workspace, hipStream_t stream);
+
+static fp2_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FP2_OK;
+  return fail(FP2_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+}  // namespace fp2
+
+using namespace fp2;
+
+extern "C" {
+
+fp2_status fp2_block_stats(const fp2_batch* batch, const fp2_kv* kv, float* kbar, float* vbar,
+                           void* stream) {
+  BatchInfo info;
+  fp2_status st = check_batch(batch, &info);
+  if (st != FP2_OK) return st;
+  if ((st = check_kv(kv, batch, info)) != FP2_OK) return st;
+  if (info.total_kblocks > 0 && (!kbar || !vbar)) return fail(FP2_ERR_INVALID, "kbar/vbar is NULL");
+  return hip_status(launch_block_stats(batch, kv, info, kbar, vbar, (hipStream_t)stream),
+                    "fp2_block_stats launch");
+}
+
+size_t fp2_plan_workspace_bytes(const fp2_batch* batch, int32_t num_kv_heads) {
+  BatchInfo info;
+  if (check_batch(batch, &info) != FP2_OK || num_kv_heads < 1) return 0;
+  return plan_workspace_bytes(info, num_kv_heads);
+}
+
+int64_t fp2_plan_max_nnz(const fp2_batch* batch, int32_t num_kv_heads) {
+  BatchInfo info;
+  if (check_batch(batch, &info) != FP2_OK || num_kv_heads < 1) return -1;
+  return info.causal_pairs * num_kv_heads;
+}
+
+fp2_status fp2_plan_mask(const fp2_batch* batch, const fp2_q* q, int32_t num_kv_heads,
+                         const float* kbar, float tau, int32_t* row_ptr, int32_t* col_idx,
+                         int64_t col_capacity, int32_t* nnz, float* scores, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  BatchInfo info;
+  fp2_status st = check_batch(batch, &info);
+  if (st != FP2_OK) return st;
+  if ((st = check_q(q, num_kv_heads, info, batch->block)) != FP2_OK) return st;
+  if (std::isnan(tau)) return fail(FP2_ERR_INVALID, "tau is NaN");
+  if (!nnz) return fail(FP2_ERR_INVALID, "nnz is NULL");
+  if (info.total_qblocks > 0) {
+    if (!kbar || !row_ptr || !col_idx) return fail(FP2_ERR_INVALID, "kbar/row_ptr/col_idx is NULL");
+    if (!workspace) return fail(FP2_ERR_INVALID, "workspace is NULL");
+  } else if (!row_ptr) {
+    return fail(FP2_ERR_INVALID, "row_ptr is NULL");
+  }
+  const int64_t need = info.causal_pairs * num_kv_heads;
+  if (col_capacity < need)
+    return fail(FP2_ERR_CAPACITY, "col_capacity " + std::to_string(col_capacity) + " < " +
+                                      std::to_string(need) + " (fp2_plan_max_nnz)");
+  const size_t wneed = plan_workspace_bytes(info, num_kv_heads);
+  if (workspace_bytes < wneed)
+    return fail(FP2_ERR_CAPACITY, "plan workspace " + std::to_string(workspace_bytes) + " < " +
+                                      std::to_string(wneed) + " bytes");
+  hipStream_t s = (hipStream_t)stream;
+  if (info.total_qblocks == 0) {  // empty plan: row_ptr = {0}, nnz = 0
+    hipError_t e = hipMemsetAsync(row_ptr, 0, sizeof(int32_t), s);
+    if (e == hipSuccess) e = hipMemsetAsync(nnz, 0, sizeof(int32_t), s);
+    return hip_status(e, "fp2_plan_mask");
+  }
+  return hip_status(launch_plan(batch, q, num_kv_heads, info, kbar, tau, row_ptr, col_idx, nnz,
+                                scores, workspace, s),
+                    "fp2_plan_mask launch");
+}
+
+size_t fp2_run_workspace_bytes(const fp2_batch* batch, int32_t num_kv_heads, int32_t head_dim) {
+  BatchInfo info;
+  if (check_batch(batch, &info) != FP2_OK || num_kv_heads < 1 || head_dim < 1) return 0;
+  return run_workspace_bytes(info, num_kv_heads, head_dim);
+}
+
+fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv* kv,
+                           const int32_t* row_ptr, const int32_t* col_idx, const float* kbar,
+                           const float* vbar, int32_t mean_correction, float softmax_scale,
+                           fp2_out_dtype out_dtype, void* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  BatchInfo info;
+  fp2_status st = check_batch(batch, &info);
+  if (st != FP2_OK) return st;
+  if ((st = check_kv(kv, batch, info)) != FP2_OK) return st;
+  if ((st = check_q(q, kv->num_kv_heads, info, batch->block)) != FP2_OK) return st;
+  if (q->dtype != kv->dtype) return fail(FP2_ERR_UNSUPPORTED, "q and kv dtypes differ");
+  if (q->head_dim != kv->head_dim) return fail(FP2_ERR_INVALID, "q and kv head_dim differ");
+  if (mean_correction != 0 && mean_correction != 1)
+    return fail(FP2_ERR_INVALID, "mean_correction must be 0 or 1");
+  if (out_dtype != FP2_OUT_BF16 && out_dtype != FP2_OUT_F32)
+    return fail(FP2_ERR_INVALID, "unknown out_dtype");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(FP2_ERR_INVALID, "softmax_scale must be finite and > 0");
+  if (info.total_qblocks == 0) return FP2_OK;
+  if (!row_ptr || !col_idx || !out) return fail(FP2_ERR_INVALID, "row_ptr/col_idx/out is NULL");
+  if (mean_correction) {
+    if (!kbar || !vbar) return fail(FP2_ERR_INVALID, "mean correction needs kbar and vbar");
+    const size_t wneed = run_workspace_bytes(info, kv->num_kv_heads, kv->head_dim);
+    if (!workspace || workspace_bytes < wneed)
+      return fail(FP2_ERR_CAPACITY, "run workspace " + std::to_string(workspace_bytes) + " < " +
+                                        std::to_string(wneed) + " bytes");
+  }
+  return hip_status(launch_prefill(batch, q, kv, info, row_ptr, col_idx, kbar, vbar,
+                                   mean_correction, softmax_scale, out_dtype == FP2_OUT_F32, out, workspace,
+                                   (hipStream_t)stream),
+                    "fp2_prefill_run launch");
+}
+
+const char* fp2_last_error(void) { return fp2::last_error(); }
+
+}  // extern "C"

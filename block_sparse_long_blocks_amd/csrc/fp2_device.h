@@ -1,0 +1,98 @@
+// Device-side helpers for the gfx950 kernels: vector types, MFMA wrappers,
+// conversions, wave/workgroup reductions, batch descriptor lookups.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp2 {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// MFMA: D(32x32 f32) += A(32xK) * B(Kx32).
+// Operand layout (wave64): lane l supplies row (l%32) of A and column (l%32)
+// of B, over K-slice [k0 + (l/32)*K/2, k0 + (l/32+1)*K/2).  Result: lane l
+// holds column l%32, rows 8*(i/4) + 4*(l/32) + (i%4) for i = 0..15.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f16_32x32x16(half8 a, half8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// OCP e4m3 x e4m3, K = 64 (format code 0 = fp8 e4m3 for both operands;
+// E8M0 scale 127 = 1.0, i.e. unscaled).
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ---------------------------------------------------------------------------
+// Conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;  // v_cvt_pk_bf16_f32: round to nearest even
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// two floats -> packed fp16 (round toward zero; exact for values that fp16 holds)
+__device__ __forceinline__ uint32_t pack_f16x2_rtz(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 4 OCP e4m3 bytes -> 4 floats (hardware conversion; gfx950 uses the OCP format)
+__device__ __forceinline__ f32x4 e4m3x4_to_f32(uint32_t w) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// ---------------------------------------------------------------------------
+// Reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// lane l <-> lane l^32
+__device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
+
+// ---------------------------------------------------------------------------
+// Batch descriptors: index of the sequence owning global block `gb`, given
+// the prefix-sum array cu[0..n] (cu[s] <= gb < cu[s+1]).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int n, int gb) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= gb) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace fp2

@@ -1,0 +1,41 @@
+// Host-side internals shared by the C ABI (fp2_api.cpp), the argument checks
+// (fp2_validate.cpp, plain C++ with no HIP dependency) and the kernel
+// launchers (*.hip).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "fp2.h"
+
+namespace fp2 {
+
+// Limits of the kernels (checked on the host; beyond them a call returns
+// FP2_ERR_UNSUPPORTED).
+constexpr int kMaxKBlocks = 16384;   // kept-block bitmask and score row held in LDS
+constexpr int kPoolRowBytes = 4096;  // G*d*elem_size of one token of a KV group
+constexpr int kRowsPerWG = 128;      // packed (head, token) query rows per attention workgroup
+
+// Sizes derived from the host mirrors of a batch.
+struct BatchInfo {
+  int64_t total_q = 0;
+  int64_t total_qblocks = 0;
+  int64_t total_kblocks = 0;
+  int64_t max_kblocks = 0;
+  int64_t causal_pairs = 0;  // sum over query blocks of (diag + 1), one KV head
+};
+
+// Sets the calling thread's error text and returns `st`.
+fp2_status fail(fp2_status st, const std::string& msg);
+const char* last_error();
+
+fp2_status check_batch(const fp2_batch* b, BatchInfo* info);
+fp2_status check_q(const fp2_q* q, int num_kv_heads, const BatchInfo& info, int block);
+fp2_status check_kv(const fp2_kv* kv, const fp2_batch* b, const BatchInfo& info);
+
+size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads);
+size_t run_workspace_bytes(const BatchInfo& info, int num_kv_heads, int head_dim);
+inline int plan_words(const BatchInfo& info) { return int((info.max_kblocks + 31) / 32); }
+
+}  // namespace fp2

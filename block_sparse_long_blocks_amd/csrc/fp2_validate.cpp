@@ -1,0 +1,142 @@
+// Host-only argument checks for the C ABI.  Plain C++: no HIP call is made
+// here, so every rejection happens before anything is enqueued.
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "fp2_internal.h"
+
+namespace fp2 {
+
+namespace {
+thread_local std::string g_err;
+
+std::string S(long long v) { return std::to_string(v); }
+}  // namespace
+
+fp2_status fail(fp2_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+const char* last_error() { return g_err.c_str(); }
+
+fp2_status check_batch(const fp2_batch* b, BatchInfo* info) {
+  if (!b) return fail(FP2_ERR_INVALID, "batch is NULL");
+  if (b->num_seqs < 0) return fail(FP2_ERR_INVALID, "num_seqs < 0");
+  if (b->block != 64 && b->block != 128)
+    return fail(FP2_ERR_UNSUPPORTED, "block must be 64 or 128, got " + S(b->block));
+  if (b->num_seqs > 0) {
+    if (!b->cu_seqlens_q || !b->seqlens_k || !b->cu_qblocks || !b->cu_kblocks)
+      return fail(FP2_ERR_INVALID, "batch device arrays must not be NULL");
+    if (!b->h_cu_seqlens_q || !b->h_seqlens_k)
+      return fail(FP2_ERR_INVALID, "batch host mirrors must not be NULL");
+    if (b->h_cu_seqlens_q[0] != 0) return fail(FP2_ERR_INVALID, "cu_seqlens_q[0] must be 0");
+  }
+  BatchInfo r;
+  const int B = b->block;
+  for (int s = 0; s < b->num_seqs; ++s) {
+    const long long n = (long long)b->h_cu_seqlens_q[s + 1] - b->h_cu_seqlens_q[s];
+    const long long T = b->h_seqlens_k[s];
+    if (n < 0) return fail(FP2_ERR_INVALID, "cu_seqlens_q decreases at sequence " + S(s));
+    if (T < n)
+      return fail(FP2_ERR_INVALID, "sequence " + S(s) + ": seqlens_k (" + S(T) +
+                                       ") < new queries (" + S(n) + ")");
+    const long long P = T - n;
+    if (P % B != 0)
+      return fail(FP2_ERR_UNSUPPORTED, "sequence " + S(s) + ": cached prefix " + S(P) +
+                                           " is not a multiple of block " + S(B));
+    const long long nqb = (n + B - 1) / B, nkb = (T + B - 1) / B;
+    r.total_q += n;
+    r.total_qblocks += nqb;
+    r.total_kblocks += nkb;
+    if (nkb > r.max_kblocks) r.max_kblocks = nkb;
+    // diag(I) = P/B + I  ->  sum_{I<nqb} (P/B + I + 1)
+    r.causal_pairs += nqb * (P / B) + nqb * (nqb + 1) / 2;
+  }
+  if (r.max_kblocks > kMaxKBlocks)
+    return fail(FP2_ERR_UNSUPPORTED, "a sequence has " + S(r.max_kblocks) +
+                                         " KV blocks; at most " + S(kMaxKBlocks) + " supported");
+  if (r.total_q > (1LL << 31) - 1 || r.total_qblocks * 64 > (1LL << 31) - 1)
+    return fail(FP2_ERR_UNSUPPORTED, "batch too large for 32-bit row indices");
+  *info = r;
+  return FP2_OK;
+}
+
+fp2_status check_q(const fp2_q* q, int num_kv_heads, const BatchInfo& info, int block) {
+  if (!q) return fail(FP2_ERR_INVALID, "q is NULL");
+  if (q->dtype != FP2_BF16 && q->dtype != FP2_FP8_E4M3)
+    return fail(FP2_ERR_INVALID, "unknown q dtype " + S(q->dtype));
+  if (q->head_dim != 64 && q->head_dim != 128)
+    return fail(FP2_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got " + S(q->head_dim));
+  if (num_kv_heads < 1) return fail(FP2_ERR_INVALID, "num_kv_heads < 1");
+  if (q->num_q_heads < 1 || q->num_q_heads % num_kv_heads != 0)
+    return fail(FP2_ERR_INVALID, "num_q_heads (" + S(q->num_q_heads) +
+                                     ") must be a positive multiple of num_kv_heads (" +
+                                     S(num_kv_heads) + ")");
+  const int G = q->num_q_heads / num_kv_heads;
+  const int esz = q->dtype == FP2_BF16 ? 2 : 1;
+  if ((long long)G * q->head_dim * esz > kPoolRowBytes)
+    return fail(FP2_ERR_UNSUPPORTED, "query group too wide: G*d*elem = " +
+                                         S((long long)G * q->head_dim * esz) + " bytes > " +
+                                         S(kPoolRowBytes));
+  if ((long long)G * block > (1LL << 20))
+    return fail(FP2_ERR_UNSUPPORTED, "G*block too large");
+  if (info.total_q > 0 && !q->q) return fail(FP2_ERR_INVALID, "q->q is NULL");
+  if (q->dtype == FP2_FP8_E4M3 && info.total_q > 0 && !q->q_scale)
+    return fail(FP2_ERR_INVALID, "e4m3 queries need q_scale");
+  return FP2_OK;
+}
+
+fp2_status check_kv(const fp2_kv* kv, const fp2_batch* b, const BatchInfo& info) {
+  if (!kv) return fail(FP2_ERR_INVALID, "kv is NULL");
+  if (kv->dtype != FP2_BF16 && kv->dtype != FP2_FP8_E4M3)
+    return fail(FP2_ERR_INVALID, "unknown kv dtype " + S(kv->dtype));
+  if (kv->head_dim != 64 && kv->head_dim != 128)
+    return fail(FP2_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got " + S(kv->head_dim));
+  if (kv->num_kv_heads < 1) return fail(FP2_ERR_INVALID, "num_kv_heads < 1");
+  if ((long long)kv->num_kv_heads * kv->head_dim * 2 > (1LL << 20))
+    return fail(FP2_ERR_UNSUPPORTED, "num_kv_heads too large");
+  if (kv->page_size < 1) return fail(FP2_ERR_INVALID, "page_size < 1");
+  if (kv->num_pages < 0 || kv->max_pages_per_seq < 0)
+    return fail(FP2_ERR_INVALID, "negative page counts");
+  if (kv->dtype == FP2_FP8_E4M3 && kv->page_size != b->block)
+    return fail(FP2_ERR_UNSUPPORTED, "e4m3 KV scales are per page: page_size (" +
+                                         S(kv->page_size) + ") must equal block (" +
+                                         S(b->block) + ")");
+  long long need_pages = 0;
+  for (int s = 0; s < b->num_seqs; ++s) {
+    const long long np = ((long long)b->h_seqlens_k[s] + kv->page_size - 1) / kv->page_size;
+    if (np > kv->max_pages_per_seq)
+      return fail(FP2_ERR_INVALID, "sequence " + S(s) + " needs " + S(np) +
+                                       " pages > max_pages_per_seq " + S(kv->max_pages_per_seq));
+    need_pages += np;
+  }
+  (void)need_pages;  // pages may be shared between sequences; no lower bound on num_pages
+  if (info.total_kblocks > 0) {
+    if (!kv->k_pages || !kv->v_pages || !kv->page_table)
+      return fail(FP2_ERR_INVALID, "k_pages, v_pages and page_table must not be NULL");
+    if (kv->dtype == FP2_FP8_E4M3 && (!kv->k_scale || !kv->v_scale))
+      return fail(FP2_ERR_INVALID, "e4m3 KV needs k_scale and v_scale");
+    if (kv->num_pages < 1) return fail(FP2_ERR_INVALID, "num_pages < 1");
+  }
+  return FP2_OK;
+}
+
+size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads) {
+  const size_t rows = (size_t)info.total_qblocks * (size_t)num_kv_heads;
+  if (rows == 0) return 0;
+  const size_t words = (size_t)plan_words(info);
+  size_t bytes = rows * words * 4;     // keep bitmask per row
+  bytes = (bytes + 255) & ~size_t(255);
+  bytes += rows * 4;                   // kept count per row
+  return (bytes + 255) & ~size_t(255);
+}
+
+size_t run_workspace_bytes(const BatchInfo& info, int num_kv_heads, int head_dim) {
+  // bf16 copies of kbar and vbar for the correction tiles
+  const size_t one = (size_t)num_kv_heads * (size_t)info.total_kblocks * (size_t)head_dim * 2;
+  return 2 * ((one + 255) & ~size_t(255));
+}
+
+}  // namespace fp2

@@ -1,0 +1,171 @@
+/*
+ * fp2.h - block-sparse causal GQA prefill attention with mean correction,
+ *         for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "FlashPrefill V2: Block-Sparse Prefill Attention for Long-Context
+ * LLM Serving" (metallab.ai paper page).  Figure 3 gives the two stages:
+ * Stage 1 packs the query heads that share a KV head (PackGQA), pools
+ * block-mean statistics and emits a CSR index of the selected KV blocks per
+ * KV head; Stage 2 runs attention over the selected blocks and folds every
+ * unselected block in through the mean correction of Figure 4, both merged
+ * in one online softmax.  Table 7 fixes the surrounding contract: a CSR
+ * index per KV head, paged KV at any page size, BF16 and FP8.  The abstract
+ * names the selection rule: instantaneous pattern discovery plus max-based
+ * dynamic thresholding.
+ *
+ * Exact definition implemented (B = block size, c = 1/sqrt(d), G = Hq/Hkv):
+ *   kbar_J, vbar_J  mean key / value over the tokens of KV block J
+ *   qbar_I          mean query over the tokens of query block I and the G
+ *                   query heads of one KV head
+ *   s_IJ            float32 (qbar_I . kbar_J) * c, for J <= diag(I)
+ *   keep            s_IJ >= max_J s_IJ - tau, or J == 0, or J == diag(I)
+ *   out             softmax attention over the kept blocks' keys (causal,
+ *                   bottom-right aligned when a prefix is cached), where
+ *                   every skipped J in [1, diag(I)) adds B*exp(q.kbar_J*c - m)
+ *                   to the denominator and the same weight times vbar_J to
+ *                   the numerator.
+ *   diag(I) = P/B + I for a sequence with a cached prefix of P tokens.
+ *
+ * Conventions for every entry point:
+ *  - All device buffers are allocated and owned by the caller.  The library
+ *    never allocates, frees or synchronises; it only enqueues kernels on the
+ *    caller's stream (a hipStream_t passed as void*, NULL = default stream).
+ *    Buffers must stay valid until the stream has passed the work.
+ *  - Arguments are checked on the host before anything is enqueued; on a
+ *    failed check nothing is launched and the status says why
+ *    (fp2_last_error() gives a message, per calling thread).
+ *  - Page ids and device-side descriptor arrays are trusted: out-of-range
+ *    page ids, or device arrays that disagree with their host mirrors, are
+ *    undefined behaviour.
+ *  - Layouts are row-major (C order).  "bf16" is bfloat16; "e4m3" is OCP
+ *    FP8 E4M3 (bias 7, max 448, no infinities).
+ */
+#ifndef FP2_H
+#define FP2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP2_OK = 0,
+  FP2_ERR_INVALID = 1,     /* malformed argument (null pointer, bad size, ...)     */
+  FP2_ERR_UNSUPPORTED = 2, /* well formed but outside what the kernels implement   */
+  FP2_ERR_CAPACITY = 3,    /* an output or workspace buffer is too small           */
+  FP2_ERR_HIP = 4          /* a HIP launch failed; the message holds HIP's text    */
+} fp2_status;
+
+typedef enum { FP2_BF16 = 0, FP2_FP8_E4M3 = 1 } fp2_dtype;
+
+/* Output element type of fp2_prefill_run. */
+typedef enum { FP2_OUT_BF16 = 0, FP2_OUT_F32 = 1 } fp2_out_dtype;
+
+/* A variable-length batch of sequences (continuous batching).  Sequence s
+ * holds seqlens_k[s] key tokens, of which the last n_s =
+ * cu_seqlens_q[s+1]-cu_seqlens_q[s] are new queries; the first
+ * P_s = seqlens_k[s]-n_s are a cached prefix (P_s must be a multiple of
+ * block).  Query blocks and KV blocks are counted per sequence:
+ * cu_qblocks[s+1]-cu_qblocks[s] = ceil(n_s/block),
+ * cu_kblocks[s+1]-cu_kblocks[s] = ceil(seqlens_k[s]/block).
+ * The device arrays and the host mirrors must hold the same values. */
+typedef struct {
+  int32_t num_seqs;              /* >= 0                                         */
+  int32_t block;                 /* B: 64 or 128                                 */
+  const int32_t *cu_seqlens_q;   /* device [num_seqs+1], cu_seqlens_q[0] == 0    */
+  const int32_t *seqlens_k;      /* device [num_seqs]                            */
+  const int32_t *cu_qblocks;     /* device [num_seqs+1]                          */
+  const int32_t *cu_kblocks;     /* device [num_seqs+1]                          */
+  const int32_t *h_cu_seqlens_q; /* host mirror of cu_seqlens_q                  */
+  const int32_t *h_seqlens_k;    /* host mirror of seqlens_k                     */
+} fp2_batch;
+
+/* Queries of the new tokens, packed over the batch: [total_q, Hq, d]. */
+typedef struct {
+  fp2_dtype dtype;
+  int32_t num_q_heads;           /* Hq, a multiple of the KV head count          */
+  int32_t head_dim;              /* d: 64 or 128                                 */
+  const void *q;                 /* device, bf16 or e4m3 [total_q, Hq, d]        */
+  const float *q_scale;          /* e4m3 only: device [total_qblocks, Hq], one
+                                    scale per (query block, head); NULL for bf16 */
+} fp2_q;
+
+/* Paged KV cache.  Token t of sequence s lives in physical page
+ * page_table[s*max_pages_per_seq + t/page_size], slot t%page_size. */
+typedef struct {
+  fp2_dtype dtype;               /* must equal the query dtype                   */
+  int32_t num_kv_heads;          /* Hkv                                          */
+  int32_t head_dim;              /* d, equal to the query head_dim               */
+  int32_t page_size;             /* any size >= 1; e4m3 requires page_size == B  */
+  int32_t num_pages;
+  int32_t max_pages_per_seq;     /* >= ceil(seqlens_k[s]/page_size) for every s  */
+  const void *k_pages;           /* device [num_pages, page_size, Hkv, d]        */
+  const void *v_pages;           /* device [num_pages, page_size, Hkv, d]        */
+  const float *k_scale;          /* e4m3 only: device [num_pages, Hkv]           */
+  const float *v_scale;          /* e4m3 only: device [num_pages, Hkv]           */
+  const int32_t *page_table;     /* device [num_seqs, max_pages_per_seq]         */
+} fp2_kv;
+
+/* Stage 1a - per-block key/value means (Figure 4's pooled statistics).
+ * kbar, vbar: device float32 [Hkv, total_kblocks, d]; entry
+ * [g, cu_kblocks[s]+J, :] is the mean of K (V) over the valid tokens of
+ * block J of sequence s, head g (e4m3 values times their page scale). */
+fp2_status fp2_block_stats(const fp2_batch *batch, const fp2_kv *kv,
+                           float *kbar, float *vbar, void *stream);
+
+/* Workspace bytes fp2_plan_mask needs for this batch (0 if empty). */
+size_t fp2_plan_workspace_bytes(const fp2_batch *batch, int32_t num_kv_heads);
+
+/* Largest possible number of kept entries: the causal (query block, KV
+ * block, KV head) count.  col_capacity must be at least this. */
+int64_t fp2_plan_max_nnz(const fp2_batch *batch, int32_t num_kv_heads);
+
+/* Stage 1b - pattern discovery and max-based thresholding (Figure 3,
+ * abstract), emitting a CSR index per KV head (Table 7).
+ *   kbar       device float32 [Hkv, total_kblocks, d] from fp2_block_stats
+ *   tau        threshold; +INFINITY keeps every causal block (dense), a
+ *              negative value keeps only the forced blocks; NaN is invalid
+ *   row_ptr    device int32 [Hkv*total_qblocks + 1]; row r = g*total_qblocks
+ *              + global query block
+ *   col_idx    device int32 [col_capacity]; KV-block indices within the
+ *              sequence, ascending within each row
+ *   nnz        device int32 [1]: number of entries written
+ *   scores     optional device float32 [Hkv*total_qblocks, max_kblocks]
+ *              (max_kblocks = largest ceil(seqlens_k/B)): the float32 block
+ *              scores, -INFINITY above the diagonal; NULL to skip
+ *   workspace  device scratch of fp2_plan_workspace_bytes() bytes */
+fp2_status fp2_plan_mask(const fp2_batch *batch, const fp2_q *q, int32_t num_kv_heads,
+                         const float *kbar, float tau,
+                         int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
+                         int32_t *nnz, float *scores,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes fp2_prefill_run needs (bf16 copies of kbar and vbar). */
+size_t fp2_run_workspace_bytes(const fp2_batch *batch, int32_t num_kv_heads, int32_t head_dim);
+
+/* Stage 2 - exact attention over the kept blocks plus the mean correction
+ * of every skipped block (Figure 3 exact path, Figure 4 surrogate terms).
+ *   row_ptr, col_idx  the CSR from fp2_plan_mask (any ascending CSR that
+ *                     holds block 0 and the diagonal of every row is valid)
+ *   kbar, vbar        device float32 [Hkv, total_kblocks, d]
+ *   mean_correction   0: skipped blocks are dropped; 1: corrected
+ *   softmax_scale     logit scale, normally 1/sqrt(d)
+ *   out_dtype         FP2_OUT_BF16 (rounded to nearest even) or FP2_OUT_F32
+ *   out               device [total_q, Hq, d] of out_dtype
+ *   workspace         device scratch of fp2_run_workspace_bytes() bytes */
+fp2_status fp2_prefill_run(const fp2_batch *batch, const fp2_q *q, const fp2_kv *kv,
+                           const int32_t *row_ptr, const int32_t *col_idx,
+                           const float *kbar, const float *vbar,
+                           int32_t mean_correction, float softmax_scale,
+                           fp2_out_dtype out_dtype, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char *fp2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP2_H */

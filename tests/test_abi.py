@@ -1,0 +1,117 @@
+"""C-ABI library: loads, exports every function include/fp2.h declares, and
+rejects malformed arguments on the host before any HIP call (these calls
+never reach a kernel, so they run without a GPU)."""
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+lib = pytest.importorskip("block_sparse_long_blocks_amd")
+import torch  # noqa: E402
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fp2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp2_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    import ctypes
+    names = declared_functions()
+    assert len(names) >= 7
+    so = ctypes.CDLL(lib.library_path())
+    for n in names:
+        assert hasattr(so, n), n
+
+
+def _batch(seqlens, nq, block=128):
+    return lib.Batch(block, seqlens, nq, device="cpu")
+
+
+def _kv(hkv=2, d=128, page=128, pages=4, dtype=torch.bfloat16, maxp=4):
+    kp = torch.zeros((pages, page, hkv, d), dtype=dtype)
+    return lib.KVCache(kp, kp.clone(), torch.zeros((1, maxp), dtype=torch.int32))
+
+
+def _q(total, hq=4, d=128, dtype=torch.bfloat16):
+    return lib.Queries(torch.zeros((max(total, 1), hq, d), dtype=dtype))
+
+
+def _expect(code, fn, *args, match=None, **kw):
+    with pytest.raises(lib.Fp2Error) as e:
+        fn(*args, **kw)
+    assert e.value.status == code, str(e.value)
+    if match:
+        assert re.search(match, str(e.value)), str(e.value)
+
+
+def test_sizes_and_counts():
+    b = _batch([1000, 256], [1000, 128])
+    # seq0: 8 q-blocks, diag 0..7 -> 36; seq1: prefix 128 -> P/B = 1, 1 q-block -> 2
+    assert lib.fp2_plan_max_nnz(b, 3) == 3 * (36 + 2)
+    assert lib.fp2_plan_workspace_bytes(b, 3) > 0
+    assert lib.fp2_run_workspace_bytes(b, 3, 128) >= 2 * 3 * (8 + 2) * 128 * 2
+
+
+def test_validation_rejects_before_launch():
+    f32 = torch.zeros(16)
+    i32 = torch.zeros(16, dtype=torch.int32)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    b = _batch([256], [256])
+    # block size
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_block_stats, _batch([256], [256], 32), _kv(), f32, f32,
+            match="block")
+    # prefix not a multiple of block
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_block_stats, _batch([300], [200]), _kv(), f32, f32,
+            match="prefix")
+    # more queries than keys
+    _expect(lib.FP2_ERR_INVALID, lib.fp2_block_stats, _batch([100], [200]), _kv(), f32, f32)
+    # head_dim
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_block_stats, b, _kv(d=96), f32, f32, match="head_dim")
+    # fp8 with page_size != block
+    kv8 = lib.KVCache(torch.zeros((4, 64, 2, 128), dtype=torch.uint8),
+                      torch.zeros((4, 64, 2, 128), dtype=torch.uint8),
+                      torch.zeros((1, 8), dtype=torch.int32), f32, f32)
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_block_stats, b, kv8, f32, f32, match="page_size")
+    # too few pages in the table
+    _expect(lib.FP2_ERR_INVALID, lib.fp2_block_stats, _batch([1024], [1024]), _kv(maxp=4), f32, f32,
+            match="max_pages_per_seq")
+    # GQA: Hq not a multiple of Hkv
+    _expect(lib.FP2_ERR_INVALID, lib.fp2_plan_mask, b, _q(256, hq=3), 2, f32, 1.0, i32, i32, i32, ws)
+    # tau NaN
+    _expect(lib.FP2_ERR_INVALID, lib.fp2_plan_mask, b, _q(256), 2, f32, math.nan, i32, i32, i32, ws,
+            match="NaN")
+    # col capacity below the causal count: 2 q-blocks -> 3 pairs x 2 heads = 6
+    _expect(lib.FP2_ERR_CAPACITY, lib.fp2_plan_mask, b, _q(256), 2, f32, 1.0, i32, i32[:5], i32, ws)
+    # plan workspace too small
+    _expect(lib.FP2_ERR_CAPACITY, lib.fp2_plan_mask, b, _q(256), 2, f32, 1.0, i32, i32, i32, ws[:8])
+    # fp8 queries without scales
+    _expect(lib.FP2_ERR_INVALID, lib.fp2_plan_mask, b, lib.Queries(torch.zeros((256, 4, 128), dtype=torch.uint8)),
+            2, f32, 1.0, i32, i32, i32, ws, match="q_scale")
+    # dtype mismatch between q and kv
+    out = torch.zeros(8)
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_prefill_run, b,
+            lib.Queries(torch.zeros((256, 4, 128), dtype=torch.uint8), f32), _kv(), i32, i32, f32, f32, True,
+            out, ws)
+    # run workspace too small for the correction
+    _expect(lib.FP2_ERR_CAPACITY, lib.fp2_prefill_run, b, _q(256), _kv(), i32, i32, f32, f32, True, out, ws[:4])
+    # bad softmax scale
+    _expect(lib.FP2_ERR_INVALID, lib.fp2_prefill_run, b, _q(256), _kv(), i32, i32, f32, f32, False, out, ws,
+            softmax_scale=-1.0)
+    # group too wide for the pooling pass
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_plan_mask, b, _q(256, hq=64), 2, f32, 1.0, i32, i32, i32, ws)
+
+
+def test_no_fallback_without_library(tmp_path, monkeypatch):
+    """The binding refuses to import when libfp2.so is absent (no CPU path)."""
+    import importlib.util
+    src = os.path.join(ROOT, "block_sparse_long_blocks_amd", "_binding.py")
+    dst = tmp_path / "_binding.py"
+    dst.write_text(open(src).read())
+    spec = importlib.util.spec_from_file_location("binding_copy", str(dst))
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError, match="not built"):
+        spec.loader.exec_module(mod)

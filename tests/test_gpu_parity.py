@@ -1,0 +1,227 @@
+"""GPU parity of the three C-ABI calls against the float64 oracle (small and
+ragged shapes that the oracle finishes in seconds but that span several tiles).
+
+Bar: block means within a rigorous float32 summation bound; kept-block lists
+identical except where the oracle flags a near-tie (score within 1e-5 of the
+row threshold); attention output within 1e-2 (bf16) / 4e-2 (fp8) max-abs of
+the oracle run on the GPU's own mask.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from helpers import compare_csr, csr_well_formed, decoded_seqs, stats_bound
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+TOL = {"bf16": 1e-2, "fp8": 4e-2}
+
+
+def bf16_half_ulp(x):
+    """Half a bfloat16 ulp at |x|: the rounding every bf16 output carries."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 0.5 * 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def check_out(got, ref, tol, out_dtype):
+    """fp32 output: max-abs <= tol.  bf16 output: <= tol plus the output's own
+    half-ulp rounding (which alone exceeds 1e-2 once |O| >= 4)."""
+    err = np.abs(got - ref)
+    bound = tol if out_dtype == "f32" else tol + bf16_half_ulp(ref)
+    bad = err > bound
+    assert np.all(np.isfinite(got))
+    assert not bad.any(), (f"{int(bad.sum())} outputs over the bound; max err {err.max():.5f}, "
+                           f"worst |O| {np.abs(ref[np.unravel_index(np.argmax(err - bound), err.shape)]):.3f}")
+    return float(err.max())
+
+
+def _cfg(name, seqlens, prefixes, hq, hkv, d, B, page, dtype="bf16", structure="band_sinks",
+         shuffle=True, seed=11):
+    return synth.Config(name=name, seqlens=tuple(seqlens), prefixes=tuple(prefixes), hq=hq, hkv=hkv, d=d,
+                        block=B, page_size=page, dtype=dtype, structure=structure, tau=1.0, seed=seed,
+                        shuffle_pages=shuffle)
+
+
+SMALL = {
+    "tiny": synth.CONFIGS["tiny"],
+    "varlen_p64": _cfg("varlen_p64", (640, 300, 1152), (256, 0, 896), 8, 2, 128, 128, 64),
+    "d64_b128_p16": _cfg("d64_b128_p16", (512, 384), (128, 256), 8, 4, 64, 128, 16),
+    "d128_b64_g8": _cfg("d128_b64_g8", (768,), (192,), 16, 2, 128, 64, 32),
+    "single_token": _cfg("single_token", (257, 1), (256, 0), 4, 2, 128, 128, 128, structure="plain"),
+    "fp8_varlen": _cfg("fp8_varlen", (1024, 512), (0, 256), 8, 2, 128, 128, 128, dtype="fp8", shuffle=True),
+}
+TAUS = {"tiny": (0.0, 0.005, 0.01, 0.02, 2.0), "varlen_p64": (0.0, 0.5, 3.0),
+        "d64_b128_p16": (0.3, 3.0), "d128_b64_g8": (0.2, 2.0), "single_token": (0.0, 1.0),
+        "fp8_varlen": (0.0, 0.5, 3.0)}
+
+_cache = {}
+
+
+def workload(name, pad_fill="zero"):
+    key = (name, pad_fill)
+    if key not in _cache:
+        w = synth.make_custom(SMALL[name], tau=1.0, pad_fill=pad_fill)
+        _cache[key] = (w, decoded_seqs(w))
+    return _cache[key]
+
+
+def layer(w, with_scores=False, out_dtype="bf16"):
+    import block_sparse_long_blocks_amd as lib
+    return lib.PrefillLayer(*lib.from_workload(w), with_scores=with_scores,
+                            out_dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_block_stats_parity(name):
+    w, seqs = workload(name)
+    L = layer(w)
+    L.stats()
+    torch.cuda.synchronize()
+    plan = O.plan_batch(seqs, w.cfg.block, 1.0)
+    kb_bound, vb_bound = stats_bound(w, seqs)
+    kb = L.kbar.cpu().numpy().astype(np.float64)
+    vb = L.vbar.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(kb - plan["kbar"]) <= kb_bound)
+    assert np.all(np.abs(vb - plan["vbar"]) <= vb_bound)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_plan_parity(name):
+    w, seqs = workload(name)
+    L = layer(w, with_scores=True)
+    L.stats()
+    for tau in TAUS[name] + (math.inf, -1.0):
+        L.plan(tau)
+        torch.cuda.synchronize()
+        rp, ci = L.csr_host()
+        plan = O.plan_batch(seqs, w.cfg.block, tau)
+        csr_well_formed(rp, ci, w)
+        rows_bad, flips, ties, hard = compare_csr(rp, ci, plan, w)
+        assert hard == 0, f"tau={tau}: {hard} mask flips outside near-ties ({flips} flips, {ties} ties)"
+        assert int(L.nnz.item()) == rp[-1]
+        # float32 scores agree with the oracle's float32 scores to ~ulp level
+        sc = L.scores.cpu().numpy()
+        off = 0
+        for s, S in enumerate(plan["s"]):
+            nqb = S.shape[1]
+            for g in range(w.cfg.hkv):
+                gs = sc[g * w.total_qblocks + off: g * w.total_qblocks + off + nqb, :S.shape[2]]
+                fin = np.isfinite(S[g])
+                assert np.array_equal(np.isfinite(gs), fin)
+                assert np.max(np.abs(gs[fin] - S[g][fin]), initial=0.0) <= 2e-6
+            off += nqb
+        if tau == math.inf:
+            assert rp[-1] == w.causal_pairs()
+        if tau == -1.0:
+            assert rp[-1] == sum(min(2, P // w.cfg.block + i + 1)
+                                 for s in range(w.num_seqs)
+                                 for P in [int(w.seqlens_k[s] - w.n_q[s])]
+                                 for i in range(int(w.cu_qblocks[s + 1] - w.cu_qblocks[s]))) * w.cfg.hkv
+
+
+def _attention_case(name, tau, corr, pad_fill="zero", out_dtype="bf16"):
+    w, seqs = workload(name, pad_fill)
+    L = layer(w, out_dtype=out_dtype)
+    out = L(tau, corr)
+    torch.cuda.synchronize()
+    rp, ci = L.csr_host()
+    nqbs = [int(w.cu_qblocks[s + 1] - w.cu_qblocks[s]) for s in range(w.num_seqs)]
+    nkbs = [-(-int(t) // w.cfg.block) for t in w.seqlens_k]
+    keeps = O.keep_from_csr(rp, ci, w.cfg.hkv, nqbs, nkbs)
+    ref = O.run_batch(seqs, w.cfg.block, tau, corr, keeps=keeps)["out"]
+    got = out[:w.total_q].float().cpu().numpy().astype(np.float64)
+    return got, ref, w, L
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("corr", [True, False])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_attention_parity(name, corr, out_dtype):
+    for tau in TAUS[name]:
+        got, ref, w, _ = _attention_case(name, tau, corr, out_dtype=out_dtype)
+        check_out(got, ref, TOL[w.cfg.dtype], out_dtype)
+
+
+@pytest.mark.parametrize("name", ["tiny", "varlen_p64", "d128_b64_g8"])
+def test_dense_mode_is_causal_attention(name):
+    got, _, w, _ = _attention_case(name, math.inf, True, out_dtype="f32")
+    _, seqs = workload(name)
+    ref = np.concatenate([O.dense(Q, K, V)[0] for Q, K, V in seqs], axis=0)
+    check_out(got, ref, TOL[w.cfg.dtype], "f32")
+
+
+@pytest.mark.parametrize("name", ["varlen_p64", "d64_b128_p16", "fp8_varlen"])
+def test_pad_slots_are_never_read(name):
+    """Unused slots of each last page hold NaN; results must equal the zero-padded run."""
+    got_z, _, w, Lz = _attention_case(name, 0.5, True, "zero")
+    got_n, _, _, Ln = _attention_case(name, 0.5, True, "nan")
+    assert np.all(np.isfinite(got_n))
+    np.testing.assert_array_equal(got_z, got_n)
+    np.testing.assert_array_equal(Lz.kbar.cpu().numpy(), Ln.kbar.cpu().numpy())
+
+
+def test_repeat_runs_bit_identical():
+    w, _ = workload("varlen_p64")
+    L = layer(w)
+    a = L(0.5, True).clone()
+    rp_a, ci_a = L.csr_host()
+    b = L(0.5, True).clone()
+    rp_b, ci_b = L.csr_host()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    np.testing.assert_array_equal(rp_a, rp_b)
+    np.testing.assert_array_equal(ci_a, ci_b)
+
+
+def test_page_shuffle_and_varlen_metamorphic():
+    """Shuffled pages == identity pages (bit-identical); a varlen batch == each sequence alone."""
+    cfg = SMALL["varlen_p64"]
+    import dataclasses
+    w_shuf = synth.make_custom(cfg, tau=0.5)
+    w_id = synth.make_custom(dataclasses.replace(cfg, shuffle_pages=False), tau=0.5)
+    o_shuf = layer(w_shuf)(0.5, True).clone()
+    o_id = layer(w_id)(0.5, True).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(o_shuf, o_id)
+    off = 0
+    for s in range(w_id.num_seqs):
+        one_cfg = dataclasses.replace(cfg, seqlens=(cfg.seqlens[s],), prefixes=(cfg.prefixes[s],),
+                                      shuffle_pages=False)
+        w1 = synth.make_custom(one_cfg, tau=0.5, seq_seeds=(cfg.seed + 1000 * s,))
+        o1 = layer(w1)(0.5, True).clone()
+        torch.cuda.synchronize()
+        n = int(w1.n_q[0])
+        assert torch.equal(o1[:n], o_id[off:off + n])
+        off += n
+
+
+def test_empty_batch_and_empty_sequence():
+    import block_sparse_long_blocks_amd as lib
+    # a batch whose middle sequence has no new queries (prefix only)
+    cfg = _cfg("with_empty", (384, 256, 200), (128, 256, 0), 4, 2, 128, 128, 64)
+    w = synth.make_custom(cfg, tau=0.5)
+    seqs = decoded_seqs(w)
+    L = layer(w)
+    out = L(0.5, True)
+    torch.cuda.synchronize()
+    rp, ci = L.csr_host()
+    nqbs = [int(w.cu_qblocks[s + 1] - w.cu_qblocks[s]) for s in range(w.num_seqs)]
+    nkbs = [-(-int(t) // 128) for t in w.seqlens_k]
+    keeps = O.keep_from_csr(rp, ci, 2, nqbs, nkbs)
+    ref = O.run_batch(seqs, 128, 0.5, True, keeps=keeps)["out"]
+    check_out(out[:w.total_q].float().cpu().numpy().astype(np.float64), ref, 1e-2, "bf16")
+    # an empty batch: every call is a no-op that succeeds
+    b = lib.Batch(128, [], [], device="cuda")
+    q = lib.Queries(torch.zeros((1, 4, 128), dtype=torch.bfloat16, device="cuda"))
+    kv = lib.KVCache(torch.zeros((1, 128, 2, 128), dtype=torch.bfloat16, device="cuda"),
+                     torch.zeros((1, 128, 2, 128), dtype=torch.bfloat16, device="cuda"),
+                     torch.zeros((1, 1), dtype=torch.int32, device="cuda"))
+    Le = lib.PrefillLayer(b, q, kv)
+    Le(1.0, True)
+    torch.cuda.synchronize()
+    assert int(Le.nnz.item()) == 0 and int(Le.row_ptr[0].item()) == 0
