@@ -1,0 +1,267 @@
+"""Benchmark of the block-sparse prefill hot path on one MI355X.
+
+One step = one prefill layer through the three C-ABI calls (fp2_block_stats ->
+fp2_plan_mask -> fp2_prefill_run) on the 128K workload: 1 sequence of 131072
+tokens, 32 query / 8 KV heads, d = 128, block 128, band + 16 sink columns,
+tau set for ~5% kept blocks, mean correction on.  Inputs are resident in HBM
+before timing starts.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+
+value = dense-equivalent TFLOP/s (bf16): the causal dense attention FLOPs of
+the layer (4 * d * Hq * sum over queries of visible keys) divided by the
+measured time of one step.  ms_per_step = ms per layer.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "ms/layer + dense-equiv TFLOP/s at 128K bf16/fp8; % MFMA peak on computed blocks"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--dense-steps", type=int, default=2, help="steps of the same kernel at tau=+inf")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 (e4m3) 128K run")
+    ap.add_argument("--no-dense", action="store_true", help="skip the tau=+inf comparison run")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=96, help="(q-block, KV head) rows timed on the CPU")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def load_taus():
+    return json.load(open(os.path.join(ROOT, "tests", "golden", "tau.json")))
+
+
+def flop_counts(w, nnz):
+    """Dense-equivalent, kept-block and correction FLOPs of one layer.
+
+    dense  : 4*d*Hq * sum over queries of visible keys (exact causal count)
+    kept   : nnz * G*B^2 * 4d   (diagonal tiles counted whole, as issued)
+    corr   : skipped (q-block, KV-block < diag, KV head) * G*B * 4d
+    """
+    cfg = w.cfg
+    d, Hq, B, G = cfg.d, cfg.hq, cfg.block, cfg.hq // cfg.hkv
+    dense = 0
+    skippable = 0  # causal pairs strictly between block 0 and the diagonal
+    for s in range(w.num_seqs):
+        T, n = int(w.seqlens_k[s]), int(w.n_q[s])
+        P = T - n
+        dense += 4 * d * Hq * (n * P + n * (n + 1) // 2)
+        nqb = -(-n // B)
+        for i in range(nqb):
+            skippable += max(0, P // B + i - 1)
+    skippable *= cfg.hkv
+    causal = w.causal_pairs()
+    kept = nnz * G * B * B * 4 * d
+    forced = causal - skippable               # block 0 + diagonal per row (1 when they coincide)
+    skipped = causal - nnz                    # every dropped pair is a skippable one
+    corr = skipped * G * B * 4 * d
+    return dict(dense=dense, kept=kept, corr=corr, causal_pairs=causal, skipped_pairs=skipped,
+                forced_pairs=forced)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("prefill_attn.hip", "fp2_device.h"):
+        h.update(open(os.path.join(ROOT, "block_sparse_long_blocks_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, launch_flops):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs, or
+    None when the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "attn_c128k_bf16_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_digest") != source_digest() or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_workload(name, tau, args, torch, lib, synth):
+    log(f"generating {name} (tau={tau:.6g}) ...")
+    t0 = time.time()
+    w = synth.make(name, tau=tau)
+    log(f"generated in {time.time() - t0:.1f}s; uploading")
+    batch, q, kv = lib.from_workload(w)
+    L = lib.PrefillLayer(batch, q, kv)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        L(tau, True)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
+        L.stats()
+        e[1].record(stream)
+        L.plan(tau)
+        e[2].record(stream)
+        L.attend(True)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    st = [sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps for i in range(3)]
+    step_ms = sum(ev[k][0].elapsed_time(ev[k][3]) for k in range(args.steps)) / args.steps
+    nnz = int(L.nnz.item())
+    fl = flop_counts(w, nnz)
+    res = dict(name=name, tau=tau, ms_per_layer=step_ms, wall_ms_per_layer=wall_ms,
+               stages_ms={"block_stats": st[0], "plan_mask": st[1], "prefill_run": st[2]},
+               nnz=nnz, density=nnz / fl["causal_pairs"], flops=fl)
+    # dense comparison: the same three calls at tau = +inf
+    if not args.no_dense:
+        for _ in range(1):
+            L(math.inf, True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.dense_steps):
+            L(math.inf, True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["dense_ms_per_layer"] = e0.elapsed_time(e1) / args.dense_steps
+        res["speedup_vs_dense"] = res["dense_ms_per_layer"] / step_ms
+        L(tau, True)  # leave the sparse plan in place
+        torch.cuda.synchronize()
+    # HBM-side figures of the two stage-1 kernels (algorithmic bytes)
+    kv_bytes = 2 * w.k_pages.nbytes
+    kbar_bytes = 2 * w.cfg.hkv * w.total_kblocks * w.cfg.d * 4
+    res["stats_gbs"] = (kv_bytes + kbar_bytes) / (st[0] * 1e-3) / 1e9
+    res["plan_gbs"] = (w.q.nbytes + kbar_bytes / 2) / (st[1] * 1e-3) / 1e9
+    del L, batch, q, kv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return w, res
+
+
+def cpu_baseline(w, tau, rows_wanted):
+    """The float64 oracle on a bounded sample of the same workload: stage 1 for the
+    sampled KV heads plus attention of the sampled (q-block, KV head) rows."""
+    import numpy as np
+    import oracle as O
+    cfg = w.cfg
+    B, G, d = cfg.block, cfg.hq // cfg.hkv, cfg.d
+    nqb = int(w.cu_qblocks[1])
+    rng = np.random.default_rng(0)
+    heads = [0, cfg.hkv // 2]
+    per_head = max(1, rows_wanted // len(heads))
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    dense_flops = 0
+    for g in heads:
+        Q = O.decode_bf16(w.q[:, g * G:(g + 1) * G, :]) if cfg.dtype == "bf16" else None
+        K = O.decode_bf16(w.k_seq[0][:, g:g + 1, :])
+        V = O.decode_bf16(w.v_seq[0][:, g:g + 1, :])
+        kbar, vbar = O.block_means(K, B), O.block_means(V, B)
+        qbar = O.pooled_query_means(Q, B, G)
+        s = O.block_scores(qbar, kbar, 0, B, d)
+        keep, _, _ = O.select_blocks(s, 0, B, tau)
+        rows = sorted(set([nqb - 1] + rng.choice(nqb, per_head - 1, replace=False).tolist()))
+        O.attend(Q, K, V, keep, B, True, kbar, vbar, rows=[(0, i) for i in rows])
+        for i in rows:
+            ntok = min(B, Q.shape[0] - i * B)
+            first = i * B
+            dense_flops += 4 * d * G * sum(first + t + 1 for t in range(ntok))
+        del Q, K, V
+    dt = time.perf_counter() - t0
+    return dict(value=dense_flops / dt / 1e12, unit="TFLOP/s (dense-equivalent)", cores=cores,
+                kind="oracle", seconds=dt,
+                sample=f"float64 numpy oracle, c128k_bf16: block means + pooled scores + threshold for "
+                       f"KV heads {heads}, then attention with mean correction for {per_head} query blocks "
+                       f"per head (incl. the last); dense-equivalent FLOPs of the sampled rows / wall time",
+                blas_threads=os.environ.get("OMP_NUM_THREADS", "default"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_long_blocks_amd as lib
+    import synth
+    taus = load_taus()
+    w, bf = run_workload("c128k_bf16", taus["c128k_bf16"]["tau"], args, torch, lib, synth)
+    fl = bf["flops"]
+    t_attn = bf["stages_ms"]["prefill_run"] * 1e-3
+    attn_flops = fl["kept"] + fl["corr"]
+    achieved = attn_flops / t_attn / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    mfma_frac_layer = attn_flops / (bf["ms_per_layer"] * 1e-3) / 1e12 / peak
+    traffic = measured_traffic("c128k_bf16", attn_flops)
+    out = {
+        "metric": METRIC,
+        "value": round(fl["dense"] / (bf["ms_per_layer"] * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s dense-equivalent (bf16, 128K)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(bf["ms_per_layer"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c128k_bf16: 1 seq L=131072, 32 q / 8 kv heads, d=128, block 128, band + 16 "
+                               "sink columns, tau for 5% kept blocks, mean correction on",
+                   "tau": bf["tau"], "density": round(bf["density"], 5), "nnz": bf["nnz"]},
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_d128_kernel<128>", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "flops_per_launch": attn_flops,
+                     "flops_basis": "kept pairs * G*B^2*4d + skipped pairs * G*B*4d"},
+        "stages_ms": {k: round(v, 4) for k, v in bf["stages_ms"].items()},
+        "mfma_frac_computed_layer": round(mfma_frac_layer, 4),
+        "stats_hbm_gbs": round(bf["stats_gbs"], 1),
+        "plan_hbm_gbs": round(bf["plan_gbs"], 1),
+    }
+    if "dense_ms_per_layer" in bf:
+        out["dense_ms_per_layer"] = round(bf["dense_ms_per_layer"], 3)
+        out["speedup_vs_dense"] = round(bf["speedup_vs_dense"], 2)
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample ...")
+        out["cpu_baseline"] = cpu_baseline(w, bf["tau"], args.cpu_rows)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 5)
+    del w
+    if not args.no_fp8:
+        w8, f8 = run_workload("c128k_fp8", taus["c128k_fp8"]["tau"], args, torch, lib, synth)
+        del w8
+        fl8 = f8["flops"]
+        t8 = f8["stages_ms"]["prefill_run"] * 1e-3
+        # QK^T on e4m3 MFMA (5 PF), PV and the correction on fp16/bf16 MFMA (2.5 PF)
+        qk8, pv8 = fl8["kept"] / 2, fl8["kept"] / 2
+        busy = qk8 / (PEAK_TFLOPS["fp8"] * 1e12) + (pv8 + fl8["corr"]) / (PEAK_TFLOPS["bf16"] * 1e12)
+        out["fp8"] = {"ms_per_layer": round(f8["ms_per_layer"], 4),
+                      "dense_equiv_tflops": round(fl8["dense"] / (f8["ms_per_layer"] * 1e-3) / 1e12, 2),
+                      "stages_ms": {k: round(v, 4) for k, v in f8["stages_ms"].items()},
+                      "tau": f8["tau"], "density": round(f8["density"], 5),
+                      "mfma_frac_attn": round(busy / t8, 4)}
+        if "dense_ms_per_layer" in f8:
+            out["fp8"]["dense_ms_per_layer"] = round(f8["dense_ms_per_layer"], 3)
+            out["fp8"]["speedup_vs_dense"] = round(f8["speedup_vs_dense"], 2)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,7 +14,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp2.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["fp2_api.cpp", "fp2_validate.cpp", "block_stats.hip", "plan_mask.hip", "prefill_attn.hip"]
+SOURCES = ["fp2_api.cpp", "fp2_validate.cpp", "block_stats.hip", "plan_mask.hip", "prefill_attn.hip",
+           "attn_bf16_d128.hip"]
 
 COMMON = ["-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{ROOT}/include", f"-I{CSRC}"]
 # gfx950 device code; packed-fp32 instructions are disabled on purpose.

@@ -1,0 +1,41 @@
+// Shared by the two attention kernels: launch arguments and constants.
+#pragma once
+
+#include "fp2_device.h"
+#include "fp2_internal.h"
+
+namespace fp2 {
+
+// The reference max of the online softmax is refreshed only when some lane's
+// max grew by more than kLazy (log2 units); probabilities are otherwise taken
+// against the stale max (at most 2^kLazy), which leaves O / l unchanged.
+constexpr float kLazy = 8.0f;
+
+struct AttnArgs {
+  const int32_t* cu_seqlens_q;
+  const int32_t* seqlens_k;
+  const int32_t* cu_qblocks;
+  const int32_t* cu_kblocks;
+  const int32_t* page_table;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const uint8_t* q;
+  const uint8_t* k_pages;
+  const uint8_t* v_pages;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  const uint16_t* kbar16;  // bf16 [Hkv, total_kblocks, D]
+  const uint16_t* vbar16;  // [Hkv, total_kblocks, D]: fp16 (first kernel) or bf16 (d128 kernel)
+  void* out;               // bf16 or f32 [total_q, Hq, D]
+  float scale_log2;        // softmax_scale * log2(e)
+  float log2_block;        // log2(B): weight B of a mean token
+  PageMap pm;
+  int num_seqs, hq, hkv, max_pages, page_size, total_qblocks, total_kblocks;
+  int correction, slices, rows, out_f32;
+};
+
+
+hipError_t launch_attn_bf16_d128(const AttnArgs& a, int block, hipStream_t stream);
+
+}  // namespace fp2

@@ -57,6 +57,7 @@ struct StatsArgs {
   const float* v_scale;
   float* kbar;
   float* vbar;
+  PageMap pm;
   int num_seqs, max_pages, page_size, hkv, d, block, total_kblocks;
 };
 
@@ -93,8 +94,9 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(StatsArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int pos = J * a.block + tok + u * R;
-          const int64_t page = pt[pos / a.page_size];
-          const int64_t off = ((page * a.page_size + pos % a.page_size) * row_bytes) + c * 16;
+          int pi, slot;
+          a.pm.split(pos, pi, slot);
+          const int64_t off = (((int64_t)pt[pi] * a.page_size + slot) * row_bytes) + c * 16;
           wk[u] = *reinterpret_cast<const uint4*>(a.k_pages + off);
           wv[u] = *reinterpret_cast<const uint4*>(a.v_pages + off);
         }
@@ -106,8 +108,9 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(StatsArgs a) {
       }
       for (; tok < count; tok += R) {
         const int pos = J * a.block + tok;
-        const int64_t page = pt[pos / a.page_size];
-        const int64_t off = ((page * a.page_size + pos % a.page_size) * row_bytes) + c * 16;
+        int pi, slot;
+        a.pm.split(pos, pi, slot);
+        const int64_t off = (((int64_t)pt[pi] * a.page_size + slot) * row_bytes) + c * 16;
         C::add(acck, *reinterpret_cast<const uint4*>(a.k_pages + off));
         C::add(accv, *reinterpret_cast<const uint4*>(a.v_pages + off));
       }
@@ -177,6 +180,7 @@ hipError_t launch_block_stats(const fp2_batch* b, const fp2_kv* kv, const BatchI
   a.num_seqs = b->num_seqs;
   a.max_pages = kv->max_pages_per_seq;
   a.page_size = kv->page_size;
+  a.pm = PageMap::make(kv->page_size);
   a.hkv = kv->num_kv_heads;
   a.d = kv->head_dim;
   a.block = b->block;

@@ -83,6 +83,41 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 __device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
 
 // ---------------------------------------------------------------------------
+// Token position -> (page index within the sequence, slot) for any page size,
+// without an integer division: a shift for powers of two, else a float
+// reciprocal estimate corrected by one step (exact for pos < 2^22; the host
+// caps sequences at 2^21 tokens).
+// ---------------------------------------------------------------------------
+struct PageMap {
+  int ps;      // page size
+  int shift;   // log2(ps) when ps is a power of two, else -1
+  float inv;   // 1.0f / ps
+
+  static PageMap make(int page_size) {
+    PageMap m;
+    m.ps = page_size;
+    m.shift = -1;
+    for (int s = 0; s < 31; ++s)
+      if ((1 << s) == page_size) m.shift = s;
+    m.inv = 1.0f / (float)page_size;
+    return m;
+  }
+  __device__ __forceinline__ void split(int pos, int& page, int& slot) const {
+    if (shift >= 0) {
+      page = pos >> shift;
+      slot = pos & (ps - 1);
+      return;
+    }
+    int q = (int)((float)pos * inv);
+    int r = pos - q * ps;
+    if (r < 0) { --q; r += ps; }
+    else if (r >= ps) { ++q; r -= ps; }
+    page = q;
+    slot = r;
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Batch descriptors: index of the sequence owning global block `gb`, given
 // the prefix-sum array cu[0..n] (cu[s] <= gb < cu[s+1]).
 // ---------------------------------------------------------------------------

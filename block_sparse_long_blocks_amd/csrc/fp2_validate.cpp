@@ -43,6 +43,8 @@ fp2_status check_batch(const fp2_batch* b, BatchInfo* info) {
       return fail(FP2_ERR_INVALID, "sequence " + S(s) + ": seqlens_k (" + S(T) +
                                        ") < new queries (" + S(n) + ")");
     const long long P = T - n;
+    if (T > (1LL << 21))
+      return fail(FP2_ERR_UNSUPPORTED, "sequence " + S(s) + ": " + S(T) + " tokens; at most 2^21 supported");
     if (P % B != 0)
       return fail(FP2_ERR_UNSUPPORTED, "sequence " + S(s) + ": cached prefix " + S(P) +
                                            " is not a multiple of block " + S(B));

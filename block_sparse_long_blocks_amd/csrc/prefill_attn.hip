@@ -28,41 +28,13 @@
 //    and non-causal blocks, through the same MFMA code path.
 //  * fp8: logits carry q_scale * k_scale, and each block's v_scale is folded
 //    into its probabilities before the PV product.
-#include "fp2_device.h"
-#include "fp2_internal.h"
+#include "attn_common.h"
 
 namespace fp2 {
 
 namespace {
 
 constexpr int kThreads = 256;
-// The reference max of the online softmax is refreshed only when some lane's
-// max grew by more than kLazy (log2 units); probabilities are otherwise taken
-// against the stale max (at most 2^kLazy), which leaves O / l unchanged.
-constexpr float kLazy = 8.0f;
-
-struct AttnArgs {
-  const int32_t* cu_seqlens_q;
-  const int32_t* seqlens_k;
-  const int32_t* cu_qblocks;
-  const int32_t* cu_kblocks;
-  const int32_t* page_table;
-  const int32_t* row_ptr;
-  const int32_t* col_idx;
-  const uint8_t* q;
-  const uint8_t* k_pages;
-  const uint8_t* v_pages;
-  const float* q_scale;
-  const float* k_scale;
-  const float* v_scale;
-  const uint16_t* kbar16;  // bf16 [Hkv, total_kblocks, D]
-  const uint16_t* vbar16;  // fp16 [Hkv, total_kblocks, D]
-  void* out;               // bf16 or f32 [total_q, Hq, D]
-  float scale_log2;        // softmax_scale * log2(e)
-  float log2_block;        // log2(B): weight B of a mean token
-  int num_seqs, hq, hkv, max_pages, page_size, total_qblocks, total_kblocks;
-  int correction, slices, rows, out_f32;
-};
 
 // key permutation inside each group of 16 for the V^T tile: the MFMA lane half
 // h consumes keys {4h..4h+3, 8+4h..8+4h+3} of the group as one 16-byte read
@@ -113,9 +85,9 @@ struct Stager {
       const int pos = J * BLK + k;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (pos < T) {
-        const int64_t page = pt[pos / a.page_size];
-        const int64_t off =
-            ((page * a.page_size + pos % a.page_size) * a.hkv + g) * (D * TL::ESZ) + chunk * 16;
+        int pi, slot;
+        a.pm.split(pos, pi, slot);
+        const int64_t off = (((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g) * (D * TL::ESZ) + chunk * 16;
         v = *reinterpret_cast<const uint4*>(a.k_pages + off);
       }
       kreg[p] = v;
@@ -130,9 +102,10 @@ struct Stager {
         const int pos = J * BLK + quad * 4 + r;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (unit < TL::UNITS && pos < T) {
-          const int64_t page = pt[pos / a.page_size];
+          int pi, slot;
+          a.pm.split(pos, pi, slot);
           const int64_t off =
-              ((page * a.page_size + pos % a.page_size) * a.hkv + g) * (D * TL::ESZ) + dchunk * 16;
+              (((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g) * (D * TL::ESZ) + dchunk * 16;
           v = *reinterpret_cast<const uint4*>(a.v_pages + off);
         }
         vreg[u][r] = v;
@@ -551,20 +524,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 }
 
 // Operand copies of the block means for the correction tiles: kbar as bf16
-// (the QK^T operand type), vbar as fp16 (the PV operand type), both rounded
-// to nearest even.
+// (the QK^T operand type); vbar as fp16 (PV operand type of the first kernel)
+// or bf16 (d128 kernel), all rounded to nearest even.
 __global__ __launch_bounds__(256) void means_to_mma_kernel(const float* __restrict__ kbar,
                                                            const float* __restrict__ vbar,
                                                            uint16_t* __restrict__ k16,
-                                                           uint16_t* __restrict__ v16, int64_t n4) {
+                                                           uint16_t* __restrict__ v16, int64_t n4,
+                                                           int v_bf16) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   const f32x4 k = reinterpret_cast<const f32x4*>(kbar)[i];
   const f32x4 v = reinterpret_cast<const f32x4*>(vbar)[i];
   reinterpret_cast<uint2*>(k16)[i] = make_uint2(pack_bf16x2(k[0], k[1]), pack_bf16x2(k[2], k[3]));
-  _Float16 hv[4] = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
   uint2 bits;
-  __builtin_memcpy(&bits, hv, sizeof(bits));
+  if (v_bf16) {
+    bits = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  } else {
+    _Float16 hv[4] = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    __builtin_memcpy(&bits, hv, sizeof(bits));
+  }
   reinterpret_cast<uint2*>(v16)[i] = bits;
 }
 
@@ -593,10 +571,11 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   const size_t one = (((size_t)hkv * info.total_kblocks * D * 2) + 255) & ~size_t(255);
   uint16_t* k16 = static_cast<uint16_t*>(workspace);
   uint16_t* v16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + one);
+  const bool d128_kernel = q->dtype == FP2_BF16 && D == 128;
   if (correction) {
     const int64_t n4 = (int64_t)hkv * info.total_kblocks * D / 4;
     hipLaunchKernelGGL(means_to_mma_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                       kbar, vbar, k16, v16, n4);
+                       kbar, vbar, k16, v16, n4, d128_kernel ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -625,6 +604,7 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.hkv = hkv;
   a.max_pages = kv->max_pages_per_seq;
   a.page_size = kv->page_size;
+  a.pm = PageMap::make(kv->page_size);
   a.total_qblocks = (int)info.total_qblocks;
   a.total_kblocks = (int)info.total_kblocks;
   a.correction = correction;
@@ -632,6 +612,7 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.slices = (G * BLK + kRowsPerWG - 1) / kRowsPerWG;
   a.rows = (int)(info.total_qblocks * hkv);
   const unsigned grid = (unsigned)(((a.rows + 7) / 8) * 8 * a.slices);
+  if (d128_kernel) return launch_attn_bf16_d128(a, BLK, stream);
   if (q->dtype == FP2_FP8_E4M3) return launch_attn_dt<true>(D, BLK, a, grid, stream);
   return launch_attn_dt<false>(D, BLK, a, grid, stream);
 }
