@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the tau=+inf comparison run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=96, help="(q-block, KV head) rows timed on the CPU")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -260,6 +262,14 @@ def main():
         if "dense_ms_per_layer" in f8:
             out["fp8"]["dense_ms_per_layer"] = round(f8["dense_ms_per_layer"], 3)
             out["fp8"]["speedup_vs_dense"] = round(f8["speedup_vs_dense"], 2)
+    if args.copy_calibration:
+        # an elementwise kernel that reads and writes exactly 1 GiB each
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = 1 << 30
     print(json.dumps(out), flush=True)
 
 

@@ -38,6 +38,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;   // 512
 constexpr int kWGRows = 32 * kWaves;    // packed query rows per workgroup
 constexpr int kD = 128;
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left unconstrained
+// (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kRowBytes = kD * 2;       // one bf16 row of K or V in global memory
 constexpr int kKS = kRowBytes + 16;     // LDS row stride of the K tile (bytes)
 constexpr int kVS = kRowBytes + 32;     // LDS row stride of the V tile (bytes)
@@ -55,18 +58,32 @@ struct Stage {
   static constexpr int NLD = BLK * (kD / 8) / kThreads;  // chunks per thread per tile
   uint4 k[NLD], v[NLD];
 
-  __device__ __forceinline__ void load_exact(const AttnArgs& a, const int32_t* pt, int g, int T, int J,
-                                             int t) {
+  int pg[NLD];  // physical page of each staged row of the tile two ahead (-1: past the end)
+
+  // Page-table entries of this thread's rows of exact block J (issued a full
+  // tile ahead of the K/V loads that use them).
+  __device__ __forceinline__ void fetch_pages(const AttnArgs& a, const int32_t* pt, int T, int J, int t) {
+#pragma unroll
+    for (int p = 0; p < NLD; ++p) {
+      const int row = (t + kThreads * p) >> 4;
+      const int pos = J * BLK + row;
+      int pi, slot;
+      a.pm.split(pos, pi, slot);
+      pg[p] = pos < T ? pt[pi] : -1;
+    }
+  }
+
+  // K/V rows of exact block J at the pages fetched by fetch_pages.
+  __device__ __forceinline__ void load_exact(const AttnArgs& a, int g, int J, int t) {
 #pragma unroll
     for (int p = 0; p < NLD; ++p) {
       const int ch = t + kThreads * p;
       const int row = ch >> 4, c = ch & 15;
-      const int pos = J * BLK + row;
       uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
-      if (pos < T) {
+      if (pg[p] >= 0) {
         int pi, slot;
-        a.pm.split(pos, pi, slot);
-        const int64_t off = (((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g) * kRowBytes + c * 16;
+        a.pm.split(J * BLK + row, pi, slot);
+        const int64_t off = (((int64_t)pg[p] * a.page_size + slot) * a.hkv + g) * kRowBytes + c * 16;
         kv = *reinterpret_cast<const uint4*>(a.k_pages + off);
         vv = *reinterpret_cast<const uint4*>(a.v_pages + off);
       }
@@ -132,15 +149,24 @@ struct Wave {
     const uint8_t* vbase = Vb + (4 * hf + (i16 >> 2)) * kVS + (go + 4 * (i16 & 3)) * 2;
 #pragma nounroll
     for (int sub = 0; sub < BLK / 64; ++sub) {
-      f32x16 s[2];
+      // S^T for 64 keys: two independent accumulator chains, alternated, with the
+      // K operand reads issued four MFMAs ahead
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s[st] = f32x16{};
-        const uint8_t* kr = kbase + (64 * sub + 32 * st) * kKS;
+      for (int kk = 0; kk < kD / 16; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < kD / 16; ++kk)
-          s[st] = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(kr + 32 * kk), qf[kk], s[st]);
+        for (int st = 0; st < 2; ++st)
+          s[st] = mfma_bf16_32x32x16(
+              *reinterpret_cast<const bf16x8*>(kbase + (64 * sub + 32 * st) * kKS + 32 * kk), qf[kk], s[st]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
       if (mode == 1) {
 #pragma unroll
         for (int st = 0; st < 2; ++st)
@@ -157,12 +183,13 @@ struct Wave {
             if (!((w >> (8 * (i >> 2) + (i & 3))) & 1u)) s[st][i] = -INFINITY;
         }
       }
-      float mx = -INFINITY;
+      float sv[32];
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
-      mx = fmaxf(mx, swap_halves(mx));
+      for (int i = 0; i < 16; ++i) {
+        sv[i] = s[0][i];
+        sv[16 + i] = s[1][i];
+      }
+      const float mx = max_halves(tree_max<32>(sv));
       const float mxs = mx * scl + bias;  // scl > 0; -inf stays -inf
       if (__any(mxs > m + kLazy)) {       // wave-uniform refresh of the reference max
         const float mnew = fmaxf(m, mxs);
@@ -175,7 +202,7 @@ struct Wave {
           for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
       }
       const float nb = bias - (m == -INFINITY ? 0.f : m);
-      float rs = 0.f;
+      float pv[32];
       bf16x8 pf[2][2];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
@@ -184,16 +211,19 @@ struct Wave {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * r + j], scl, nb));
-            rs += p;
+            pv[16 * st + 8 * r + j] = p;
             pf[st][r][j] = (__bf16)p;
           }
-      l += rs;
+      l += tree_sum<32>(pv);
+      // O^T += V^T P^T: four independent chains (dt), alternated, with the
+      // transposing V reads (two per MFMA) issued four MFMAs ahead
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt) {
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
-          for (int r = 0; r < 2; ++r) {
+          for (int dt = 0; dt < kD / 32; ++dt) {
             const uint8_t* vr = vbase + (64 * sub + 32 * st + 16 * r) * kVS + 64 * dt;
             const i16x4 v0 = ds_read_tr16(vr);
             const i16x4 v1 = ds_read_tr16(vr + 8 * kVS);
@@ -202,7 +232,14 @@ struct Wave {
             __builtin_memcpy(&va, vv, sizeof(va));
             o[dt] = mfma_bf16_32x32x16(va, pf[st][r], o[dt]);
           }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 };
@@ -249,7 +286,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   const int tq = prow % BLK + (lane & 31);
   const bool q_valid = wave_active && (I * BLK + tq < n);
 
-  const int kbeg = a.row_ptr[row], kend = a.row_ptr[row + 1];
+  // uniform values: later loads indexed by them become scalar loads, which
+  // do not share the vector-memory counter with the tile prefetch
+  const int kbeg = ld_uniform(a.row_ptr, row);
+  const int kend = ld_uniform(a.row_ptr, row + 1);
   const int nexact = kend - kbeg;
 
   // ---- mean-token tiles that hold at least one skipped block
@@ -297,37 +337,64 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
       if (q_valid) v = *reinterpret_cast<const uint4*>(qrow + (16 * kk + 8 * hf) * 2);
       ws.qf[kk] = __builtin_bit_cast(bf16x8, v);
     }
+    // Complete the query loads here: otherwise the compiler's wait for them lands
+    // inside the tile loop, where it would also wait for the next tile's prefetch.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
 
+  // Tile pipeline: at iteration i the LDS buffer i%2 holds tile i, the
+  // staging registers hold tile i+1 (in flight), the page entries of tile
+  // i+2 are in flight, and the block indices of tiles i..i+3 sit in uniform
+  // registers.  No step of an iteration waits on a global load issued in the
+  // same iteration, so global latency overlaps a full tile of compute.
   Stage<BLK> stg;
-  auto load = [&](int idx) {
-    if (idx < nexact) stg.load_exact(a, pt, g, T, a.col_idx[kbeg + idx], t);
-    else stg.load_mean(a, mrow0, mtile[idx - nexact], diag, t);
+  auto block_of = [&](int idx) -> int {  // first block (KV block or mean token) of tile idx
+    if (idx >= ntiles) return 0;
+    if (idx < nexact) return ld_uniform(a.col_idx, kbeg + idx);
+    return mtile[idx - nexact];
+  };
+  auto stage = [&](int idx, int j) {  // global -> staging registers
+    if (idx < nexact) stg.load_exact(a, g, j, t);
+    else stg.load_mean(a, mrow0, j, diag, t);
+  };
+  auto pages = [&](int idx, int j) {
+    if (idx < nexact) stg.fetch_pages(a, pt, T, j, t);
   };
 
+  int j0 = block_of(0), j1 = block_of(1), j2 = block_of(2), j3 = block_of(3);
   if (ntiles > 0) {
-    load(0);
+    pages(0, j0);
+    stage(0, j0);
     stg.commit(Kb[0], Vb[0], t);
   }
-  if (ntiles > 1) load(1);
+  if (ntiles > 1) {
+    pages(1, j1);
+    stage(1, j1);
+  }
+  if (ntiles > 2) pages(2, j2);
   __syncthreads();
   const float scl = a.scale_log2;
   for (int idx = 0; idx < ntiles; ++idx) {
     const int cur = idx & 1;
+    const int j4 = block_of(idx + 4);
     if (wave_active) {
       const bool exact = idx < nexact;
-      const int mode = exact ? (a.col_idx[kbeg + idx] == diag ? 1 : 0) : 2;
-      ws.tile(mode, Kb[cur], Vb[cur], lane, scl, exact ? 0.f : a.log2_block, tq,
-              exact ? 0 : mtile[idx - nexact], diag, kept);
+      const int mode = exact ? (j0 == diag ? 1 : 0) : 2;
+      ws.tile(mode, Kb[cur], Vb[cur], lane, scl, exact ? 0.f : a.log2_block, tq, exact ? 0 : j0, diag, kept);
     }
     if (idx + 1 < ntiles) stg.commit(Kb[cur ^ 1], Vb[cur ^ 1], t);
-    if (idx + 2 < ntiles) load(idx + 2);
+    if (idx + 2 < ntiles) stage(idx + 2, j2);
+    if (idx + 3 < ntiles) pages(idx + 3, j3);
+    j0 = j1;
+    j1 = j2;
+    j2 = j3;
+    j3 = j4;
     __syncthreads();
   }
 
   // ---- epilogue: O / l
   if (q_valid) {
-    const float inv = 1.0f / (ws.l + swap_halves(ws.l));
+    const float inv = 1.0f / sum_halves(ws.l);
     const int64_t obase = ((int64_t)(q0 + I * BLK + tq) * a.hq + h) * kD;
     if (a.out_f32) {
       float* orow = static_cast<float*>(a.out) + obase;

@@ -79,8 +79,32 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 
-// lane l <-> lane l^32
+// Combine the values of lanes l and l^32 (the two halves of a score column).
+// v_permlane32_swap returns {v[l % 32], v[l % 32 + 32]} in either order, so a
+// symmetric combine of the pair is the same for both halves (checked on gfx950).
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// lane l <-> lane l^32 (cross-lane crossbar; used where only the partner's value is wanted)
 __device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
+
+// Tree reductions over N register values (N a power of two): depth log2(N)
+// instead of a serial chain.
+template <int N>
+__device__ __forceinline__ float tree_max(const float* x) {
+  if constexpr (N == 1) return x[0];
+  else return fmaxf(tree_max<N / 2>(x), tree_max<N / 2>(x + N / 2));
+}
+template <int N>
+__device__ __forceinline__ float tree_sum(const float* x) {
+  if constexpr (N == 1) return x[0];
+  else return tree_sum<N / 2>(x) + tree_sum<N / 2>(x + N / 2);
+}
 
 // ---------------------------------------------------------------------------
 // Token position -> (page index within the sequence, slot) for any page size,
@@ -116,6 +140,13 @@ struct PageMap {
     slot = r;
   }
 };
+
+// Load of a value that is uniform across the wave and read-only for the whole
+// kernel, through the scalar memory path (constant address space): it does
+// not share the vector-memory counter with in-flight vector loads.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)(p))[i];
+}
 
 // ---------------------------------------------------------------------------
 // Batch descriptors: index of the sequence owning global block `gb`, given
