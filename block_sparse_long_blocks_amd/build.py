@@ -20,11 +20,14 @@ SOURCES = ["fp2_api.cpp", "fp2_validate.cpp", "block_stats.hip", "plan_mask.hip"
 COMMON = ["-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{ROOT}/include", f"-I{CSRC}"]
 # gfx950 device code; packed-fp32 instructions are disabled on purpose.
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The bf16 attention kernel never produces a NaN (padding is staged as zeros,
+# masks are -inf), so its max reductions need no NaN quieting.
+EXTRA = {"attn_bf16_d128.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src, opt):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, opt, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, *EXTRA.get(src, []), opt, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -1,6 +1,6 @@
-// Stage 2 for bf16 inputs with head_dim 128: block-sparse causal GQA attention
-// over the kept KV blocks plus the mean correction of every skipped block, in
-// one online softmax.
+// Stage 2 for bf16 inputs with head_dim 128 and block 128: block-sparse
+// causal GQA attention over the kept KV blocks plus the mean correction of
+// every skipped block, in one online softmax.
 //
 // FlashPrefill V2 (metallab.ai paper page): Figure 3 (exact path over the
 // CSR-selected blocks, correction path merged in the online softmax),
@@ -11,113 +11,167 @@
 //  * One workgroup = 8 waves = 256 packed query rows of one CSR row (the G
 //    query heads of a KV head times B tokens); each wave owns 32 tokens of one
 //    head, so every K/V tile staged in LDS feeds 256 query rows.
-//  * Tiles (kept KV blocks, then mean-token tiles) stream through two LDS
-//    buffers: the next tile's global loads are in flight in registers while
-//    the current tile is computed, and one barrier per tile separates them.
-//  * K and V tiles are stored row-major with padded rows (K 272 bytes, V 288
-//    bytes per 256-byte row).  The padding makes the three access patterns
-//    free of LDS bank conflicts (the staging writes, the QK^T operand reads of
-//    16 rows x one 16-byte chunk, the transposing PV operand reads of
-//    ds_read_tr16_b64 over 4 rows x 2 chunks) while every address stays one
-//    per-lane base plus an immediate offset.
-//  * S^T = K Q^T on the bf16 32x32x16 MFMA: a lane holds the keys of one query,
-//    so row max / row sum are in-lane plus one lane^32 exchange.  O^T = V^T P^T
-//    on the same MFMA takes P straight from the score registers (as bf16) and
-//    V^T through ds_read_tr16_b64 from the row-major V tile, so V is never
-//    transposed in staging.
-//  * The logit scale is folded into the exponent's FMA; masks are applied only
-//    on the diagonal block (causal) and on mean-token tiles (kept, block 0 and
-//    non-causal mean tokens); the reference max is refreshed lazily.
+//  * V is first transposed into V^T tiles (one 128 d x 128 key tile per KV
+//    block and head, keys in the order the PV MFMA consumes them), and the
+//    vbar of the mean tokens likewise; kbar is rounded to bf16 rows.
+//  * Tiles stream global -> LDS by DMA (global_load_lds, 16 bytes a lane)
+//    into two LDS buffers: the next tile's DMA runs while the current tile is
+//    computed; one barrier per tile.  No staging registers, no LDS writes
+//    from the waves.
+//  * K tiles (rows = keys) and V^T tiles (rows = d) share one LDS layout:
+//    256-byte rows in groups of four (one 1 KB DMA unit), groups 1088 bytes
+//    apart, 16-byte chunk k of row r in slot k ^ (r & 3).  Every operand read
+//    is a conflict-free ds_read_b128 at one of two per-lane bases plus an
+//    immediate offset.
+//  * S^T = K Q^T on the bf16 32x32x16 MFMA (a lane holds the keys of one
+//    query, so row max / row sum are in-lane plus one lane^32 exchange);
+//    O^T = V^T P^T on the same MFMA with P straight from the score registers.
+//  * Each tile runs in 32-key steps, software-pipelined: one scheduling
+//    region holds the QK^T MFMAs of step j+1, the PV MFMAs of step j-1 and
+//    the softmax of step j, so matrix cores, LDS and vector ALU overlap
+//    within a wave.  Masks enter as the score accumulator's initial value;
+//    the reference max is refreshed lazily.
 #include "attn_common.h"
 
 namespace fp2 {
 
 namespace {
 
+constexpr int kBlk = 128;
+constexpr int kD = 128;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;   // 512
 constexpr int kWGRows = 32 * kWaves;    // packed query rows per workgroup
-constexpr int kD = 128;
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left unconstrained
 // (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int kWaitVmcnt0 = 0x0F70;
-constexpr int kRowBytes = kD * 2;       // one bf16 row of K or V in global memory
-constexpr int kKS = kRowBytes + 16;     // LDS row stride of the K tile (bytes)
-constexpr int kVS = kRowBytes + 32;     // LDS row stride of the V tile (bytes)
+// buffer resource word 3 for raw (untyped, unswizzled) 32-bit buffer loads on gfx9
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kRowBytes = kD * 2;            // a K row (d values) or a V^T row (128 keys), bf16
+constexpr int kGS = 4 * kRowBytes + 64;      // LDS stride of a 4-row group
+constexpr int kTileLds = (kBlk / 4) * kGS;   // one K or V^T tile in LDS
+constexpr int kTileGlobal = kBlk * kRowBytes;  // one V^T tile in global memory
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ __forceinline__ i16x4 ds_read_tr16(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+// Position p of a V^T row holds key key_of_pos(p): within each group of 16,
+// positions 0-7 hold keys {0-3, 8-11} and positions 8-15 keys {4-7, 12-15},
+// the keys that lane half 0 resp. 1 of a score accumulator holds.
+__device__ __forceinline__ constexpr int key_of_pos(int p) {
+  return (p & ~15) + 4 * ((p >> 3) & 1) + (p & 3) + 8 * ((p >> 2) & 1);
 }
 
-// Register staging of one K tile and one V tile (BLK rows x 16 chunks each).
-template <int BLK>
-struct Stage {
-  static constexpr int NLD = BLK * (kD / 8) / kThreads;  // chunks per thread per tile
-  uint4 k[NLD], v[NLD];
+// ---------------------------------------------------------------------------
+// Operand preparation
+// ---------------------------------------------------------------------------
+struct PrepArgs {
+  const int32_t* cu_kblocks;
+  const int32_t* seqlens_k;
+  const int32_t* page_table;
+  const uint8_t* v_pages;
+  const float* kbar;
+  const float* vbar;
+  uint16_t* kbar16;  // bf16 [Hkv, total_kblocks, D]
+  uint8_t* vt;       // V^T tiles [Hkv, total_kblocks]
+  uint8_t* vbt;      // vbar^T tiles [Hkv, mt_cap]
+  PageMap pm;
+  int num_seqs, hkv, max_pages, page_size, total_kblocks, mt_cap;
+};
 
-  int pg[NLD];  // physical page of each staged row of the tile two ahead (-1: past the end)
-
-  // Page-table entries of this thread's rows of exact block J (issued a full
-  // tile ahead of the K/V loads that use them).
-  __device__ __forceinline__ void fetch_pages(const AttnArgs& a, const int32_t* pt, int T, int J, int t) {
+// 8x8 transpose of 16-bit elements: in[e] is row e (word q = elements 2q, 2q+1);
+// out[e] receives element e of every input row.
+__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
 #pragma unroll
-    for (int p = 0; p < NLD; ++p) {
-      const int row = (t + kThreads * p) >> 4;
-      const int pos = J * BLK + row;
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t w[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint4 v = in[r];
+      w[r] = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+    }
+    out[e] = make_uint4(__builtin_amdgcn_perm(w[1], w[0], sel), __builtin_amdgcn_perm(w[3], w[2], sel),
+                        __builtin_amdgcn_perm(w[5], w[4], sel), __builtin_amdgcn_perm(w[7], w[6], sel));
+  }
+}
+
+// One V^T tile per (KV block, head): thread t moves the 8 keys at positions
+// 8(t/16) .. +7 for the 8 d values of chunk t%16.  Keys past the sequence end
+// are zero.
+__global__ __launch_bounds__(256) void vt_exact_kernel(PrepArgs a) {
+  const int kb = blockIdx.x, g = blockIdx.y;
+  const int s = find_seq(a.cu_kblocks, a.num_seqs, kb);
+  const int J = kb - a.cu_kblocks[s];
+  const int T = a.seqlens_k[s];
+  const int32_t* pt = a.page_table + (int64_t)s * a.max_pages;
+  const int t = threadIdx.x, c = t >> 4, dc = t & 15;
+  uint4 in[8], out[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int pos = J * kBlk + key_of_pos(8 * c + e);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (pos < T) {
       int pi, slot;
       a.pm.split(pos, pi, slot);
-      pg[p] = pos < T ? pt[pi] : -1;
+      v = *reinterpret_cast<const uint4*>(a.v_pages + (((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g) * kRowBytes +
+                                          dc * 16);
     }
+    in[e] = v;
   }
-
-  // K/V rows of exact block J at the pages fetched by fetch_pages.
-  __device__ __forceinline__ void load_exact(const AttnArgs& a, int g, int J, int t) {
+  transpose8x8(in, out);
+  uint8_t* dst = a.vt + ((int64_t)g * a.total_kblocks + kb) * kTileGlobal + c * 16;
 #pragma unroll
-    for (int p = 0; p < NLD; ++p) {
-      const int ch = t + kThreads * p;
-      const int row = ch >> 4, c = ch & 15;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
-      if (pg[p] >= 0) {
-        int pi, slot;
-        a.pm.split(J * BLK + row, pi, slot);
-        const int64_t off = (((int64_t)pg[p] * a.page_size + slot) * a.hkv + g) * kRowBytes + c * 16;
-        kv = *reinterpret_cast<const uint4*>(a.k_pages + off);
-        vv = *reinterpret_cast<const uint4*>(a.v_pages + off);
-      }
-      k[p] = kv;
-      v[p] = vv;
-    }
-  }
+  for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dst + (8 * dc + e) * kRowBytes) = out[e];
+}
 
-  // mean tokens J0 + row (rows at or past jend are zero)
-  __device__ __forceinline__ void load_mean(const AttnArgs& a, int64_t mrow0, int J0, int jend, int t) {
+// Mean tokens: tile mt of sequence s holds mean tokens [128 mt, 128 mt + 128)
+// of that sequence (vbar^T as bf16, zero past the sequence's blocks); the
+// same workgroup rounds those tokens' kbar rows to bf16.  Tile index
+// cu_kblocks[s]/128 + s + mt never collides across sequences and stays
+// below mt_cap = total_kblocks/128 + num_seqs + 1.
+__global__ __launch_bounds__(256) void vt_mean_kernel(PrepArgs a) {
+  const int mt = blockIdx.x, s = blockIdx.y, g = blockIdx.z;
+  const int kb0 = a.cu_kblocks[s];
+  const int nkb = a.cu_kblocks[s + 1] - kb0;
+  if (mt * kBlk >= nkb) return;
+  const int t = threadIdx.x, c = t >> 4, dc = t & 15;
+  const int64_t row0 = (int64_t)g * a.total_kblocks + kb0;
+  uint4 in[8], out[8];
 #pragma unroll
-    for (int p = 0; p < NLD; ++p) {
-      const int ch = t + kThreads * p;
-      const int row = ch >> 4, c = ch & 15;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
-      if (J0 + row < jend) {
-        const int64_t off = (mrow0 + J0 + row) * kD + c * 8;
-        kv = *reinterpret_cast<const uint4*>(a.kbar16 + off);
-        vv = *reinterpret_cast<const uint4*>(a.vbar16 + off);
-      }
-      k[p] = kv;
-      v[p] = vv;
+  for (int e = 0; e < 8; ++e) {
+    const int jm = mt * kBlk + key_of_pos(8 * c + e);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (jm < nkb) {
+      const float* src = a.vbar + (row0 + jm) * kD + dc * 8;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+      v = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                     pack_bf16x2(hi[2], hi[3]));
+    }
+    in[e] = v;
+  }
+  transpose8x8(in, out);
+  const int64_t tile = (int64_t)g * a.mt_cap + kb0 / kBlk + s + mt;
+  uint8_t* dst = a.vbt + tile * kTileGlobal + c * 16;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dst + (8 * dc + e) * kRowBytes) = out[e];
+  // kbar rows of the same mean tokens
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int id = t + 256 * u;
+    const int jm = mt * kBlk + (id >> 4), ch = id & 15;
+    if (jm < nkb) {
+      const float* src = a.kbar + (row0 + jm) * kD + ch * 8;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+      *reinterpret_cast<uint4*>(a.kbar16 + (row0 + jm) * kD + ch * 8) =
+          make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                     pack_bf16x2(hi[2], hi[3]));
     }
   }
+}
 
-  __device__ __forceinline__ void commit(uint8_t* Kb, uint8_t* Vb, int t) const {
-#pragma unroll
-    for (int p = 0; p < NLD; ++p) {
-      const int ch = t + kThreads * p;
-      *reinterpret_cast<uint4*>(Kb + (ch >> 4) * kKS + (ch & 15) * 16) = k[p];
-      *reinterpret_cast<uint4*>(Vb + (ch >> 4) * kVS + (ch & 15) * 16) = v[p];
-    }
-  }
-};
+// ---------------------------------------------------------------------------
+// Attention
+// ---------------------------------------------------------------------------
 
 // bits of the 32 mean tokens [32*w, 32*w + 32) that are skipped blocks, i.e.
 // in [1, diag) and not kept
@@ -130,131 +184,224 @@ __device__ __forceinline__ uint32_t skipped_word(const uint32_t* kept, int w, in
   return m;
 }
 
-template <int BLK>
+// bf16 pair (1, 1): the dot product with it sums two probabilities
+typedef __bf16 bf16x2e __attribute__((ext_vector_type(2)));
+constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;
+
+// sched_group_barrier masks (LLVM AMDGPU IGroupLP)
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedValu = 0x002 | 0x400;  // VALU and transcendental
+
+// Scheduling patterns for the regions of a tile: four operand reads up
+// front, then each MFMA followed by the next read (while any are left) and V
+// vector ALU instructions.  The counts must not exceed what the region holds,
+// or the compiler drops the whole pattern (vector ALU instructions beyond the
+// groups are placed freely).  Written out flat as macros: the compiler
+// honours these barriers only when they sit, loop-free, in the body that
+// holds the instructions.
+#define FP2_SG(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+#define FP2_MDV(V) FP2_SG(kSchedMfma, 1); FP2_SG(kSchedDsRead, 1); FP2_SG(kSchedValu, (V))
+#define FP2_MV(V) FP2_SG(kSchedMfma, 1); FP2_SG(kSchedValu, (V))
+#define FP2_MD FP2_SG(kSchedMfma, 1); FP2_SG(kSchedDsRead, 1)
+// 8 MFMAs, 8 reads, no vector ALU
+#define FP2_PATTERN_8 FP2_SG(kSchedDsRead, 4); FP2_MD; FP2_MD; FP2_MD; FP2_MD; FP2_SG(kSchedMfma, 4)
+// 8 MFMAs, 8 reads, V vector ALU per MFMA
+#define FP2_PATTERN_8V(V)                                                          \
+  FP2_SG(kSchedDsRead, 4); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V);         \
+  FP2_MV(V); FP2_MV(V); FP2_MV(V); FP2_MV(V)
+// 16 MFMAs, 16 reads, V vector ALU per MFMA
+#define FP2_PATTERN_16V(V)                                                         \
+  FP2_SG(kSchedDsRead, 4); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V);         \
+  FP2_MDV(V); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V);          \
+  FP2_MDV(V); FP2_MDV(V); FP2_MV(V); FP2_MV(V); FP2_MV(V); FP2_MV(V)
+
+// Per-wave state and the work of one tile (32-key steps, see the header).
+//
+// Score accumulator element i of lane l (query l%32) is key
+// 8(i/4) + 4(l/32) + i%4 of its step.  A masked score is -inf; a mean token's
+// score carries log2(B)/scale extra, so that its probability carries the
+// block weight B.
 struct Wave {
+  static constexpr int NS = kBlk / 32;  // 32-key steps per tile
   bf16x8 qf[kD / 16];
   f32x16 o[kD / 32];
-  float m;  // reference max (log2 units), shared by lanes l and l^32
-  float l;  // this lane's half of the denominator
+  float m;    // reference max (log2 units), shared by lanes l and l^32
+  float thr;  // m + kLazy: a row max above it refreshes m
+  float nb;   // -m (0 while m = -inf): exp2(s * scale + nb) is the probability
+  float l;    // this lane's half of the denominator
 
-  // mode 0: exact block; 1: diagonal block (causal mask); 2: mean-token tile
-  // starting at mean token J0.  The mode is wave-uniform; one code path
-  // serves all three so the register allocation is shared.
-  __device__ __forceinline__ void tile(int mode, const uint8_t* Kb, const uint8_t* Vb, int lane, float scl, float bias,
-                                       int tq, int J0, int diag, const uint32_t* kept) {
-    const int c = lane & 31, hf = lane >> 5;
-    const int i16 = lane & 15, go = lane & 16;  // tr-read lane within its 16-lane group; d offset
-    // per-lane bases: K row c, chunk hf; V^T read row 4hf + i16/4, column go + 4(i16%4)
-    const uint8_t* kbase = Kb + c * kKS + hf * 16;
-    const uint8_t* vbase = Vb + (4 * hf + (i16 >> 2)) * kVS + (go + 4 * (i16 & 3)) * 2;
-#pragma nounroll
-    for (int sub = 0; sub < BLK / 64; ++sub) {
-      // S^T for 64 keys: two independent accumulator chains, alternated, with the
-      // K operand reads issued four MFMAs ahead
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-      __builtin_amdgcn_sched_barrier(0);
+  // S^T of step j accumulated onto c; K row 32j + l%32, chunk 2kk + l/32
+  // (all operand reads are written before the MFMAs; the region's
+  // scheduling pattern then moves them next to their MFMAs)
+  __device__ __forceinline__ f32x16 qk(const uint8_t* Kt, int off0, int off1, int j, f32x16 c) const {
+    bf16x8 kf[kD / 16];
 #pragma unroll
-      for (int kk = 0; kk < kD / 16; ++kk)
+    for (int kk = 0; kk < kD / 16; ++kk)
+      kf[kk] = *reinterpret_cast<const bf16x8*>(Kt + ((kk & 1) ? off1 : off0) + 8 * kGS * j + 64 * (kk >> 1));
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-          s[st] = mfma_bf16_32x32x16(
-              *reinterpret_cast<const bf16x8*>(kbase + (64 * sub + 32 * st) * kKS + 32 * kk), qf[kk], s[st]);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    for (int kk = 0; kk < kD / 16; ++kk) c = mfma_bf16_32x32x16(kf[kk], qf[kk], c);
+    return c;
+  }
+
+  // O^T += V^T P^T over the 32 keys of step j; V^T row 32dt + l%32, chunk
+  // 4j + 2r + l/32
+  __device__ __forceinline__ void pv(const uint8_t* Vt, int off0, int off1, int j, const bf16x8 (&pf)[2]) {
+    bf16x8 vf[2][kD / 32];
 #pragma unroll
-      for (int i = 0; i < 12; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (mode == 1) {
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+      for (int dt = 0; dt < kD / 32; ++dt)
+        vf[r][dt] = *reinterpret_cast<const bf16x8*>(Vt + (r ? off1 : off0) + 8 * kGS * dt + 64 * j);
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (64 * sub + 32 * st + 8 * (i >> 2) + 4 * hf + (i & 3) > tq) s[st][i] = -INFINITY;
-      }
-      if (mode == 2) {
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const uint32_t w = skipped_word(kept, (J0 >> 5) + 2 * sub + st, diag) >> (4 * hf);
+      for (int dt = 0; dt < kD / 32; ++dt) o[dt] = mfma_bf16_32x32x16(vf[r][dt], pf[r], o[dt]);
+  }
+
+  // Initial score accumulator of step j on diagonal and mean-token tiles
+  // (mode 1: -inf where key > query, else 0; mode 2: log2(B)/scale for a
+  // skipped block's mean token, -inf for the others).
+  __device__ __forceinline__ f32x16 mask(int mode, int j, int hf, int tq, float cb, const uint32_t* kept, int J0,
+                                         int diag) const {
+    f32x16 c;
+    if (mode == 1) {
+      int lim = tq - 32 * j - 4 * hf;  // element i is masked iff 8(i/4) + i%4 > lim
+      asm volatile("" : "+v"(lim));    // computed here, not hoisted ahead of the branch
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (!((w >> (8 * (i >> 2) + (i & 3))) & 1u)) s[st][i] = -INFINITY;
-        }
-      }
-      float sv[32];
+      for (int i = 0; i < 16; ++i) c[i] = 8 * (i >> 2) + (i & 3) > lim ? -INFINITY : 0.f;
+    } else {
+      uint32_t w = skipped_word(kept, (J0 >> 5) + j, diag) >> (4 * hf);
+      asm volatile("" : "+v"(w));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sv[i] = s[0][i];
-        sv[16 + i] = s[1][i];
-      }
-      const float mx = max_halves(tree_max<32>(sv));
-      const float mxs = mx * scl + bias;  // scl > 0; -inf stays -inf
-      if (__any(mxs > m + kLazy)) {       // wave-uniform refresh of the reference max
-        const float mnew = fmaxf(m, mxs);
-        const float alpha = __builtin_amdgcn_exp2f(m - (mnew == -INFINITY ? 0.f : mnew));
-        m = mnew;
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-      }
-      const float nb = bias - (m == -INFINITY ? 0.f : m);
-      float pv[32];
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * r + j], scl, nb));
-            pv[16 * st + 8 * r + j] = p;
-            pf[st][r][j] = (__bf16)p;
-          }
-      l += tree_sum<32>(pv);
-      // O^T += V^T P^T: four independent chains (dt), alternated, with the
-      // transposing V reads (two per MFMA) issued four MFMAs ahead
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-          for (int dt = 0; dt < kD / 32; ++dt) {
-            const uint8_t* vr = vbase + (64 * sub + 32 * st + 16 * r) * kVS + 64 * dt;
-            const i16x4 v0 = ds_read_tr16(vr);
-            const i16x4 v1 = ds_read_tr16(vr + 8 * kVS);
-            const i16x4 vv[2] = {v0, v1};
-            bf16x8 va;
-            __builtin_memcpy(&va, vv, sizeof(va));
-            o[dt] = mfma_bf16_32x32x16(va, pf[st][r], o[dt]);
-          }
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int i = 0; i < 12; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 16; ++i) c[i] = (w >> (8 * (i >> 2) + (i & 3))) & 1u ? cb : -INFINITY;
     }
+    return c;
+  }
+
+  // Probabilities of one step as bf16 against the current reference max,
+  // their sum added to l.  Returns whether some row's max exceeds thr (for
+  // the whole wave); the caller then refreshes the max and redoes the step.
+  __device__ __forceinline__ bool softmax(const f32x16& s, float scl, bf16x8 (&pf)[2], float& mxs) {
+    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);  // max3 chain
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+    mx = fmaxf(mx, s[15]);
+    mxs = max_halves(mx) * scl;  // scl > 0: -inf stays -inf
+    const bool up = __any(mxs > thr);
+    float acc = l;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w[q] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * r + 2 * q], scl, nb)),
+                           __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * r + 2 * q + 1], scl, nb)));
+        // the denominator sums the same rounded probabilities that PV uses
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2e, w[q]),
+                                              __builtin_bit_cast(bf16x2e, kOnesBf16x2), acc, false);
+      }
+      // computed here, not sunk into the next step's region
+      asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+      pf[r] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    asm volatile("" : "+v"(acc));
+    l = acc;
+    return up;
+  }
+
+  // Raises the reference max to cover this step's row maxima mxs, rescales O
+  // (which holds every step before this one) and l_prev (l before this
+  // step), and redoes the step's probabilities.
+  __device__ __forceinline__ void refresh(const f32x16& s, float scl, float mxs, float l_prev, bf16x8 (&pf)[2]) {
+    const float mnew = fmaxf(m, mxs);
+    const float alpha = __builtin_amdgcn_exp2f(m - (mnew == -INFINITY ? 0.f : mnew));
+    m = mnew;
+    thr = mnew + kLazy;
+    nb = mnew == -INFINITY ? 0.f : -mnew;
+    rescale(alpha);
+    float acc = l_prev * alpha;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w[q] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * r + 2 * q], scl, nb)),
+                           __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * r + 2 * q + 1], scl, nb)));
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2e, w[q]),
+                                              __builtin_bit_cast(bf16x2e, kOnesBf16x2), acc, false);
+      }
+      pf[r] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    l = acc;
+  }
+
+  __device__ __forceinline__ void rescale(float alpha) {
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+  }
+
+  // mode 0 exact block, 1 diagonal block, 2 mean-token tile starting at
+  // mean token J0 (wave-uniform).  MASKED (modes 1, 2) sets up each step's
+  // masks in a small block between the scheduling regions and starts the
+  // score accumulators from them; exact blocks start from zero.
+  template <bool MASKED>
+  __device__ __forceinline__ void tile(int mode, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1, int hf,
+                                       float scl, float cb, int tq, int J0, int diag, const uint32_t* kept) {
+    f32x16 cz = f32x16{};
+    if constexpr (MASKED) cz = mask(mode, 0, hf, tq, cb, kept, J0, diag);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s = qk(Kt, off0, off1, 0, cz);
+    FP2_PATTERN_8;
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pp[2];  // probabilities of the previous step
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      if constexpr (MASKED) {
+        if (j + 1 < NS) cz = mask(mode, j + 1, hf, tq, cb, kept, J0, diag);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 sn = f32x16{};
+      if (j + 1 < NS) sn = qk(Kt, off0, off1, j + 1, cz);
+      if (j > 0) pv(Vt, off0, off1, j - 1, pp);
+      bf16x8 pc[2];
+      float mxs;
+      const float l_prev = l;
+      const bool up = softmax(s, scl, pc, mxs);
+      // the softmax has about 50 vector ALU instructions
+      if (j == 0 || j + 1 == NS) {
+        FP2_PATTERN_8V(5);
+      } else {
+        FP2_PATTERN_16V(3);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (up) refresh(s, scl, mxs, l_prev, pc);  // after PV(j-1), before PV(j)
+      pp[0] = pc[0];
+      pp[1] = pc[1];
+      s = sn;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv(Vt, off0, off1, NS - 1, pp);
+    FP2_PATTERN_8;
+    __builtin_amdgcn_sched_barrier(0);
   }
 };
 
-template <int BLK>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t Kb[2][BLK * kKS];
-  __shared__ __attribute__((aligned(16))) uint8_t Vb[2][BLK * kVS];
+  // two K and two V^T buffers, as separate objects so that the compiler can
+  // tell the DMA target from the buffers being read
+  __shared__ __attribute__((aligned(1024))) uint8_t K0[kTileLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t K1[kTileLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t V0[kTileLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t V1[kTileLds];
   __shared__ uint32_t kept[kMaxKBlocks / 32];
-  __shared__ int mtile[kMaxKBlocks / 64 + 1];
+  __shared__ int mtile[kMaxKBlocks / kBlk + 1];
   __shared__ int s_nmean;
 
-  // ---- tile decode (as the first kernel): 8 consecutive CSR ranks form a
-  // group, the slices of one rank share blockIdx % 8 (one XCD), latest query
-  // blocks first
+  // ---- tile decode: 8 consecutive CSR ranks form a group, the slices of
+  // one rank share blockIdx % 8 (one XCD), latest query blocks first
   const int b = blockIdx.x;
   const int per_grp = 8 * a.slices;
   const int grp = b / per_grp;
@@ -271,23 +418,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   const int q0 = a.cu_seqlens_q[s];
   const int n = a.cu_seqlens_q[s + 1] - q0;
   const int T = a.seqlens_k[s];
-  const int diag = (T - n) / BLK + I;
+  const int diag = (T - n) / kBlk + I;
   const int G = a.hq / a.hkv;
   const int32_t* pt = a.page_table + (int64_t)s * a.max_pages;
-  const int64_t mrow0 = (int64_t)g * a.total_kblocks + a.cu_kblocks[s];
+  const int kb0 = a.cu_kblocks[s];
+  const int64_t mrow0 = (int64_t)g * a.total_kblocks + kb0;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int hf = lane >> 5;
   const int prow = slice * kWGRows + wave * 32;
-  const bool wave_active = prow < G * BLK;
-  const int h = g * G + prow / BLK;
-  const int tq = prow % BLK + (lane & 31);
-  const bool q_valid = wave_active && (I * BLK + tq < n);
+  const bool wave_active = prow < G * kBlk;
+  const int h = g * G + prow / kBlk;
+  const int tq = prow % kBlk + (lane & 31);
+  const bool q_valid = wave_active && (I * kBlk + tq < n);
 
   // uniform values: later loads indexed by them become scalar loads, which
-  // do not share the vector-memory counter with the tile prefetch
+  // do not share the vector-memory counter with the tile DMA
   const int kbeg = ld_uniform(a.row_ptr, row);
   const int kend = ld_uniform(a.row_ptr, row + 1);
   const int nexact = kend - kbeg;
@@ -304,17 +452,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     }
     __syncthreads();
     if (wave == 0) {
-      const int ncand = (diag + BLK - 1) / BLK;
+      const int ncand = (diag + kBlk - 1) / kBlk;
       int base = 0;
       for (int m0 = 0; m0 < ncand; m0 += 64) {
         const int mt = m0 + lane;
         bool flag = false;
         if (mt < ncand) {
 #pragma unroll
-          for (int w = 0; w < BLK / 32; ++w) flag |= skipped_word(kept, mt * (BLK / 32) + w, diag) != 0u;
+          for (int w = 0; w < kBlk / 32; ++w) flag |= skipped_word(kept, mt * (kBlk / 32) + w, diag) != 0u;
         }
         const uint64_t bal = __ballot(flag);
-        if (flag) mtile[base + __popcll(bal & ((1ull << lane) - 1ull))] = mt * BLK;
+        if (flag) mtile[base + __popcll(bal & ((1ull << lane) - 1ull))] = mt * kBlk;
         base += __popcll(bal);
       }
       if (lane == 0) s_nmean = base;
@@ -324,78 +472,160 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   }
   const int ntiles = nexact + nmean;
 
-  Wave<BLK> ws;
+  Wave ws;
   ws.m = -INFINITY;
+  ws.thr = -INFINITY;
+  ws.nb = 0.f;
   ws.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt) ws.o[dt] = f32x16{};
   {
-    const uint8_t* qrow = a.q + ((int64_t)(q0 + I * BLK + tq) * a.hq + h) * kRowBytes;
+    const uint8_t* qrow = a.q + ((int64_t)(q0 + I * kBlk + tq) * a.hq + h) * kRowBytes;
 #pragma unroll
     for (int kk = 0; kk < kD / 16; ++kk) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (q_valid) v = *reinterpret_cast<const uint4*>(qrow + (16 * kk + 8 * hf) * 2);
       ws.qf[kk] = __builtin_bit_cast(bf16x8, v);
     }
-    // Complete the query loads here: otherwise the compiler's wait for them lands
-    // inside the tile loop, where it would also wait for the next tile's prefetch.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
 
-  // Tile pipeline: at iteration i the LDS buffer i%2 holds tile i, the
-  // staging registers hold tile i+1 (in flight), the page entries of tile
-  // i+2 are in flight, and the block indices of tiles i..i+3 sit in uniform
-  // registers.  No step of an iteration waits on a global load issued in the
-  // same iteration, so global latency overlaps a full tile of compute.
-  Stage<BLK> stg;
-  auto block_of = [&](int idx) -> int {  // first block (KV block or mean token) of tile idx
-    if (idx >= ntiles) return 0;
-    if (idx < nexact) return ld_uniform(a.col_idx, kbeg + idx);
-    return mtile[idx - nexact];
+  // ---- DMA of one tile: wave w moves rows 16w .. 16w+15 (row groups 4w ..
+  // 4w+3) of the K and the V^T tile; lane i of group 4w+p moves row
+  // 16w + 4p + i/16, chunk (i%16) ^ (i/16), into its 16-byte slot.  When
+  // those 16 rows lie in one page (page size a multiple of 16, rows inside
+  // the sequence) the address is a wave-uniform base plus per-lane offsets
+  // fixed for the whole kernel; otherwise each lane looks up its own page.
+  const int uoff = 16 * ((lane & 15) ^ (lane >> 4));
+  const uint32_t voff = (uint32_t)((lane >> 4) * kRowBytes + uoff);  // + 1024 p: rows of 256 bytes
+  const uint32_t tok = (uint32_t)a.hkv * kRowBytes;                  // K row stride in the cache
+  const uint32_t koff = (uint32_t)(lane >> 4) * tok + uoff;          // + 4 p tok
+  const bool pages16 = a.page_size % 16 == 0;
+  // Uniform values for later tiles (block indices, page entries) come through
+  // vector buffer loads: they share the vector-memory counter with the DMA,
+  // so the wait at each tile barrier covers them.  Scalar loads would share
+  // the LDS counter instead, and every tile's first operand-read wait would
+  // then also wait for them.
+  const __amdgpu_buffer_rsrc_t rcol =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.col_idx + kbeg), (short)0, nexact * 4, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rpt =
+      __builtin_amdgcn_make_buffer_rsrc((void*)pt, (short)0, a.max_pages * 4, kBufferFlags);
+  auto page_of = [&](int J) -> int {  // page of rows 16w.. of block J (valid after the next barrier)
+    int pi, slot;
+    a.pm.split(min(J * kBlk + 16 * wave, T - 1), pi, slot);
+    return __builtin_amdgcn_raw_buffer_load_b32(rpt, pi * 4, 0, 0);
   };
-  auto stage = [&](int idx, int j) {  // global -> staging registers
-    if (idx < nexact) stg.load_exact(a, g, j, t);
-    else stg.load_mean(a, mrow0, j, diag, t);
+  // a value loaded before the last barrier, read as a wave-uniform scalar there
+  // (pinned after the barrier so the read is not hoisted next to its load)
+  auto after_barrier = [](int v) {
+    asm volatile("" : "+v"(v));
+    return __builtin_amdgcn_readfirstlane(v);
   };
-  auto pages = [&](int idx, int j) {
-    if (idx < nexact) stg.fetch_pages(a, pt, T, j, t);
+  int pgu = 0;  // page of rows 16w.. of the exact tile being moved (uniform)
+  auto lds = [](uint8_t* p) { return (__attribute__((address_space(3))) void*)p; };
+  auto dma = [&](int idx, int j, uint8_t* Kd, uint8_t* Vd) {
+    uint8_t* kd = Kd + 4 * wave * kGS;
+    uint8_t* vd = Vd + 4 * wave * kGS;
+    if (idx < nexact) {
+      const uint8_t* vsrc = a.vt + (((int64_t)g * a.total_kblocks + kb0 + j) * kBlk + 16 * wave) * kRowBytes + voff;
+      const int r0 = j * kBlk + 16 * wave;
+      if (pages16 && r0 + 15 < T) {
+        int pi, slot;
+        a.pm.split(r0, pi, slot);
+        const uint8_t* kb = a.k_pages + (((int64_t)pgu * a.page_size + slot) * a.hkv + g) * kRowBytes;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          __builtin_amdgcn_global_load_lds(kb + koff + 4 * p * tok, lds(kd + p * kGS), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          int pi, slot;
+          a.pm.split(min(r0 + 4 * p + (lane >> 4), T - 1), pi, slot);  // rows past the end repeat the last key
+          const uint8_t* ksrc = a.k_pages + (((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g) * kRowBytes + uoff;
+          __builtin_amdgcn_global_load_lds(ksrc, lds(kd + p * kGS), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
+        }
+      }
+    } else {
+      const uint8_t* vsrc =
+          a.vbt + (((int64_t)g * a.mt_cap + kb0 / kBlk + s + j / kBlk) * kBlk + 16 * wave) * kRowBytes + voff;
+      const uint8_t* k16 = reinterpret_cast<const uint8_t*>(a.kbar16);
+      const int r0 = j + 16 * wave;
+      if (r0 + 15 < diag) {
+        const uint8_t* kb = k16 + (mrow0 + r0) * kRowBytes + voff;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          __builtin_amdgcn_global_load_lds(kb + 1024 * p, lds(kd + p * kGS), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int jm = min(r0 + 4 * p + (lane >> 4), diag - 1);  // tokens past diag repeat a real one (masked)
+          __builtin_amdgcn_global_load_lds(k16 + (mrow0 + jm) * kRowBytes + uoff, lds(kd + p * kGS), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
+        }
+      }
+    }
   };
 
-  int j0 = block_of(0), j1 = block_of(1), j2 = block_of(2), j3 = block_of(3);
+  // per-lane operand offsets (see Wave::qk / Wave::pv): row l%32 of a 32-row
+  // slab, chunk parity 0 / 1 of the lane's half
+  const int c = lane & 31, x = c & 3;
+  const int rbase = (c >> 2) * kGS + x * kRowBytes;
+  const int off0 = rbase + 16 * (hf ^ x);
+  const int off1 = rbase + 16 * ((2 + hf) ^ x);
+
+  // Tile pipeline: at iteration i the LDS buffers i%2 hold tile i and the
+  // DMA of tile i+1 into the other buffers is in flight; the block index of
+  // tile i+2 and the page entry of tile i+1 arrived with the last barrier,
+  // the loads of tile i+3's block index and tile i+2's page entry are in
+  // flight.
+  auto mean_of = [&](int idx) -> int { return idx < ntiles ? mtile[idx - nexact] : 0; };
+  int j0 = 0, j1 = 0, j2v = 0, pgv = 0;
+  if (0 < nexact) j0 = ld_uniform(a.col_idx, kbeg);
+  else if (0 < ntiles) j0 = mean_of(0);
+  if (1 < nexact) j1 = ld_uniform(a.col_idx, kbeg + 1);
+  else if (1 < ntiles) j1 = mean_of(1);
+  if (2 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 2 * 4, 0, 0);
   if (ntiles > 0) {
-    pages(0, j0);
-    stage(0, j0);
-    stg.commit(Kb[0], Vb[0], t);
+    if (nexact > 0) pgu = __builtin_amdgcn_readfirstlane(page_of(j0));
+    dma(0, j0, K0, V0);
   }
-  if (ntiles > 1) {
-    pages(1, j1);
-    stage(1, j1);
-  }
-  if (ntiles > 2) pages(2, j2);
+  if (1 < nexact) pgv = page_of(j1);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   const float scl = a.scale_log2;
-  for (int idx = 0; idx < ntiles; ++idx) {
-    const int cur = idx & 1;
-    const int j4 = block_of(idx + 4);
+  const float cb = a.log2_block / scl;  // mean-token weight log2(B) in score units
+
+  auto iter = [&](int idx, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
+    const int j2 = idx + 2 < nexact ? after_barrier(j2v) : mean_of(idx + 2);
+    if (idx + 1 < nexact) pgu = after_barrier(pgv);
+    if (idx + 1 < ntiles) dma(idx + 1, j1, Kn, Vn);
+    if (idx + 2 < nexact) pgv = page_of(j2);
+    if (idx + 3 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, (idx + 3) * 4, 0, 0);
     if (wave_active) {
-      const bool exact = idx < nexact;
-      const int mode = exact ? (j0 == diag ? 1 : 0) : 2;
-      ws.tile(mode, Kb[cur], Vb[cur], lane, scl, exact ? 0.f : a.log2_block, tq, exact ? 0 : j0, diag, kept);
+      const int mode = idx >= nexact ? 2 : (j0 == diag ? 1 : 0);
+      if (mode)
+        ws.tile<true>(mode, Kc, Vc, off0, off1, hf, scl, cb, tq, j0, diag, kept);
+      else
+        ws.tile<false>(0, Kc, Vc, off0, off1, hf, scl, cb, tq, j0, diag, kept);
     }
-    if (idx + 1 < ntiles) stg.commit(Kb[cur ^ 1], Vb[cur ^ 1], t);
-    if (idx + 2 < ntiles) stage(idx + 2, j2);
-    if (idx + 3 < ntiles) pages(idx + 3, j3);
     j0 = j1;
     j1 = j2;
-    j2 = j3;
-    j3 = j4;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's DMA and loads for later tiles have landed
     __syncthreads();
+  };
+  for (int idx = 0; idx < ntiles; idx += 2) {
+    iter(idx, K0, V0, K1, V1);
+    if (idx + 1 < ntiles) iter(idx + 1, K1, V1, K0, V0);
   }
 
   // ---- epilogue: O / l
   if (q_valid) {
     const float inv = 1.0f / sum_halves(ws.l);
-    const int64_t obase = ((int64_t)(q0 + I * BLK + tq) * a.hq + h) * kD;
+    const int64_t obase = ((int64_t)(q0 + I * kBlk + tq) * a.hq + h) * kD;
     if (a.out_f32) {
       float* orow = static_cast<float*>(a.out) + obase;
 #pragma unroll
@@ -420,18 +650,55 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   }
 }
 
+#undef FP2_PATTERN_16V
+#undef FP2_PATTERN_8V
+#undef FP2_PATTERN_8
+#undef FP2_MD
+#undef FP2_MV
+#undef FP2_MDV
+#undef FP2_SG
+
 }  // namespace
 
-// Launch with a.slices computed for kWGRows rows per workgroup.
-hipError_t launch_attn_bf16_d128(const AttnArgs& a_in, int block, hipStream_t stream) {
+hipError_t launch_attn_bf16_d128(const AttnArgs& a_in, const float* kbar, const float* vbar, int max_kblocks,
+                                 hipStream_t stream) {
   AttnArgs a = a_in;
+  uint16_t* kbar16 = const_cast<uint16_t*>(a.kbar16);
+  uint8_t* vbt = const_cast<uint8_t*>(a.vbt);
+  uint8_t* vt = const_cast<uint8_t*>(a.vt);
+  PrepArgs p;
+  p.cu_kblocks = a.cu_kblocks;
+  p.seqlens_k = a.seqlens_k;
+  p.page_table = a.page_table;
+  p.v_pages = a.v_pages;
+  p.kbar = kbar;
+  p.vbar = vbar;
+  p.kbar16 = kbar16;
+  p.vt = vt;
+  p.vbt = vbt;
+  p.pm = a.pm;
+  p.num_seqs = a.num_seqs;
+  p.hkv = a.hkv;
+  p.max_pages = a.max_pages;
+  p.page_size = a.page_size;
+  p.total_kblocks = a.total_kblocks;
+  p.mt_cap = a.mt_cap;
+  if (a.total_kblocks > 0) {
+    hipLaunchKernelGGL(vt_exact_kernel, dim3((unsigned)a.total_kblocks, (unsigned)a.hkv), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.correction) {
+      hipLaunchKernelGGL(vt_mean_kernel,
+                         dim3((unsigned)((max_kblocks + kBlk - 1) / kBlk), (unsigned)a.num_seqs, (unsigned)a.hkv),
+                         dim3(256), 0, stream, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
   const int G = a.hq / a.hkv;
-  a.slices = (G * block + kWGRows - 1) / kWGRows;
+  a.slices = (G * kBlk + kWGRows - 1) / kWGRows;
   const unsigned grid = (unsigned)(((a.rows + 7) / 8) * 8 * a.slices);
-  if (block == 128)
-    hipLaunchKernelGGL(attn_bf16_d128_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_bf16_d128_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -26,16 +26,21 @@ struct AttnArgs {
   const float* k_scale;
   const float* v_scale;
   const uint16_t* kbar16;  // bf16 [Hkv, total_kblocks, D]
-  const uint16_t* vbar16;  // [Hkv, total_kblocks, D]: fp16 (first kernel) or bf16 (d128 kernel)
+  const uint16_t* vbar16;  // fp16 [Hkv, total_kblocks, D] (register-staged kernel)
+  const uint8_t* vt;       // V^T tiles of every KV block (bf16 d128 kernel)
+  const uint8_t* vbt;      // vbar^T tiles of the mean tokens (bf16 d128 kernel)
   void* out;               // bf16 or f32 [total_q, Hq, D]
   float scale_log2;        // softmax_scale * log2(e)
   float log2_block;        // log2(B): weight B of a mean token
   PageMap pm;
   int num_seqs, hq, hkv, max_pages, page_size, total_qblocks, total_kblocks;
-  int correction, slices, rows, out_f32;
+  int correction, slices, rows, out_f32, mt_cap;
 };
 
 
-hipError_t launch_attn_bf16_d128(const AttnArgs& a, int block, hipStream_t stream);
+// Transposes V (and vbar, and rounds kbar) into the workspace parts that
+// a.vt, a.vbt and a.kbar16 point to, then runs the bf16 d=128 B=128 kernel.
+hipError_t launch_attn_bf16_d128(const AttnArgs& a, const float* kbar, const float* vbar, int max_kblocks,
+                                 hipStream_t stream);
 
 }  // namespace fp2

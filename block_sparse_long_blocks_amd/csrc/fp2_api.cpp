@@ -87,10 +87,11 @@ fp2_status fp2_plan_mask(const fp2_batch* batch, const fp2_q* q, int32_t num_kv_
                     "fp2_plan_mask launch");
 }
 
-size_t fp2_run_workspace_bytes(const fp2_batch* batch, int32_t num_kv_heads, int32_t head_dim) {
+size_t fp2_run_workspace_bytes(const fp2_batch* batch, int32_t num_kv_heads, int32_t head_dim,
+                               fp2_dtype dtype) {
   BatchInfo info;
   if (check_batch(batch, &info) != FP2_OK || num_kv_heads < 1 || head_dim < 1) return 0;
-  return run_workspace_bytes(info, num_kv_heads, head_dim);
+  return run_layout(info, batch->num_seqs, num_kv_heads, head_dim, dtype, batch->block).total;
 }
 
 fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv* kv,
@@ -113,9 +114,10 @@ fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv*
     return fail(FP2_ERR_INVALID, "softmax_scale must be finite and > 0");
   if (info.total_qblocks == 0) return FP2_OK;
   if (!row_ptr || !col_idx || !out) return fail(FP2_ERR_INVALID, "row_ptr/col_idx/out is NULL");
-  if (mean_correction) {
-    if (!kbar || !vbar) return fail(FP2_ERR_INVALID, "mean correction needs kbar and vbar");
-    const size_t wneed = run_workspace_bytes(info, kv->num_kv_heads, kv->head_dim);
+  if (mean_correction && (!kbar || !vbar)) return fail(FP2_ERR_INVALID, "mean correction needs kbar and vbar");
+  if (mean_correction || vt_path(q->dtype, q->head_dim, batch->block)) {
+    const size_t wneed =
+        run_layout(info, batch->num_seqs, kv->num_kv_heads, kv->head_dim, kv->dtype, batch->block).total;
     if (!workspace || workspace_bytes < wneed)
       return fail(FP2_ERR_CAPACITY, "run workspace " + std::to_string(workspace_bytes) + " < " +
                                         std::to_string(wneed) + " bytes");

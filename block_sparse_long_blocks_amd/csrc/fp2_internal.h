@@ -35,7 +35,21 @@ fp2_status check_q(const fp2_q* q, int num_kv_heads, const BatchInfo& info, int 
 fp2_status check_kv(const fp2_kv* kv, const fp2_batch* b, const BatchInfo& info);
 
 size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads);
-size_t run_workspace_bytes(const BatchInfo& info, int num_kv_heads, int head_dim);
+// fp2_prefill_run runs the DMA kernel on V^T tiles for bf16, d = 128,
+// B = 128, and the register-staged kernel otherwise.
+inline bool vt_path(int dtype, int head_dim, int block) {
+  return dtype == FP2_BF16 && head_dim == 128 && block == 128;
+}
+
+// Byte offsets of the parts of the fp2_prefill_run workspace.
+struct RunLayout {
+  size_t k16 = 0;      // bf16 kbar rows [Hkv, total_kblocks, d]
+  size_t v16 = 0;      // fp16 vbar rows (register-staged path) or vbar^T tiles (V^T path)
+  size_t vt = 0;       // V^T tiles of every KV block (V^T path)
+  size_t total = 0;
+  int64_t mt_cap = 0;  // vbar^T tiles per KV head (V^T path)
+};
+RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_kv_heads, int head_dim, int dtype, int block);
 inline int plan_words(const BatchInfo& info) { return int((info.max_kblocks + 31) / 32); }
 
 }  // namespace fp2

@@ -135,10 +135,23 @@ size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads) {
   return (bytes + 255) & ~size_t(255);
 }
 
-size_t run_workspace_bytes(const BatchInfo& info, int num_kv_heads, int head_dim) {
-  // bf16 copies of kbar and vbar for the correction tiles
-  const size_t one = (size_t)num_kv_heads * (size_t)info.total_kblocks * (size_t)head_dim * 2;
-  return 2 * ((one + 255) & ~size_t(255));
+RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_kv_heads, int head_dim, int dtype, int block) {
+  auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
+  RunLayout L;
+  const size_t tkb = (size_t)info.total_kblocks, hkv = (size_t)num_kv_heads;
+  if (tkb == 0) return L;
+  const size_t rows = up(hkv * tkb * (size_t)head_dim * 2);  // one bf16/fp16 copy of kbar or vbar
+  L.k16 = 0;
+  L.v16 = rows;
+  if (vt_path(dtype, head_dim, block)) {
+    const size_t tile = (size_t)block * (size_t)head_dim * 2;  // one 128 x 128 bf16 tile
+    L.mt_cap = (int64_t)(tkb / (size_t)block + (size_t)num_seqs + 1);
+    L.vt = L.v16 + hkv * (size_t)L.mt_cap * tile;
+    L.total = L.vt + hkv * tkb * tile;
+  } else {
+    L.total = L.v16 + rows;
+  }
+  return L;
 }
 
 }  // namespace fp2

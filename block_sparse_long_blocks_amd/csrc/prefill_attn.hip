@@ -524,25 +524,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 }
 
 // Operand copies of the block means for the correction tiles: kbar as bf16
-// (the QK^T operand type); vbar as fp16 (PV operand type of the first kernel)
-// or bf16 (d128 kernel), all rounded to nearest even.
+// (the QK^T operand type) and vbar as fp16 (the PV operand type of this
+// kernel), both rounded to nearest even.
 __global__ __launch_bounds__(256) void means_to_mma_kernel(const float* __restrict__ kbar,
                                                            const float* __restrict__ vbar,
                                                            uint16_t* __restrict__ k16,
-                                                           uint16_t* __restrict__ v16, int64_t n4,
-                                                           int v_bf16) {
+                                                           uint16_t* __restrict__ v16, int64_t n4) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   const f32x4 k = reinterpret_cast<const f32x4*>(kbar)[i];
   const f32x4 v = reinterpret_cast<const f32x4*>(vbar)[i];
   reinterpret_cast<uint2*>(k16)[i] = make_uint2(pack_bf16x2(k[0], k[1]), pack_bf16x2(k[2], k[3]));
+  _Float16 hv[4] = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
   uint2 bits;
-  if (v_bf16) {
-    bits = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-  } else {
-    _Float16 hv[4] = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-    __builtin_memcpy(&bits, hv, sizeof(bits));
-  }
+  __builtin_memcpy(&bits, hv, sizeof(bits));
   reinterpret_cast<uint2*>(v16)[i] = bits;
 }
 
@@ -568,14 +563,15 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
                           void* out, void* workspace, hipStream_t stream) {
   if (info.total_qblocks == 0) return hipSuccess;
   const int D = q->head_dim, BLK = b->block, hkv = kv->num_kv_heads;
-  const size_t one = (((size_t)hkv * info.total_kblocks * D * 2) + 255) & ~size_t(255);
-  uint16_t* k16 = static_cast<uint16_t*>(workspace);
-  uint16_t* v16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + one);
-  const bool d128_kernel = q->dtype == FP2_BF16 && D == 128;
-  if (correction) {
+  const bool vt = vt_path(q->dtype, D, BLK);
+  const RunLayout L = run_layout(info, b->num_seqs, hkv, D, q->dtype, BLK);
+  uint8_t* wsb = static_cast<uint8_t*>(workspace);
+  uint16_t* k16 = reinterpret_cast<uint16_t*>(wsb + L.k16);
+  uint16_t* v16 = reinterpret_cast<uint16_t*>(wsb + L.v16);
+  if (correction && !vt) {
     const int64_t n4 = (int64_t)hkv * info.total_kblocks * D / 4;
     hipLaunchKernelGGL(means_to_mma_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                       kbar, vbar, k16, v16, n4, d128_kernel ? 1 : 0);
+                       kbar, vbar, k16, v16, n4);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -595,6 +591,9 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.v_scale = kv->v_scale;
   a.kbar16 = k16;
   a.vbar16 = v16;
+  a.vt = wsb + L.vt;
+  a.vbt = wsb + L.v16;
+  a.mt_cap = (int)L.mt_cap;
   a.out = out;
   a.out_f32 = out_f32;
   a.scale_log2 = softmax_scale * kLog2e;
@@ -612,7 +611,7 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.slices = (G * BLK + kRowsPerWG - 1) / kRowsPerWG;
   a.rows = (int)(info.total_qblocks * hkv);
   const unsigned grid = (unsigned)(((a.rows + 7) / 8) * 8 * a.slices);
-  if (d128_kernel) return launch_attn_bf16_d128(a, BLK, stream);
+  if (vt) return launch_attn_bf16_d128(a, kbar, vbar, (int)info.max_kblocks, stream);
   if (q->dtype == FP2_FP8_E4M3) return launch_attn_dt<true>(D, BLK, a, grid, stream);
   return launch_attn_dt<false>(D, BLK, a, grid, stream);
 }

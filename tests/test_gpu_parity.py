@@ -54,10 +54,14 @@ SMALL = {
     "d128_b64_g8": _cfg("d128_b64_g8", (768,), (192,), 16, 2, 128, 64, 32),
     "single_token": _cfg("single_token", (257, 1), (256, 0), 4, 2, 128, 128, 128, structure="plain"),
     "fp8_varlen": _cfg("fp8_varlen", (1024, 512), (0, 256), 8, 2, 128, 128, 128, dtype="fp8", shuffle=True),
+    # bf16 d=128 B=128 with pages that split a 16-row DMA group (per-lane page lookups), one query
+    # head per KV head (half of each workgroup idle) and eight (four slices per query block)
+    "d128_p24_g1": _cfg("d128_p24_g1", (900, 260), (128, 0), 2, 2, 128, 128, 24),
+    "d128_p8_g8": _cfg("d128_p8_g8", (700,), (384,), 16, 2, 128, 128, 8),
 }
 TAUS = {"tiny": (0.0, 0.005, 0.01, 0.02, 2.0), "varlen_p64": (0.0, 0.5, 3.0),
         "d64_b128_p16": (0.3, 3.0), "d128_b64_g8": (0.2, 2.0), "single_token": (0.0, 1.0),
-        "fp8_varlen": (0.0, 0.5, 3.0)}
+        "fp8_varlen": (0.0, 0.5, 3.0), "d128_p24_g1": (0.0, 1.0), "d128_p8_g8": (0.0, 1.0)}
 
 _cache = {}
 
