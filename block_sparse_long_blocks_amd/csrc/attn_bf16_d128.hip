@@ -187,6 +187,10 @@ __device__ __forceinline__ uint32_t skipped_word(const uint32_t* kept, int w, in
 // bf16 pair (1, 1): the dot product with it sums two probabilities
 typedef __bf16 bf16x2e __attribute__((ext_vector_type(2)));
 constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;
+// a step whose probabilities (per lane: 16 of them) sum to this or more
+// refreshes the reference max; probabilities stay below 2^64, so P (bf16),
+// l and O (float32) cannot overflow
+constexpr float kPmax = 18446744073709551616.0f;  // 2^64
 
 // sched_group_barrier masks (LLVM AMDGPU IGroupLP)
 constexpr int kSchedMfma = 0x008;
@@ -227,7 +231,6 @@ struct Wave {
   bf16x8 qf[kD / 16];
   f32x16 o[kD / 32];
   float m;    // reference max (log2 units), shared by lanes l and l^32
-  float thr;  // m + kLazy: a row max above it refreshes m
   float nb;   // -m (0 while m = -inf): exp2(s * scale + nb) is the probability
   float l;    // this lane's half of the denominator
 
@@ -279,17 +282,17 @@ struct Wave {
     return c;
   }
 
-  // Probabilities of one step as bf16 against the current reference max,
-  // their sum added to l.  Returns whether some row's max exceeds thr (for
-  // the whole wave); the caller then refreshes the max and redoes the step.
-  __device__ __forceinline__ bool softmax(const f32x16& s, float scl, bf16x8 (&pf)[2], float& mxs) {
-    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);  // max3 chain
+  __device__ __forceinline__ void rescale(float alpha) {
 #pragma unroll
-    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
-    mx = fmaxf(mx, s[15]);
-    mxs = max_halves(mx) * scl;  // scl > 0: -inf stays -inf
-    const bool up = __any(mxs > thr);
-    float acc = l;
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+  }
+
+  // bf16 probabilities of one step against the reference max; returns the
+  // sum of the rounded probabilities (two independent accumulation chains)
+  __device__ __forceinline__ float probs(const f32x16& s, float scl, bf16x8 (&pf)[2]) const {
+    float acc[2] = {0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       uint32_t w[4];
@@ -298,49 +301,43 @@ struct Wave {
         w[q] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * r + 2 * q], scl, nb)),
                            __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * r + 2 * q + 1], scl, nb)));
         // the denominator sums the same rounded probabilities that PV uses
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2e, w[q]),
-                                              __builtin_bit_cast(bf16x2e, kOnesBf16x2), acc, false);
+        acc[q & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2e, w[q]),
+                                                     __builtin_bit_cast(bf16x2e, kOnesBf16x2), acc[q & 1], false);
       }
       // computed here, not sunk into the next step's region
       asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
       pf[r] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
     }
-    asm volatile("" : "+v"(acc));
-    l = acc;
-    return up;
+    return acc[0] + acc[1];
   }
 
-  // Raises the reference max to cover this step's row maxima mxs, rescales O
-  // (which holds every step before this one) and l_prev (l before this
-  // step), and redoes the step's probabilities.
-  __device__ __forceinline__ void refresh(const f32x16& s, float scl, float mxs, float l_prev, bf16x8 (&pf)[2]) {
-    const float mnew = fmaxf(m, mxs);
+  // Probabilities of one step against the current reference max, their sum
+  // added to l.  The row max is not tracked on this path: the reference max
+  // is set from the first step's scores (every row sees key 0 there) and
+  // refreshed only when a step's probabilities reach kPmax, which keeps P,
+  // l and O finite and exact while O / l does not depend on the reference.
+  // Returns whether the whole wave must refresh and redo the step.
+  __device__ __forceinline__ bool softmax(const f32x16& s, float scl, bf16x8 (&pf)[2]) {
+    float step = probs(s, scl, pf);
+    asm volatile("" : "+v"(step));
+    l += step;
+    return __any(!(step < kPmax));  // also catches inf
+  }
+
+  // Sets the reference max to cover this step's scores, rescales O (which
+  // holds every step before this one) and l_prev (l before this step), and
+  // redoes the step's probabilities.
+  __device__ __forceinline__ void refresh(const f32x16& s, float scl, float l_prev, bf16x8 (&pf)[2]) {
+    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);  // max3 chain
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+    mx = fmaxf(mx, s[15]);
+    const float mnew = fmaxf(m, max_halves(mx) * scl);  // scl > 0: -inf stays -inf
     const float alpha = __builtin_amdgcn_exp2f(m - (mnew == -INFINITY ? 0.f : mnew));
     m = mnew;
-    thr = mnew + kLazy;
     nb = mnew == -INFINITY ? 0.f : -mnew;
     rescale(alpha);
-    float acc = l_prev * alpha;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        w[q] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * r + 2 * q], scl, nb)),
-                           __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * r + 2 * q + 1], scl, nb)));
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2e, w[q]),
-                                              __builtin_bit_cast(bf16x2e, kOnesBf16x2), acc, false);
-      }
-      pf[r] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-    }
-    l = acc;
-  }
-
-  __device__ __forceinline__ void rescale(float alpha) {
-#pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    l = l_prev * alpha + probs(s, scl, pf);
   }
 
   // mode 0 exact block, 1 diagonal block, 2 mean-token tile starting at
@@ -348,8 +345,8 @@ struct Wave {
   // masks in a small block between the scheduling regions and starts the
   // score accumulators from them; exact blocks start from zero.
   template <bool MASKED>
-  __device__ __forceinline__ void tile(int mode, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1, int hf,
-                                       float scl, float cb, int tq, int J0, int diag, const uint32_t* kept) {
+  __device__ __forceinline__ void tile(int mode, bool first, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1,
+                                       int hf, float scl, float cb, int tq, int J0, int diag, const uint32_t* kept) {
     f32x16 cz = f32x16{};
     if constexpr (MASKED) cz = mask(mode, 0, hf, tq, cb, kept, J0, diag);
     __builtin_amdgcn_sched_barrier(0);
@@ -367,17 +364,16 @@ struct Wave {
       if (j + 1 < NS) sn = qk(Kt, off0, off1, j + 1, cz);
       if (j > 0) pv(Vt, off0, off1, j - 1, pp);
       bf16x8 pc[2];
-      float mxs;
       const float l_prev = l;
-      const bool up = softmax(s, scl, pc, mxs);
-      // the softmax has about 50 vector ALU instructions
+      const bool up = softmax(s, scl, pc) || (first && j == 0);
+      // the softmax has about 36 vector ALU instructions
       if (j == 0 || j + 1 == NS) {
-        FP2_PATTERN_8V(5);
+        FP2_PATTERN_8V(4);
       } else {
-        FP2_PATTERN_16V(3);
+        FP2_PATTERN_16V(2);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (up) refresh(s, scl, mxs, l_prev, pc);  // after PV(j-1), before PV(j)
+      if (up) refresh(s, scl, l_prev, pc);  // after PV(j-1), before PV(j)
       pp[0] = pc[0];
       pp[1] = pc[1];
       s = sn;
@@ -474,7 +470,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
 
   Wave ws;
   ws.m = -INFINITY;
-  ws.thr = -INFINITY;
   ws.nb = 0.f;
   ws.l = 0.f;
 #pragma unroll
@@ -608,9 +603,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     if (wave_active) {
       const int mode = idx >= nexact ? 2 : (j0 == diag ? 1 : 0);
       if (mode)
-        ws.tile<true>(mode, Kc, Vc, off0, off1, hf, scl, cb, tq, j0, diag, kept);
+        ws.tile<true>(mode, idx == 0, Kc, Vc, off0, off1, hf, scl, cb, tq, j0, diag, kept);
       else
-        ws.tile<false>(0, Kc, Vc, off0, off1, hf, scl, cb, tq, j0, diag, kept);
+        ws.tile<false>(0, idx == 0, Kc, Vc, off0, off1, hf, scl, cb, tq, j0, diag, kept);
     }
     j0 = j1;
     j1 = j2;
