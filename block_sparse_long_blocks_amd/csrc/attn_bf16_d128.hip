@@ -484,12 +484,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     }
   }
 
-  // ---- DMA of one tile: wave w moves rows 16w .. 16w+15 (row groups 4w ..
-  // 4w+3) of the K and the V^T tile; lane i of group 4w+p moves row
-  // 16w + 4p + i/16, chunk (i%16) ^ (i/16), into its 16-byte slot.  When
-  // those 16 rows lie in one page (page size a multiple of 16, rows inside
-  // the sequence) the address is a wave-uniform base plus per-lane offsets
-  // fixed for the whole kernel; otherwise each lane looks up its own page.
+  // ---- DMA of one tile, issued by waves 0-3 only (one per SIMD): while a
+  // wave waits to issue its share into the memory pipeline, the other wave on
+  // its SIMD keeps the matrix core busy.  Wave w < 4 moves rows 32w .. 32w+31
+  // (row groups 8w .. 8w+7) of the K and the V^T tile; lane i of group 8w+p
+  // moves row 32w + 4p + i/16, chunk (i%16) ^ (i/16), into its 16-byte slot.
+  // When each 16-row half lies in one page (page size a multiple of 16, rows
+  // inside the sequence) the address is a wave-uniform base plus per-lane
+  // offsets fixed for the whole kernel; otherwise each lane looks up its own
+  // page.
+  const bool mover = wave < 4;
   const int uoff = 16 * ((lane & 15) ^ (lane >> 4));
   const uint32_t voff = (uint32_t)((lane >> 4) * kRowBytes + uoff);  // + 1024 p: rows of 256 bytes
   const uint32_t tok = (uint32_t)a.hkv * kRowBytes;                  // K row stride in the cache
@@ -504,9 +508,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.col_idx + kbeg), (short)0, nexact * 4, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rpt =
       __builtin_amdgcn_make_buffer_rsrc((void*)pt, (short)0, a.max_pages * 4, kBufferFlags);
-  auto page_of = [&](int J) -> int {  // page of rows 16w.. of block J (valid after the next barrier)
+  auto page_of = [&](int J, int hh) -> int {  // page of rows 32w + 16hh.. of block J (valid after the next barrier)
     int pi, slot;
-    a.pm.split(min(J * kBlk + 16 * wave, T - 1), pi, slot);
+    a.pm.split(min(J * kBlk + 32 * wave + 16 * hh, T - 1), pi, slot);
     return __builtin_amdgcn_raw_buffer_load_b32(rpt, pi * 4, 0, 0);
   };
   // a value loaded before the last barrier, read as a wave-uniform scalar there
@@ -515,26 +519,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     asm volatile("" : "+v"(v));
     return __builtin_amdgcn_readfirstlane(v);
   };
-  int pgu = 0;  // page of rows 16w.. of the exact tile being moved (uniform)
+  int pgu[2] = {0, 0};  // pages of the two 16-row halves of the exact tile being moved (uniform)
   auto lds = [](uint8_t* p) { return (__attribute__((address_space(3))) void*)p; };
-  auto dma = [&](int idx, int j, uint8_t* Kd, uint8_t* Vd) {
-    uint8_t* kd = Kd + 4 * wave * kGS;
-    uint8_t* vd = Vd + 4 * wave * kGS;
+  auto dma = [&](int idx, int j, uint8_t* Kd, uint8_t* Vd) __attribute__((always_inline)) {
+    uint8_t* kd = Kd + 8 * wave * kGS;
+    uint8_t* vd = Vd + 8 * wave * kGS;
     if (idx < nexact) {
-      const uint8_t* vsrc = a.vt + (((int64_t)g * a.total_kblocks + kb0 + j) * kBlk + 16 * wave) * kRowBytes + voff;
-      const int r0 = j * kBlk + 16 * wave;
-      if (pages16 && r0 + 15 < T) {
-        int pi, slot;
-        a.pm.split(r0, pi, slot);
-        const uint8_t* kb = a.k_pages + (((int64_t)pgu * a.page_size + slot) * a.hkv + g) * kRowBytes;
+      const uint8_t* vsrc = a.vt + (((int64_t)g * a.total_kblocks + kb0 + j) * kBlk + 32 * wave) * kRowBytes + voff;
+      const int r0 = j * kBlk + 32 * wave;
+      if (pages16 && r0 + 31 < T) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          __builtin_amdgcn_global_load_lds(kb + koff + 4 * p * tok, lds(kd + p * kGS), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
+        for (int hh = 0; hh < 2; ++hh) {
+          int pi, slot;
+          a.pm.split(r0 + 16 * hh, pi, slot);
+          const uint8_t* kb = a.k_pages + (((int64_t)pgu[hh] * a.page_size + slot) * a.hkv + g) * kRowBytes + koff;
+#pragma unroll
+          for (int p = 4 * hh; p < 4 * hh + 4; ++p) {
+            __builtin_amdgcn_global_load_lds(kb + 4 * (p - 4 * hh) * tok, lds(kd + p * kGS), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
+          }
         }
       } else {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < 8; ++p) {
           int pi, slot;
           a.pm.split(min(r0 + 4 * p + (lane >> 4), T - 1), pi, slot);  // rows past the end repeat the last key
           const uint8_t* ksrc = a.k_pages + (((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g) * kRowBytes + uoff;
@@ -544,19 +551,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
       }
     } else {
       const uint8_t* vsrc =
-          a.vbt + (((int64_t)g * a.mt_cap + kb0 / kBlk + s + j / kBlk) * kBlk + 16 * wave) * kRowBytes + voff;
+          a.vbt + (((int64_t)g * a.mt_cap + kb0 / kBlk + s + j / kBlk) * kBlk + 32 * wave) * kRowBytes + voff;
       const uint8_t* k16 = reinterpret_cast<const uint8_t*>(a.kbar16);
-      const int r0 = j + 16 * wave;
-      if (r0 + 15 < diag) {
+      const int r0 = j + 32 * wave;
+      if (r0 + 31 < diag) {
         const uint8_t* kb = k16 + (mrow0 + r0) * kRowBytes + voff;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < 8; ++p) {
           __builtin_amdgcn_global_load_lds(kb + 1024 * p, lds(kd + p * kGS), 16, 0, 0);
           __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
         }
       } else {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < 8; ++p) {
           const int jm = min(r0 + 4 * p + (lane >> 4), diag - 1);  // tokens past diag repeat a real one (masked)
           __builtin_amdgcn_global_load_lds(k16 + (mrow0 + jm) * kRowBytes + uoff, lds(kd + p * kGS), 16, 0, 0);
           __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
@@ -574,21 +581,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
 
   // Tile pipeline: at iteration i the LDS buffers i%2 hold tile i and the
   // DMA of tile i+1 into the other buffers is in flight; the block index of
-  // tile i+2 and the page entry of tile i+1 arrived with the last barrier,
-  // the loads of tile i+3's block index and tile i+2's page entry are in
+  // tile i+2 and the page entries of tile i+1 arrived with the last barrier,
+  // the loads of tile i+3's block index and tile i+2's page entries are in
   // flight.
   auto mean_of = [&](int idx) -> int { return idx < ntiles ? mtile[idx - nexact] : 0; };
-  int j0 = 0, j1 = 0, j2v = 0, pgv = 0;
+  int j0 = 0, j1 = 0, j2v = 0, pgv[2] = {0, 0};
   if (0 < nexact) j0 = ld_uniform(a.col_idx, kbeg);
   else if (0 < ntiles) j0 = mean_of(0);
   if (1 < nexact) j1 = ld_uniform(a.col_idx, kbeg + 1);
   else if (1 < ntiles) j1 = mean_of(1);
   if (2 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 2 * 4, 0, 0);
-  if (ntiles > 0) {
-    if (nexact > 0) pgu = __builtin_amdgcn_readfirstlane(page_of(j0));
-    dma(0, j0, K0, V0);
+  if (mover) {
+    if (ntiles > 0) {
+      if (nexact > 0) {
+        pgu[0] = __builtin_amdgcn_readfirstlane(page_of(j0, 0));
+        pgu[1] = __builtin_amdgcn_readfirstlane(page_of(j0, 1));
+      }
+      dma(0, j0, K0, V0);
+    }
+    if (1 < nexact) {
+      pgv[0] = page_of(j1, 0);
+      pgv[1] = page_of(j1, 1);
+    }
   }
-  if (1 < nexact) pgv = page_of(j1);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   const float scl = a.scale_log2;
@@ -596,9 +611,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
 
   auto iter = [&](int idx, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
     const int j2 = idx + 2 < nexact ? after_barrier(j2v) : mean_of(idx + 2);
-    if (idx + 1 < nexact) pgu = after_barrier(pgv);
-    if (idx + 1 < ntiles) dma(idx + 1, j1, Kn, Vn);
-    if (idx + 2 < nexact) pgv = page_of(j2);
+    if (mover) {
+      if (idx + 1 < nexact) {
+        pgu[0] = after_barrier(pgv[0]);
+        pgu[1] = after_barrier(pgv[1]);
+      }
+      if (idx + 1 < ntiles) dma(idx + 1, j1, Kn, Vn);
+      if (idx + 2 < nexact) {
+        pgv[0] = page_of(j2, 0);
+        pgv[1] = page_of(j2, 1);
+      }
+    }
     if (idx + 3 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, (idx + 3) * 4, 0, 0);
     if (wave_active) {
       const int mode = idx >= nexact ? 2 : (j0 == diag ? 1 : 0);
