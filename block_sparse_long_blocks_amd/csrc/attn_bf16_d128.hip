@@ -383,6 +383,140 @@ struct Wave {
     FP2_PATTERN_8;
     __builtin_amdgcn_sched_barrier(0);
   }
+
+  // ---- exact tiles on a fixed instruction schedule ----
+  //
+  // The 64 MFMAs of a tile run in the order QK(0) | QK(1) | QK(2),PV(0)
+  // alternating | QK(3),PV(1) alternating | PV(2) | PV(3) (op n = 0..63, six
+  // regions of 8, 8, 16, 16, 8, 8).  Each op is one slot closed by a
+  // scheduling barrier, so the order below is the issue order: op n's LDS
+  // operand is read kLA slots ahead (across regions), and the softmax of
+  // step j runs in region j+1 as a stream of groups spread over the slots,
+  // each value produced a group or more before it is consumed, so that no
+  // vector instruction waits on the one just before it and the matrix core
+  // keeps getting work.  The refresh test of step j closes region j+1,
+  // before PV(j) reads P(j).
+  static constexpr int kLA = 4;
+  static constexpr int kGroups = 20;
+  static constexpr int kDma0 = 8;  // the next tile's eight DMA instructions go out after ops 9, 11, .., 23
+
+  __device__ static constexpr bool op_qk(int n) { return n < 16 || (n < 48 && (n & 1) == 0); }
+  __device__ static constexpr int op_step(int n) {
+    return op_qk(n) ? (n < 8 ? 0 : n < 16 ? 1 : n < 32 ? 2 : 3) : (n < 32 ? 0 : n < 48 ? 1 : n < 56 ? 2 : 3);
+  }
+  // QK: d-slice kk; PV: 4 r + dt
+  __device__ static constexpr int op_idx(int n) { return n < 16 ? (n & 7) : n < 48 ? ((n & 15) >> 1) : (n & 7); }
+
+  __device__ __forceinline__ const uint8_t* op_addr(int n, const uint8_t* Kt, const uint8_t* Vt, int off0,
+                                                    int off1) const {
+    const int j = op_step(n), i = op_idx(n);
+    if (op_qk(n)) return Kt + ((i & 1) ? off1 : off0) + 8 * kGS * j + 64 * (i >> 1);
+    return Vt + ((i >> 2) ? off1 : off0) + 8 * kGS * (i & 3) + 64 * j;
+  }
+
+  // softmax stream of one step: group g computes x[g] (g < 16), e[g-2]
+  // (2 <= g < 18), the bf16 pair w[(g-4)/2] (even g >= 4) and adds e[g-4]
+  // to the row sum (g >= 4)
+  struct Soft {
+    float x[16], e[16], acc[2];
+    uint32_t w[8];
+  };
+  __device__ __forceinline__ void soft_group(int g, Soft& st, const f32x16& s, float scl) const {
+    if (g < 16) {
+      st.x[g] = __builtin_fmaf(s[g], scl, nb);
+      asm volatile("" : "+v"(st.x[g]));
+    }
+    if (g >= 2 && g < 18) {
+      st.e[g - 2] = __builtin_amdgcn_exp2f(st.x[g - 2]);
+      asm volatile("" : "+v"(st.e[g - 2]));
+    }
+    if (g >= 4 && g < 20 && (g & 1) == 0) {
+      st.w[(g - 4) >> 1] = pack_bf16x2(st.e[g - 4], st.e[g - 3]);
+      asm volatile("" : "+v"(st.w[(g - 4) >> 1]));
+    }
+    if (g >= 4 && g < 20) {
+      st.acc[g & 1] += st.e[g - 4];
+      asm volatile("" : "+v"(st.acc[g & 1]));
+    }
+  }
+
+  // one region: ops [n0, n0 + S), with the softmax stream of s when SOFT
+  template <int N0, int S, bool SOFT, class Dma>
+  __device__ __forceinline__ void region(bf16x8 (&fr)[8], f32x16& sn, const bf16x8 (&pp)[2], Soft& st,
+                                         const f32x16& s, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1,
+                                         float scl, Dma& dma) {
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      const int n = N0 + t;
+      if (op_qk(n)) {
+        sn = mfma_bf16_32x32x16(fr[n & 7], qf[op_idx(n)], sn);
+      } else {
+        const int i = op_idx(n);
+        o[i & 3] = mfma_bf16_32x32x16(fr[n & 7], pp[i >> 2], o[i & 3]);
+      }
+      if (n + kLA < 64) fr[(n + kLA) & 7] = *reinterpret_cast<const bf16x8*>(op_addr(n + kLA, Kt, Vt, off0, off1));
+      if (n >= kDma0 && n < kDma0 + 16 && ((n - kDma0) & 1)) dma((n - kDma0) >> 1);
+      if constexpr (SOFT) {
+#pragma unroll
+        for (int g = t * kGroups / S; g < (t + 1) * kGroups / S; ++g) soft_group(g, st, s, scl);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // closes the softmax of a step: P, l, and the refresh when the step's
+  // probabilities reached kPmax (or it is the first step of the row)
+  __device__ __forceinline__ void soft_close(Soft& st, const f32x16& s, float scl, bool force, bf16x8 (&pc)[2]) {
+    pc[0] = __builtin_bit_cast(bf16x8, make_uint4(st.w[0], st.w[1], st.w[2], st.w[3]));
+    pc[1] = __builtin_bit_cast(bf16x8, make_uint4(st.w[4], st.w[5], st.w[6], st.w[7]));
+    const float step = st.acc[0] + st.acc[1];
+    const float l_prev = l;
+    l += step;
+    if (__any(!(step < kPmax)) || force) refresh(s, scl, l_prev, pc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  template <class Dma>
+  __device__ __forceinline__ void tile_fast(bool first, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1,
+                                            float scl, Dma&& dma) {
+    bf16x8 fr[8];
+    bf16x8 pp[2] = {qf[0], qf[0]}, pc[2];
+    f32x16 s = f32x16{}, sn = f32x16{};
+    Soft st;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < kLA; ++n) fr[n] = *reinterpret_cast<const bf16x8*>(op_addr(n, Kt, Vt, off0, off1));
+    __builtin_amdgcn_sched_barrier(0);
+    region<0, 8, false>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // QK(0)
+    s = sn;
+    sn = f32x16{};
+    st.acc[0] = st.acc[1] = 0.f;
+    region<8, 8, true>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // QK(1), softmax(0)
+    soft_close(st, s, scl, first, pc);
+    pp[0] = pc[0];
+    pp[1] = pc[1];
+    s = sn;
+    sn = f32x16{};
+    st.acc[0] = st.acc[1] = 0.f;
+    region<16, 16, true>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // QK(2), PV(0), softmax(1)
+    soft_close(st, s, scl, false, pc);
+    pp[0] = pc[0];
+    pp[1] = pc[1];
+    s = sn;
+    sn = f32x16{};
+    st.acc[0] = st.acc[1] = 0.f;
+    region<32, 16, true>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // QK(3), PV(1), softmax(2)
+    soft_close(st, s, scl, false, pc);
+    pp[0] = pc[0];
+    pp[1] = pc[1];
+    s = sn;
+    st.acc[0] = st.acc[1] = 0.f;
+    region<48, 8, true>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // PV(2), softmax(3)
+    soft_close(st, s, scl, false, pc);
+    pp[0] = pc[0];
+    pp[1] = pc[1];
+    region<56, 8, false>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // PV(3)
+  }
 };
 
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a) {
@@ -484,16 +618,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     }
   }
 
-  // ---- DMA of one tile, issued by waves 0-3 only (one per SIMD): while a
-  // wave waits to issue its share into the memory pipeline, the other wave on
-  // its SIMD keeps the matrix core busy.  Wave w < 4 moves rows 32w .. 32w+31
-  // (row groups 8w .. 8w+7) of the K and the V^T tile; lane i of group 8w+p
-  // moves row 32w + 4p + i/16, chunk (i%16) ^ (i/16), into its 16-byte slot.
-  // When each 16-row half lies in one page (page size a multiple of 16, rows
-  // inside the sequence) the address is a wave-uniform base plus per-lane
-  // offsets fixed for the whole kernel; otherwise each lane looks up its own
-  // page.
-  const bool mover = wave < 4;
+  // ---- DMA of one tile: wave w moves rows 16w .. 16w+15 (LDS row groups
+  // 4w .. 4w+3) of the K and the V^T tile, four instructions each; lane i of
+  // instruction p moves row 16w + 4p + i/16, chunk (i%16) ^ (i/16), into its
+  // 16-byte slot.  On the fast paths (the 16 rows lie in one page and inside
+  // the sequence, or are 16 whole mean tokens below the diagonal) the source
+  // of instruction p is a wave-uniform base plus p times a uniform step plus
+  // a per-lane offset fixed for the kernel, and exact tiles issue the eight
+  // instructions one by one between their MFMAs; otherwise each lane looks up
+  // its own row and all eight go out at once.
   const int uoff = 16 * ((lane & 15) ^ (lane >> 4));
   const uint32_t voff = (uint32_t)((lane >> 4) * kRowBytes + uoff);  // + 1024 p: rows of 256 bytes
   const uint32_t tok = (uint32_t)a.hkv * kRowBytes;                  // K row stride in the cache
@@ -508,9 +641,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.col_idx + kbeg), (short)0, nexact * 4, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rpt =
       __builtin_amdgcn_make_buffer_rsrc((void*)pt, (short)0, a.max_pages * 4, kBufferFlags);
-  auto page_of = [&](int J, int hh) -> int {  // page of rows 32w + 16hh.. of block J (valid after the next barrier)
+  auto page_of = [&](int J) -> int {  // page of rows 16w.. of block J (valid after the next barrier)
     int pi, slot;
-    a.pm.split(min(J * kBlk + 32 * wave + 16 * hh, T - 1), pi, slot);
+    a.pm.split(min(J * kBlk + 16 * wave, T - 1), pi, slot);
     return __builtin_amdgcn_raw_buffer_load_b32(rpt, pi * 4, 0, 0);
   };
   // a value loaded before the last barrier, read as a wave-uniform scalar there
@@ -519,57 +652,67 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     asm volatile("" : "+v"(v));
     return __builtin_amdgcn_readfirstlane(v);
   };
-  int pgu[2] = {0, 0};  // pages of the two 16-row halves of the exact tile being moved (uniform)
   auto lds = [](uint8_t* p) { return (__attribute__((address_space(3))) void*)p; };
-  auto dma = [&](int idx, int j, uint8_t* Kd, uint8_t* Vd) __attribute__((always_inline)) {
-    uint8_t* kd = Kd + 8 * wave * kGS;
-    uint8_t* vd = Vd + 8 * wave * kGS;
+  // the fast-path sources of one tile (instruction p: kb + p * kstep + kvo, vb + 1024 p + voff)
+  struct DmaPlan {
+    const uint8_t* kb;
+    const uint8_t* vb;
+    uint32_t kstep, kvo;
+    bool fast;
+  };
+  // Plans the DMA of tile idx (block or mean token j, page entry pg of this
+  // wave's rows) into Kd / Vd; slow paths are issued here.
+  auto plan = [&](int idx, int j, int pg, uint8_t* Kd, uint8_t* Vd) __attribute__((always_inline)) {
+    DmaPlan pl;
+    uint8_t* kd = Kd + 4 * wave * kGS;
+    uint8_t* vd = Vd + 4 * wave * kGS;
     if (idx < nexact) {
-      const uint8_t* vsrc = a.vt + (((int64_t)g * a.total_kblocks + kb0 + j) * kBlk + 32 * wave) * kRowBytes + voff;
-      const int r0 = j * kBlk + 32 * wave;
-      if (pages16 && r0 + 31 < T) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          int pi, slot;
-          a.pm.split(r0 + 16 * hh, pi, slot);
-          const uint8_t* kb = a.k_pages + (((int64_t)pgu[hh] * a.page_size + slot) * a.hkv + g) * kRowBytes + koff;
-#pragma unroll
-          for (int p = 4 * hh; p < 4 * hh + 4; ++p) {
-            __builtin_amdgcn_global_load_lds(kb + 4 * (p - 4 * hh) * tok, lds(kd + p * kGS), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
-          }
-        }
+      pl.vb = a.vt + (((int64_t)g * a.total_kblocks + kb0 + j) * kBlk + 16 * wave) * kRowBytes;
+      const int r0 = j * kBlk + 16 * wave;
+      pl.fast = pages16 && r0 + 15 < T;
+      if (pl.fast) {
+        int pi, slot;
+        a.pm.split(r0, pi, slot);
+        pl.kb = a.k_pages + (((int64_t)pg * a.page_size + slot) * a.hkv + g) * kRowBytes;
+        pl.kstep = 4 * tok;
+        pl.kvo = koff;
       } else {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
+        for (int p = 0; p < 4; ++p) {
           int pi, slot;
           a.pm.split(min(r0 + 4 * p + (lane >> 4), T - 1), pi, slot);  // rows past the end repeat the last key
           const uint8_t* ksrc = a.k_pages + (((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g) * kRowBytes + uoff;
           __builtin_amdgcn_global_load_lds(ksrc, lds(kd + p * kGS), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(pl.vb + voff + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
         }
       }
     } else {
-      const uint8_t* vsrc =
-          a.vbt + (((int64_t)g * a.mt_cap + kb0 / kBlk + s + j / kBlk) * kBlk + 32 * wave) * kRowBytes + voff;
+      pl.vb = a.vbt + (((int64_t)g * a.mt_cap + kb0 / kBlk + s + j / kBlk) * kBlk + 16 * wave) * kRowBytes;
       const uint8_t* k16 = reinterpret_cast<const uint8_t*>(a.kbar16);
-      const int r0 = j + 32 * wave;
-      if (r0 + 31 < diag) {
-        const uint8_t* kb = k16 + (mrow0 + r0) * kRowBytes + voff;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          __builtin_amdgcn_global_load_lds(kb + 1024 * p, lds(kd + p * kGS), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
-        }
+      const int r0 = j + 16 * wave;
+      pl.fast = r0 + 15 < diag;
+      if (pl.fast) {
+        pl.kb = k16 + (mrow0 + r0) * kRowBytes;
+        pl.kstep = 1024;
+        pl.kvo = voff;
       } else {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
+        for (int p = 0; p < 4; ++p) {
           const int jm = min(r0 + 4 * p + (lane >> 4), diag - 1);  // tokens past diag repeat a real one (masked)
           __builtin_amdgcn_global_load_lds(k16 + (mrow0 + jm) * kRowBytes + uoff, lds(kd + p * kGS), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vsrc + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(pl.vb + voff + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
         }
       }
     }
+    return pl;
+  };
+  // instruction i of a fast plan: K row group i/2 (even i) or V^T row group i/2 (odd i)
+  auto issue = [&](const DmaPlan& pl, int i, uint8_t* Kd, uint8_t* Vd) __attribute__((always_inline)) {
+    const int p = i >> 1;
+    if ((i & 1) == 0)
+      __builtin_amdgcn_global_load_lds(pl.kb + p * pl.kstep + pl.kvo, lds(Kd + (4 * wave + p) * kGS), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(pl.vb + 1024 * p + voff, lds(Vd + (4 * wave + p) * kGS), 16, 0, 0);
   };
 
   // per-lane operand offsets (see Wave::qk / Wave::pv): row l%32 of a 32-row
@@ -585,25 +728,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   // the loads of tile i+3's block index and tile i+2's page entries are in
   // flight.
   auto mean_of = [&](int idx) -> int { return idx < ntiles ? mtile[idx - nexact] : 0; };
-  int j0 = 0, j1 = 0, j2v = 0, pgv[2] = {0, 0};
+  int j0 = 0, j1 = 0, j2v = 0, pgv = 0;
   if (0 < nexact) j0 = ld_uniform(a.col_idx, kbeg);
   else if (0 < ntiles) j0 = mean_of(0);
   if (1 < nexact) j1 = ld_uniform(a.col_idx, kbeg + 1);
   else if (1 < ntiles) j1 = mean_of(1);
   if (2 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 2 * 4, 0, 0);
-  if (mover) {
-    if (ntiles > 0) {
-      if (nexact > 0) {
-        pgu[0] = __builtin_amdgcn_readfirstlane(page_of(j0, 0));
-        pgu[1] = __builtin_amdgcn_readfirstlane(page_of(j0, 1));
-      }
-      dma(0, j0, K0, V0);
-    }
-    if (1 < nexact) {
-      pgv[0] = page_of(j1, 0);
-      pgv[1] = page_of(j1, 1);
+  if (ntiles > 0) {
+    const int pg0 = 0 < nexact ? __builtin_amdgcn_readfirstlane(page_of(j0)) : 0;
+    const DmaPlan pl = plan(0, j0, pg0, K0, V0);
+    if (pl.fast) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) issue(pl, i, K0, V0);
     }
   }
+  if (1 < nexact) pgv = page_of(j1);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   const float scl = a.scale_log2;
@@ -611,24 +750,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
 
   auto iter = [&](int idx, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
     const int j2 = idx + 2 < nexact ? after_barrier(j2v) : mean_of(idx + 2);
-    if (mover) {
-      if (idx + 1 < nexact) {
-        pgu[0] = after_barrier(pgv[0]);
-        pgu[1] = after_barrier(pgv[1]);
-      }
-      if (idx + 1 < ntiles) dma(idx + 1, j1, Kn, Vn);
-      if (idx + 2 < nexact) {
-        pgv[0] = page_of(j2, 0);
-        pgv[1] = page_of(j2, 1);
-      }
-    }
+    DmaPlan pl;
+    pl.fast = false;
+    if (idx + 1 < ntiles) pl = plan(idx + 1, j1, idx + 1 < nexact ? after_barrier(pgv) : 0, Kn, Vn);
+    if (idx + 2 < nexact) pgv = page_of(j2);
     if (idx + 3 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, (idx + 3) * 4, 0, 0);
-    if (wave_active) {
-      const int mode = idx >= nexact ? 2 : (j0 == diag ? 1 : 0);
-      if (mode)
-        ws.tile<true>(mode, idx == 0, Kc, Vc, off0, off1, hf, scl, cb, tq, j0, diag, kept);
-      else
-        ws.tile<false>(0, idx == 0, Kc, Vc, off0, off1, hf, scl, cb, tq, j0, diag, kept);
+    const int mode = idx >= nexact ? 2 : (j0 == diag ? 1 : 0);
+    if (mode == 0 && wave_active) {
+      ws.tile_fast(idx == 0, Kc, Vc, off0, off1, scl, [&](int i) __attribute__((always_inline)) {
+        if (pl.fast) issue(pl, i, Kn, Vn);
+      });
+    } else {
+      if (pl.fast) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) issue(pl, i, Kn, Vn);
+      }
+      if (wave_active) ws.tile<true>(mode, idx == 0, Kc, Vc, off0, off1, hf, scl, cb, tq, j0, diag, kept);
     }
     j0 = j1;
     j1 = j2;
