@@ -51,6 +51,13 @@ constexpr int kRowBytes = kD * 2;            // a K row (d values) or a V^T row 
 constexpr int kGS = 4 * kRowBytes + 64;      // LDS stride of a 4-row group
 constexpr int kTileLds = (kBlk / 4) * kGS;   // one K or V^T tile in LDS
 constexpr int kTileGlobal = kBlk * kRowBytes;  // one V^T tile in global memory
+// tile DMA: waves 0 .. kDmaWaves-1 each move kDmaRows rows of the K and the
+// V^T tile (kDmaInstr instructions, K and V^T alternating)
+constexpr int kDmaWaves = 4;
+constexpr int kDmaRows = kBlk / kDmaWaves;
+constexpr int kDmaHalves = kDmaRows / 16;
+constexpr int kDmaInstr = kDmaRows / 2;
+constexpr int kDmaSlotStep = 16 / kDmaInstr;
 
 // Position p of a V^T row holds key key_of_pos(p): within each group of 16,
 // positions 0-7 hold keys {0-3, 8-11} and positions 8-15 keys {4-7, 12-15},
@@ -398,7 +405,7 @@ struct Wave {
   // before PV(j) reads P(j).
   static constexpr int kLA = 4;
   static constexpr int kGroups = 20;
-  static constexpr int kDma0 = 8;  // the next tile's eight DMA instructions go out after ops 9, 11, .., 23
+  static constexpr int kDma0 = 8;  // the next tile's DMA instructions go out from op 8 on, kDmaSlotStep apart
 
   __device__ static constexpr bool op_qk(int n) { return n < 16 || (n < 48 && (n & 1) == 0); }
   __device__ static constexpr int op_step(int n) {
@@ -455,7 +462,8 @@ struct Wave {
         o[i & 3] = mfma_bf16_32x32x16(fr[n & 7], pp[i >> 2], o[i & 3]);
       }
       if (n + kLA < 64) fr[(n + kLA) & 7] = *reinterpret_cast<const bf16x8*>(op_addr(n + kLA, Kt, Vt, off0, off1));
-      if (n >= kDma0 && n < kDma0 + 16 && ((n - kDma0) & 1)) dma((n - kDma0) >> 1);
+      if (n >= kDma0 && n < kDma0 + kDmaInstr * kDmaSlotStep && (n - kDma0) % kDmaSlotStep == kDmaSlotStep - 1)
+        dma((n - kDma0) / kDmaSlotStep);
       if constexpr (SOFT) {
 #pragma unroll
         for (int g = t * kGroups / S; g < (t + 1) * kGroups / S; ++g) soft_group(g, st, s, scl);
@@ -618,15 +626,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     }
   }
 
-  // ---- DMA of one tile: wave w moves rows 16w .. 16w+15 (LDS row groups
-  // 4w .. 4w+3) of the K and the V^T tile, four instructions each; lane i of
-  // instruction p moves row 16w + 4p + i/16, chunk (i%16) ^ (i/16), into its
-  // 16-byte slot.  On the fast paths (the 16 rows lie in one page and inside
-  // the sequence, or are 16 whole mean tokens below the diagonal) the source
-  // of instruction p is a wave-uniform base plus p times a uniform step plus
-  // a per-lane offset fixed for the kernel, and exact tiles issue the eight
-  // instructions one by one between their MFMAs; otherwise each lane looks up
-  // its own row and all eight go out at once.
+  // ---- DMA of one tile: wave w < kDmaWaves moves rows R w .. R w + R-1
+  // (R = kDmaRows; LDS row groups R w/4 ..) of the K and the V^T tile, R/4
+  // instructions each; lane i of instruction p moves row R w + 4p + i/16,
+  // chunk (i%16) ^ (i/16), into its 16-byte slot.  On the fast paths (each 16
+  // rows lie in one page and all inside the sequence, or they are whole mean
+  // tokens below the diagonal) the source of instruction p is a wave-uniform
+  // base per 16 rows plus a uniform step plus a per-lane offset fixed for the
+  // kernel, and exact tiles issue the instructions one by one between their
+  // MFMAs; otherwise each lane looks up its own row and all go out at once.
+  const bool dma_wave = wave < kDmaWaves;
   const int uoff = 16 * ((lane & 15) ^ (lane >> 4));
   const uint32_t voff = (uint32_t)((lane >> 4) * kRowBytes + uoff);  // + 1024 p: rows of 256 bytes
   const uint32_t tok = (uint32_t)a.hkv * kRowBytes;                  // K row stride in the cache
@@ -641,9 +650,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.col_idx + kbeg), (short)0, nexact * 4, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rpt =
       __builtin_amdgcn_make_buffer_rsrc((void*)pt, (short)0, a.max_pages * 4, kBufferFlags);
-  auto page_of = [&](int J) -> int {  // page of rows 16w.. of block J (valid after the next barrier)
+  auto page_of = [&](int J, int hh) -> int {  // page of rows R w + 16 hh.. of block J (valid after the next barrier)
     int pi, slot;
-    a.pm.split(min(J * kBlk + 16 * wave, T - 1), pi, slot);
+    a.pm.split(min(J * kBlk + kDmaRows * wave + 16 * hh, T - 1), pi, slot);
     return __builtin_amdgcn_raw_buffer_load_b32(rpt, pi * 4, 0, 0);
   };
   // a value loaded before the last barrier, read as a wave-uniform scalar there
@@ -655,30 +664,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   auto lds = [](uint8_t* p) { return (__attribute__((address_space(3))) void*)p; };
   // the fast-path sources of one tile (instruction p: kb + p * kstep + kvo, vb + 1024 p + voff)
   struct DmaPlan {
-    const uint8_t* kb;
+    const uint8_t* kb[kDmaHalves];
     const uint8_t* vb;
     uint32_t kstep, kvo;
     bool fast;
   };
   // Plans the DMA of tile idx (block or mean token j, page entry pg of this
   // wave's rows) into Kd / Vd; slow paths are issued here.
-  auto plan = [&](int idx, int j, int pg, uint8_t* Kd, uint8_t* Vd) __attribute__((always_inline)) {
+  auto plan = [&](int idx, int j, const int (&pg)[kDmaHalves], uint8_t* Kd, uint8_t* Vd) __attribute__((always_inline)) {
     DmaPlan pl;
-    uint8_t* kd = Kd + 4 * wave * kGS;
-    uint8_t* vd = Vd + 4 * wave * kGS;
+    pl.fast = false;
+    if (!dma_wave) return pl;
+    uint8_t* kd = Kd + (kDmaRows / 4) * wave * kGS;
+    uint8_t* vd = Vd + (kDmaRows / 4) * wave * kGS;
     if (idx < nexact) {
-      pl.vb = a.vt + (((int64_t)g * a.total_kblocks + kb0 + j) * kBlk + 16 * wave) * kRowBytes;
-      const int r0 = j * kBlk + 16 * wave;
-      pl.fast = pages16 && r0 + 15 < T;
+      pl.vb = a.vt + (((int64_t)g * a.total_kblocks + kb0 + j) * kBlk + kDmaRows * wave) * kRowBytes;
+      const int r0 = j * kBlk + kDmaRows * wave;
+      pl.fast = pages16 && r0 + kDmaRows - 1 < T;
       if (pl.fast) {
-        int pi, slot;
-        a.pm.split(r0, pi, slot);
-        pl.kb = a.k_pages + (((int64_t)pg * a.page_size + slot) * a.hkv + g) * kRowBytes;
+#pragma unroll
+        for (int hh = 0; hh < kDmaHalves; ++hh) {
+          int pi, slot;
+          a.pm.split(r0 + 16 * hh, pi, slot);
+          pl.kb[hh] = a.k_pages + (((int64_t)pg[hh] * a.page_size + slot) * a.hkv + g) * kRowBytes;
+        }
         pl.kstep = 4 * tok;
         pl.kvo = koff;
       } else {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < kDmaRows / 4; ++p) {
           int pi, slot;
           a.pm.split(min(r0 + 4 * p + (lane >> 4), T - 1), pi, slot);  // rows past the end repeat the last key
           const uint8_t* ksrc = a.k_pages + (((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g) * kRowBytes + uoff;
@@ -687,17 +701,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
         }
       }
     } else {
-      pl.vb = a.vbt + (((int64_t)g * a.mt_cap + kb0 / kBlk + s + j / kBlk) * kBlk + 16 * wave) * kRowBytes;
+      pl.vb = a.vbt + (((int64_t)g * a.mt_cap + kb0 / kBlk + s + j / kBlk) * kBlk + kDmaRows * wave) * kRowBytes;
       const uint8_t* k16 = reinterpret_cast<const uint8_t*>(a.kbar16);
-      const int r0 = j + 16 * wave;
-      pl.fast = r0 + 15 < diag;
+      const int r0 = j + kDmaRows * wave;
+      pl.fast = r0 + kDmaRows - 1 < diag;
       if (pl.fast) {
-        pl.kb = k16 + (mrow0 + r0) * kRowBytes;
+#pragma unroll
+        for (int hh = 0; hh < kDmaHalves; ++hh) pl.kb[hh] = k16 + (mrow0 + r0 + 16 * hh) * kRowBytes;
         pl.kstep = 1024;
         pl.kvo = voff;
       } else {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < kDmaRows / 4; ++p) {
           const int jm = min(r0 + 4 * p + (lane >> 4), diag - 1);  // tokens past diag repeat a real one (masked)
           __builtin_amdgcn_global_load_lds(k16 + (mrow0 + jm) * kRowBytes + uoff, lds(kd + p * kGS), 16, 0, 0);
           __builtin_amdgcn_global_load_lds(pl.vb + voff + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
@@ -709,10 +724,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   // instruction i of a fast plan: K row group i/2 (even i) or V^T row group i/2 (odd i)
   auto issue = [&](const DmaPlan& pl, int i, uint8_t* Kd, uint8_t* Vd) __attribute__((always_inline)) {
     const int p = i >> 1;
+    const int grp = (kDmaRows / 4) * wave + p;
     if ((i & 1) == 0)
-      __builtin_amdgcn_global_load_lds(pl.kb + p * pl.kstep + pl.kvo, lds(Kd + (4 * wave + p) * kGS), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(pl.kb[p >> 2] + (p & 3) * pl.kstep + pl.kvo, lds(Kd + grp * kGS), 16, 0, 0);
     else
-      __builtin_amdgcn_global_load_lds(pl.vb + 1024 * p + voff, lds(Vd + (4 * wave + p) * kGS), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(pl.vb + 1024 * p + voff, lds(Vd + grp * kGS), 16, 0, 0);
   };
 
   // per-lane operand offsets (see Wave::qk / Wave::pv): row l%32 of a 32-row
@@ -728,21 +744,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   // the loads of tile i+3's block index and tile i+2's page entries are in
   // flight.
   auto mean_of = [&](int idx) -> int { return idx < ntiles ? mtile[idx - nexact] : 0; };
-  int j0 = 0, j1 = 0, j2v = 0, pgv = 0;
+  int j0 = 0, j1 = 0, j2v = 0, pgv[kDmaHalves] = {};
   if (0 < nexact) j0 = ld_uniform(a.col_idx, kbeg);
   else if (0 < ntiles) j0 = mean_of(0);
   if (1 < nexact) j1 = ld_uniform(a.col_idx, kbeg + 1);
   else if (1 < ntiles) j1 = mean_of(1);
   if (2 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 2 * 4, 0, 0);
   if (ntiles > 0) {
-    const int pg0 = 0 < nexact ? __builtin_amdgcn_readfirstlane(page_of(j0)) : 0;
+    int pg0[kDmaHalves] = {};
+    if (0 < nexact && dma_wave) {
+#pragma unroll
+      for (int hh = 0; hh < kDmaHalves; ++hh) pg0[hh] = __builtin_amdgcn_readfirstlane(page_of(j0, hh));
+    }
     const DmaPlan pl = plan(0, j0, pg0, K0, V0);
     if (pl.fast) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) issue(pl, i, K0, V0);
+      for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, K0, V0);
     }
   }
-  if (1 < nexact) pgv = page_of(j1);
+  if (1 < nexact && dma_wave) {
+#pragma unroll
+    for (int hh = 0; hh < kDmaHalves; ++hh) pgv[hh] = page_of(j1, hh);
+  }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   const float scl = a.scale_log2;
@@ -752,8 +775,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     const int j2 = idx + 2 < nexact ? after_barrier(j2v) : mean_of(idx + 2);
     DmaPlan pl;
     pl.fast = false;
-    if (idx + 1 < ntiles) pl = plan(idx + 1, j1, idx + 1 < nexact ? after_barrier(pgv) : 0, Kn, Vn);
-    if (idx + 2 < nexact) pgv = page_of(j2);
+    if (idx + 1 < ntiles) {
+      int pg[kDmaHalves] = {};
+      if (idx + 1 < nexact && dma_wave) {
+#pragma unroll
+        for (int hh = 0; hh < kDmaHalves; ++hh) pg[hh] = after_barrier(pgv[hh]);
+      }
+      pl = plan(idx + 1, j1, pg, Kn, Vn);
+    }
+    if (idx + 2 < nexact && dma_wave) {
+#pragma unroll
+      for (int hh = 0; hh < kDmaHalves; ++hh) pgv[hh] = page_of(j2, hh);
+    }
     if (idx + 3 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, (idx + 3) * 4, 0, 0);
     const int mode = idx >= nexact ? 2 : (j0 == diag ? 1 : 0);
     if (mode == 0 && wave_active) {
@@ -763,7 +796,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     } else {
       if (pl.fast) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) issue(pl, i, Kn, Vn);
+        for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, Kn, Vn);
       }
       if (wave_active) ws.tile<true>(mode, idx == 0, Kc, Vc, off0, off1, hf, scl, cb, tq, j0, diag, kept);
     }
