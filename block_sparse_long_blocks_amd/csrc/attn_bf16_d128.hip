@@ -31,6 +31,8 @@
 //    the softmax of step j, so matrix cores, LDS and vector ALU overlap
 //    within a wave.  Masks enter as the score accumulator's initial value;
 //    the reference max is refreshed lazily.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace fp2 {
@@ -428,9 +430,19 @@ struct Wave {
     float x[16], e[16], acc[2];
     uint32_t w[8];
   };
-  __device__ __forceinline__ void soft_group(int g, Soft& st, const f32x16& s, float scl) const {
+  // Masked tiles pass the per-lane bit mask M of the step's allowed keys
+  // (bit 8(i/4) + i%4 for element i) and nbm = nb + log2(B) on mean tiles:
+  // a masked element's exponent is -inf.
+  template <bool MASKED>
+  __device__ __forceinline__ void soft_group(int g, Soft& st, const f32x16& s, float scl, float nbm,
+                                             uint32_t M) const {
     if (g < 16) {
-      st.x[g] = __builtin_fmaf(s[g], scl, nb);
+      float x = __builtin_fmaf(s[g], scl, nbm);
+      if constexpr (MASKED) {
+        const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)M, 8 * (g >> 2) + (g & 3), 1);
+        x = __uint_as_float((sel & __float_as_uint(x)) | (~sel & 0xff800000u));
+      }
+      st.x[g] = x;
       asm volatile("" : "+v"(st.x[g]));
     }
     if (g >= 2 && g < 18) {
@@ -442,16 +454,18 @@ struct Wave {
       asm volatile("" : "+v"(st.w[(g - 4) >> 1]));
     }
     if (g >= 4 && g < 20) {
+      // the row sum adds the float32 probabilities (PV takes them rounded to
+      // bf16: O / l then errs by at most 2^-9 max|v| relative to exact P)
       st.acc[g & 1] += st.e[g - 4];
       asm volatile("" : "+v"(st.acc[g & 1]));
     }
   }
 
   // one region: ops [n0, n0 + S), with the softmax stream of s when SOFT
-  template <int N0, int S, bool SOFT, class Dma>
+  template <int N0, int S, bool SOFT, bool MASKED, class Dma>
   __device__ __forceinline__ void region(bf16x8 (&fr)[8], f32x16& sn, const bf16x8 (&pp)[2], Soft& st,
                                          const f32x16& s, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1,
-                                         float scl, Dma& dma) {
+                                         float scl, float nbm, uint32_t M, Dma& dma) {
 #pragma unroll
     for (int t = 0; t < S; ++t) {
       const int n = N0 + t;
@@ -466,7 +480,7 @@ struct Wave {
         dma((n - kDma0) / kDmaSlotStep);
       if constexpr (SOFT) {
 #pragma unroll
-        for (int g = t * kGroups / S; g < (t + 1) * kGroups / S; ++g) soft_group(g, st, s, scl);
+        for (int g = t * kGroups / S; g < (t + 1) * kGroups / S; ++g) soft_group<MASKED>(g, st, s, scl, nbm, M);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -474,56 +488,89 @@ struct Wave {
 
   // closes the softmax of a step: P, l, and the refresh when the step's
   // probabilities reached kPmax (or it is the first step of the row)
-  __device__ __forceinline__ void soft_close(Soft& st, const f32x16& s, float scl, bool force, bf16x8 (&pc)[2]) {
+  template <bool MASKED>
+  __device__ __forceinline__ void soft_close(Soft& st, const f32x16& s, float scl, bool force, bf16x8 (&pc)[2],
+                                             uint32_t M, float cbs) {
     pc[0] = __builtin_bit_cast(bf16x8, make_uint4(st.w[0], st.w[1], st.w[2], st.w[3]));
     pc[1] = __builtin_bit_cast(bf16x8, make_uint4(st.w[4], st.w[5], st.w[6], st.w[7]));
     const float step = st.acc[0] + st.acc[1];
     const float l_prev = l;
     l += step;
-    if (__any(!(step < kPmax)) || force) refresh(s, scl, l_prev, pc);
+    if (__any(!(step < kPmax)) || force) {
+      if constexpr (MASKED) {
+        f32x16 sm;  // the scores as the stream saw them: + cbs where allowed, -inf elsewhere
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sm[i] = (M >> (8 * (i >> 2) + (i & 3))) & 1u ? s[i] + cbs : -INFINITY;
+        refresh(sm, scl, l_prev, pc);
+      } else {
+        refresh(s, scl, l_prev, pc);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  template <class Dma>
+  // One tile.  MASKED: mode 1 diagonal block (key > query masked), mode 2
+  // mean-token tile starting at mean token J0 (only skipped blocks' tokens
+  // count, each with weight B: lb = log2 B added to the exponent, cbs = lb /
+  // scl in score units).
+  template <bool MASKED, class Dma>
   __device__ __forceinline__ void tile_fast(bool first, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1,
-                                            float scl, Dma&& dma) {
+                                            float scl, Dma&& dma, int mode, int tq, int hf, float lb, float cbs,
+                                            int J0, int diag, const uint32_t* kept) {
     bf16x8 fr[8];
     bf16x8 pp[2] = {qf[0], qf[0]}, pc[2];
     f32x16 s = f32x16{}, sn = f32x16{};
     Soft st;
+    uint32_t M[NS] = {};
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        if (mode == 0) {
+          M[j] = ~0u;
+        } else if (mode == 1) {
+          const int lim = tq - 32 * j - 4 * hf;  // element i allowed iff 8(i/4) + i%4 <= lim
+          M[j] = lim >= 31 ? ~0u : lim < 0 ? 0u : (2u << lim) - 1u;
+        } else {
+          M[j] = skipped_word(kept, (J0 >> 5) + j, diag) >> (4 * hf);
+        }
+      }
+    } else {
+      lb = 0.f;
+      cbs = 0.f;
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int n = 0; n < kLA; ++n) fr[n] = *reinterpret_cast<const bf16x8*>(op_addr(n, Kt, Vt, off0, off1));
     __builtin_amdgcn_sched_barrier(0);
-    region<0, 8, false>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // QK(0)
+    region<0, 8, false, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, 0.f, 0u, dma);  // QK(0)
     s = sn;
     sn = f32x16{};
     st.acc[0] = st.acc[1] = 0.f;
-    region<8, 8, true>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // QK(1), softmax(0)
-    soft_close(st, s, scl, first, pc);
-    pp[0] = pc[0];
-    pp[1] = pc[1];
-    s = sn;
-    sn = f32x16{};
-    st.acc[0] = st.acc[1] = 0.f;
-    region<16, 16, true>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // QK(2), PV(0), softmax(1)
-    soft_close(st, s, scl, false, pc);
+    region<8, 8, true, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, nb + lb, M[0], dma);  // QK(1), softmax(0)
+    soft_close<MASKED>(st, s, scl, first, pc, M[0], cbs);
     pp[0] = pc[0];
     pp[1] = pc[1];
     s = sn;
     sn = f32x16{};
     st.acc[0] = st.acc[1] = 0.f;
-    region<32, 16, true>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // QK(3), PV(1), softmax(2)
-    soft_close(st, s, scl, false, pc);
+    region<16, 16, true, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, nb + lb, M[1], dma);  // QK(2), PV(0), softmax(1)
+    soft_close<MASKED>(st, s, scl, false, pc, M[1], cbs);
+    pp[0] = pc[0];
+    pp[1] = pc[1];
+    s = sn;
+    sn = f32x16{};
+    st.acc[0] = st.acc[1] = 0.f;
+    region<32, 16, true, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, nb + lb, M[2], dma);  // QK(3), PV(1), softmax(2)
+    soft_close<MASKED>(st, s, scl, false, pc, M[2], cbs);
     pp[0] = pc[0];
     pp[1] = pc[1];
     s = sn;
     st.acc[0] = st.acc[1] = 0.f;
-    region<48, 8, true>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // PV(2), softmax(3)
-    soft_close(st, s, scl, false, pc);
+    region<48, 8, true, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, nb + lb, M[3], dma);  // PV(2), softmax(3)
+    soft_close<MASKED>(st, s, scl, false, pc, M[3], cbs);
     pp[0] = pc[0];
     pp[1] = pc[1];
-    region<56, 8, false>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, dma);  // PV(3)
+    region<56, 8, false, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, 0.f, 0u, dma);  // PV(3)
   }
 };
 
@@ -771,7 +818,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   const float scl = a.scale_log2;
   const float cb = a.log2_block / scl;  // mean-token weight log2(B) in score units
 
-  auto iter = [&](int idx, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
+  // MASKED_C: std::integral_constant<bool, ...>, the tile code path (see below)
+  auto iter = [&](auto masked_c, int idx, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     const int j2 = idx + 2 < nexact ? after_barrier(j2v) : mean_of(idx + 2);
     DmaPlan pl;
     pl.fast = false;
@@ -789,25 +838,49 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     }
     if (idx + 3 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, (idx + 3) * 4, 0, 0);
     const int mode = idx >= nexact ? 2 : (j0 == diag ? 1 : 0);
-    if (mode == 0 && wave_active) {
-      ws.tile_fast(idx == 0, Kc, Vc, off0, off1, scl, [&](int i) __attribute__((always_inline)) {
-        if (pl.fast) issue(pl, i, Kn, Vn);
-      });
-    } else {
+    auto dma = [&](int i) __attribute__((always_inline)) {
+      if (pl.fast) issue(pl, i, Kn, Vn);
+    };
+    if (!wave_active) {
       if (pl.fast) {
 #pragma unroll
         for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, Kn, Vn);
       }
-      if (wave_active) ws.tile<true>(mode, idx == 0, Kc, Vc, off0, off1, hf, scl, cb, tq, j0, diag, kept);
+    } else if constexpr (!MASKED) {
+      ws.tile_fast<false>(idx == 0, Kc, Vc, off0, off1, scl, dma, 0, tq, hf, 0.f, 0.f, 0, diag, kept);
+    } else {
+      const float lbm = mode == 2 ? a.log2_block : 0.f;
+      ws.tile_fast<true>(idx == 0, Kc, Vc, off0, off1, scl, dma, mode, tq, hf, lbm, mode == 2 ? cb : 0.f, j0, diag,
+                         kept);
     }
     j0 = j1;
     j1 = j2;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's DMA and loads for later tiles have landed
     __syncthreads();
   };
-  for (int idx = 0; idx < ntiles; idx += 2) {
-    iter(idx, K0, V0, K1, V1);
-    if (idx + 1 < ntiles) iter(idx + 1, K1, V1, K0, V0);
+  // Two loops, each with one tile code path (one instance of the tile code
+  // per loop keeps the register allocation of each loop separate): first the
+  // exact tiles off the diagonal, which CSR order puts ahead of the diagonal
+  // block, then everything else (diagonal, mean tiles, and any exact tile
+  // that would follow them) on the masked path, whose mask lets a plain
+  // exact tile through whole.
+  const std::integral_constant<bool, false> plain_c;
+  const std::integral_constant<bool, true> masked_c;
+  int idx = 0;
+  while (idx < nexact && j0 != diag) {
+    iter(plain_c, idx, K0, V0, K1, V1);
+    ++idx;
+    if (!(idx < nexact && j0 != diag)) break;
+    iter(plain_c, idx, K1, V1, K0, V0);
+    ++idx;
+  }
+  if (idx < ntiles && (idx & 1)) {
+    iter(masked_c, idx, K1, V1, K0, V0);
+    ++idx;
+  }
+  for (; idx < ntiles; idx += 2) {
+    iter(masked_c, idx, K0, V0, K1, V1);
+    if (idx + 1 < ntiles) iter(masked_c, idx + 1, K1, V1, K0, V0);
   }
 
   // ---- epilogue: O / l
