@@ -81,7 +81,7 @@ def flop_counts(w, nnz):
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("attn_bf16_d128.hip", "attn_common.h", "fp2_device.h"):
+    for f in ("attn_d128.hip", "attn_common.h", "fp2_device.h"):
         h.update(open(os.path.join(ROOT, "block_sparse_long_blocks_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

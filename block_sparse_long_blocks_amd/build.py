@@ -15,14 +15,14 @@ LIB = os.path.join(PKG, "libfp2.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["fp2_api.cpp", "fp2_validate.cpp", "block_stats.hip", "plan_mask.hip", "prefill_attn.hip",
-           "attn_bf16_d128.hip"]
+           "attn_d128.hip"]
 
 COMMON = ["-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{ROOT}/include", f"-I{CSRC}"]
 # gfx950 device code; packed-fp32 instructions are disabled on purpose.
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # The bf16 attention kernel never produces a NaN (padding is staged as zeros,
 # masks are -inf), so its max reductions need no NaN quieting.
-EXTRA = {"attn_bf16_d128.hip": ["-fno-honor-nans"]}
+EXTRA = {"attn_d128.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src, opt):

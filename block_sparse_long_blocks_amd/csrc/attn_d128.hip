@@ -59,7 +59,6 @@ constexpr int kDmaWaves = 4;
 constexpr int kDmaRows = kBlk / kDmaWaves;
 constexpr int kDmaHalves = kDmaRows / 16;
 constexpr int kDmaInstr = kDmaRows / 2;
-constexpr int kDmaSlotStep = 16 / kDmaInstr;
 
 // Position p of a V^T row holds key key_of_pos(p): within each group of 16,
 // positions 0-7 hold keys {0-3, 8-11} and positions 8-15 keys {4-7, 12-15},
@@ -73,14 +72,18 @@ __device__ __forceinline__ constexpr int key_of_pos(int p) {
 // ---------------------------------------------------------------------------
 struct PrepArgs {
   const int32_t* cu_kblocks;
+  const int32_t* cu_seqlens_q;
   const int32_t* seqlens_k;
   const int32_t* page_table;
+  const uint8_t* k_pages;
   const uint8_t* v_pages;
+  const float* v_scale;  // e4m3: [num_pages, Hkv]
   const float* kbar;
   const float* vbar;
   uint16_t* kbar16;  // bf16 [Hkv, total_kblocks, D]
   uint8_t* vt;       // V^T tiles [Hkv, total_kblocks]
   uint8_t* vbt;      // vbar^T tiles [Hkv, mt_cap]
+  uint8_t* kd;       // e4m3: K codes as bf16 rows [Hkv, total_kblocks, B, D]
   PageMap pm;
   int num_seqs, hkv, max_pages, page_size, total_kblocks, mt_cap;
 };
@@ -104,7 +107,9 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
 
 // One V^T tile per (KV block, head): thread t moves the 8 keys at positions
 // 8(t/16) .. +7 for the 8 d values of chunk t%16.  Keys past the sequence end
-// are zero.
+// are zero.  e4m3 V is dequantized (code times the page's scale, rounded to
+// bf16).
+template <bool FP8>
 __global__ __launch_bounds__(256) void vt_exact_kernel(PrepArgs a) {
   const int kb = blockIdx.x, g = blockIdx.y;
   const int s = find_seq(a.cu_kblocks, a.num_seqs, kb);
@@ -120,8 +125,16 @@ __global__ __launch_bounds__(256) void vt_exact_kernel(PrepArgs a) {
     if (pos < T) {
       int pi, slot;
       a.pm.split(pos, pi, slot);
-      v = *reinterpret_cast<const uint4*>(a.v_pages + (((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g) * kRowBytes +
-                                          dc * 16);
+      const int64_t rowi = ((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g;
+      if constexpr (FP8) {
+        const uint2 c8 = *reinterpret_cast<const uint2*>(a.v_pages + rowi * kD + dc * 8);
+        const float sc = a.v_scale[(int64_t)pt[pi] * a.hkv + g];
+        const f32x4 lo = e4m3x4_to_f32(c8.x), hi = e4m3x4_to_f32(c8.y);
+        v = make_uint4(pack_bf16x2(lo[0] * sc, lo[1] * sc), pack_bf16x2(lo[2] * sc, lo[3] * sc),
+                       pack_bf16x2(hi[0] * sc, hi[1] * sc), pack_bf16x2(hi[2] * sc, hi[3] * sc));
+      } else {
+        v = *reinterpret_cast<const uint4*>(a.v_pages + rowi * kRowBytes + dc * 16);
+      }
     }
     in[e] = v;
   }
@@ -129,6 +142,35 @@ __global__ __launch_bounds__(256) void vt_exact_kernel(PrepArgs a) {
   uint8_t* dst = a.vt + ((int64_t)g * a.total_kblocks + kb) * kTileGlobal + c * 16;
 #pragma unroll
   for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dst + (8 * dc + e) * kRowBytes) = out[e];
+}
+
+// e4m3 K codes of every block that is some query block's diagonal (the
+// blocks from the sequence's cached prefix length / B on), widened to bf16
+// rows (exact; the scale stays apart), zero past the sequence end.
+__global__ __launch_bounds__(256) void kd_kernel(PrepArgs a) {
+  const int kb = blockIdx.x, g = blockIdx.y;
+  const int s = find_seq(a.cu_kblocks, a.num_seqs, kb);
+  const int J = kb - a.cu_kblocks[s];
+  const int T = a.seqlens_k[s];
+  const int P = T - (a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s]);
+  if (J < P / kBlk) return;
+  const int32_t* pt = a.page_table + (int64_t)s * a.max_pages;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int id = t + 256 * u;
+    const int r = id >> 4, ch = id & 15;  // row, 8-wide d chunk
+    const int pos = J * kBlk + r;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (pos < T) {
+      const uint2 c8 = *reinterpret_cast<const uint2*>(
+          a.k_pages + (((int64_t)pt[J] * kBlk + r) * a.hkv + g) * kD + ch * 8);  // one page per block
+      const f32x4 lo = e4m3x4_to_f32(c8.x), hi = e4m3x4_to_f32(c8.y);
+      v = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                     pack_bf16x2(hi[2], hi[3]));
+    }
+    *reinterpret_cast<uint4*>(a.kd + (((int64_t)g * a.total_kblocks + kb) * kBlk + r) * kRowBytes + ch * 16) = v;
+  }
 }
 
 // Mean tokens: tile mt of sequence s holds mean tokens [128 mt, 128 mt + 128)
@@ -201,34 +243,6 @@ constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;
 // l and O (float32) cannot overflow
 constexpr float kPmax = 18446744073709551616.0f;  // 2^64
 
-// sched_group_barrier masks (LLVM AMDGPU IGroupLP)
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-constexpr int kSchedValu = 0x002 | 0x400;  // VALU and transcendental
-
-// Scheduling patterns for the regions of a tile: four operand reads up
-// front, then each MFMA followed by the next read (while any are left) and V
-// vector ALU instructions.  The counts must not exceed what the region holds,
-// or the compiler drops the whole pattern (vector ALU instructions beyond the
-// groups are placed freely).  Written out flat as macros: the compiler
-// honours these barriers only when they sit, loop-free, in the body that
-// holds the instructions.
-#define FP2_SG(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
-#define FP2_MDV(V) FP2_SG(kSchedMfma, 1); FP2_SG(kSchedDsRead, 1); FP2_SG(kSchedValu, (V))
-#define FP2_MV(V) FP2_SG(kSchedMfma, 1); FP2_SG(kSchedValu, (V))
-#define FP2_MD FP2_SG(kSchedMfma, 1); FP2_SG(kSchedDsRead, 1)
-// 8 MFMAs, 8 reads, no vector ALU
-#define FP2_PATTERN_8 FP2_SG(kSchedDsRead, 4); FP2_MD; FP2_MD; FP2_MD; FP2_MD; FP2_SG(kSchedMfma, 4)
-// 8 MFMAs, 8 reads, V vector ALU per MFMA
-#define FP2_PATTERN_8V(V)                                                          \
-  FP2_SG(kSchedDsRead, 4); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V);         \
-  FP2_MV(V); FP2_MV(V); FP2_MV(V); FP2_MV(V)
-// 16 MFMAs, 16 reads, V vector ALU per MFMA
-#define FP2_PATTERN_16V(V)                                                         \
-  FP2_SG(kSchedDsRead, 4); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V);         \
-  FP2_MDV(V); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V); FP2_MDV(V);          \
-  FP2_MDV(V); FP2_MDV(V); FP2_MV(V); FP2_MV(V); FP2_MV(V); FP2_MV(V)
-
 // Per-wave state and the work of one tile (32-key steps, see the header).
 //
 // Score accumulator element i of lane l (query l%32) is key
@@ -237,59 +251,12 @@ constexpr int kSchedValu = 0x002 | 0x400;  // VALU and transcendental
 // block weight B.
 struct Wave {
   static constexpr int NS = kBlk / 32;  // 32-key steps per tile
-  bf16x8 qf[kD / 16];
+  bf16x8 qf[kD / 16];  // bf16 query fragments (e4m3 inputs: the codes widened, for bf16 K tiles)
+  i32x8 qf8[kD / 64];  // e4m3 query fragments (e4m3 inputs)
   f32x16 o[kD / 32];
   float m;    // reference max (log2 units), shared by lanes l and l^32
   float nb;   // -m (0 while m = -inf): exp2(s * scale + nb) is the probability
   float l;    // this lane's half of the denominator
-
-  // S^T of step j accumulated onto c; K row 32j + l%32, chunk 2kk + l/32
-  // (all operand reads are written before the MFMAs; the region's
-  // scheduling pattern then moves them next to their MFMAs)
-  __device__ __forceinline__ f32x16 qk(const uint8_t* Kt, int off0, int off1, int j, f32x16 c) const {
-    bf16x8 kf[kD / 16];
-#pragma unroll
-    for (int kk = 0; kk < kD / 16; ++kk)
-      kf[kk] = *reinterpret_cast<const bf16x8*>(Kt + ((kk & 1) ? off1 : off0) + 8 * kGS * j + 64 * (kk >> 1));
-#pragma unroll
-    for (int kk = 0; kk < kD / 16; ++kk) c = mfma_bf16_32x32x16(kf[kk], qf[kk], c);
-    return c;
-  }
-
-  // O^T += V^T P^T over the 32 keys of step j; V^T row 32dt + l%32, chunk
-  // 4j + 2r + l/32
-  __device__ __forceinline__ void pv(const uint8_t* Vt, int off0, int off1, int j, const bf16x8 (&pf)[2]) {
-    bf16x8 vf[2][kD / 32];
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt)
-        vf[r][dt] = *reinterpret_cast<const bf16x8*>(Vt + (r ? off1 : off0) + 8 * kGS * dt + 64 * j);
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt) o[dt] = mfma_bf16_32x32x16(vf[r][dt], pf[r], o[dt]);
-  }
-
-  // Initial score accumulator of step j on diagonal and mean-token tiles
-  // (mode 1: -inf where key > query, else 0; mode 2: log2(B)/scale for a
-  // skipped block's mean token, -inf for the others).
-  __device__ __forceinline__ f32x16 mask(int mode, int j, int hf, int tq, float cb, const uint32_t* kept, int J0,
-                                         int diag) const {
-    f32x16 c;
-    if (mode == 1) {
-      int lim = tq - 32 * j - 4 * hf;  // element i is masked iff 8(i/4) + i%4 > lim
-      asm volatile("" : "+v"(lim));    // computed here, not hoisted ahead of the branch
-#pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = 8 * (i >> 2) + (i & 3) > lim ? -INFINITY : 0.f;
-    } else {
-      uint32_t w = skipped_word(kept, (J0 >> 5) + j, diag) >> (4 * hf);
-      asm volatile("" : "+v"(w));
-#pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = (w >> (8 * (i >> 2) + (i & 3))) & 1u ? cb : -INFINITY;
-    }
-    return c;
-  }
 
   __device__ __forceinline__ void rescale(float alpha) {
 #pragma unroll
@@ -320,19 +287,6 @@ struct Wave {
     return acc[0] + acc[1];
   }
 
-  // Probabilities of one step against the current reference max, their sum
-  // added to l.  The row max is not tracked on this path: the reference max
-  // is set from the first step's scores (every row sees key 0 there) and
-  // refreshed only when a step's probabilities reach kPmax, which keeps P,
-  // l and O finite and exact while O / l does not depend on the reference.
-  // Returns whether the whole wave must refresh and redo the step.
-  __device__ __forceinline__ bool softmax(const f32x16& s, float scl, bf16x8 (&pf)[2]) {
-    float step = probs(s, scl, pf);
-    asm volatile("" : "+v"(step));
-    l += step;
-    return __any(!(step < kPmax));  // also catches inf
-  }
-
   // Sets the reference max to cover this step's scores, rescales O (which
   // holds every step before this one) and l_prev (l before this step), and
   // redoes the step's probabilities.
@@ -349,77 +303,82 @@ struct Wave {
     l = l_prev * alpha + probs(s, scl, pf);
   }
 
-  // mode 0 exact block, 1 diagonal block, 2 mean-token tile starting at
-  // mean token J0 (wave-uniform).  MASKED (modes 1, 2) sets up each step's
-  // masks in a small block between the scheduling regions and starts the
-  // score accumulators from them; exact blocks start from zero.
-  template <bool MASKED>
-  __device__ __forceinline__ void tile(int mode, bool first, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1,
-                                       int hf, float scl, float cb, int tq, int J0, int diag, const uint32_t* kept) {
-    f32x16 cz = f32x16{};
-    if constexpr (MASKED) cz = mask(mode, 0, hf, tq, cb, kept, J0, diag);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 s = qk(Kt, off0, off1, 0, cz);
-    FP2_PATTERN_8;
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 pp[2];  // probabilities of the previous step
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      if constexpr (MASKED) {
-        if (j + 1 < NS) cz = mask(mode, j + 1, hf, tq, cb, kept, J0, diag);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 sn = f32x16{};
-      if (j + 1 < NS) sn = qk(Kt, off0, off1, j + 1, cz);
-      if (j > 0) pv(Vt, off0, off1, j - 1, pp);
-      bf16x8 pc[2];
-      const float l_prev = l;
-      const bool up = softmax(s, scl, pc) || (first && j == 0);
-      // the softmax has about 36 vector ALU instructions
-      if (j == 0 || j + 1 == NS) {
-        FP2_PATTERN_8V(4);
-      } else {
-        FP2_PATTERN_16V(2);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (up) refresh(s, scl, l_prev, pc);  // after PV(j-1), before PV(j)
-      pp[0] = pc[0];
-      pp[1] = pc[1];
-      s = sn;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    pv(Vt, off0, off1, NS - 1, pp);
-    FP2_PATTERN_8;
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // ---- exact tiles on a fixed instruction schedule ----
+  // ---- tiles on a fixed instruction schedule ----
   //
-  // The 64 MFMAs of a tile run in the order QK(0) | QK(1) | QK(2),PV(0)
-  // alternating | QK(3),PV(1) alternating | PV(2) | PV(3) (op n = 0..63, six
-  // regions of 8, 8, 16, 16, 8, 8).  Each op is one slot closed by a
-  // scheduling barrier, so the order below is the issue order: op n's LDS
-  // operand is read kLA slots ahead (across regions), and the softmax of
-  // step j runs in region j+1 as a stream of groups spread over the slots,
-  // each value produced a group or more before it is consumed, so that no
-  // vector instruction waits on the one just before it and the matrix core
-  // keeps getting work.  The refresh test of step j closes region j+1,
-  // before PV(j) reads P(j).
+  // A tile's MFMAs run in a fixed order of ops n: QK(0) | QK(1) | QK(2) with
+  // PV(0) | QK(3) with PV(1) | PV(2) | PV(3), six regions.  bf16 QK (QK8
+  // false): 8 MFMAs 32x32x16 per step, 64 ops, regions of 8, 8, 16, 16, 8, 8
+  // with QK and PV alternating.  e4m3 QK (QK8 true): 2 MFMAs 32x32x64 per
+  // step, 40 ops, regions of 2, 2, 10, 10, 8, 8 with the two QK ops at the
+  // head and the middle of regions 2 and 3.  Each op is one slot closed by a
+  // scheduling barrier, so this is the issue order: an op's LDS operand (16
+  // bytes, 32 for an e4m3 QK op) is read kLA slots ahead (across regions),
+  // and the softmax of step j runs in region j+1 as a stream of groups
+  // spread over the slots, each value produced a group or more before it is
+  // consumed, so that no vector instruction waits on the one just before it
+  // and the matrix core keeps getting work.  The refresh test of step j
+  // closes region j+1, before PV(j) reads P(j).
   static constexpr int kLA = 4;
   static constexpr int kGroups = 20;
-  static constexpr int kDma0 = 8;  // the next tile's DMA instructions go out from op 8 on, kDmaSlotStep apart
+  static constexpr int kRing = 16;  // operand reads in flight (16-byte registers quads)
 
-  __device__ static constexpr bool op_qk(int n) { return n < 16 || (n < 48 && (n & 1) == 0); }
-  __device__ static constexpr int op_step(int n) {
-    return op_qk(n) ? (n < 8 ? 0 : n < 16 ? 1 : n < 32 ? 2 : 3) : (n < 32 ? 0 : n < 48 ? 1 : n < 56 ? 2 : 3);
+  template <bool QK8>
+  static constexpr int n_ops() { return QK8 ? 40 : 64; }
+  // first op of region r (r = 0..6)
+  template <bool QK8>
+  static constexpr int region_start(int r) {
+    constexpr int b16[7] = {0, 8, 16, 32, 48, 56, 64};
+    constexpr int b8[7] = {0, 2, 4, 14, 24, 32, 40};
+    return QK8 ? b8[r] : b16[r];
   }
-  // QK: d-slice kk; PV: 4 r + dt
-  __device__ static constexpr int op_idx(int n) { return n < 16 ? (n & 7) : n < 48 ? ((n & 15) >> 1) : (n & 7); }
+  template <bool QK8>
+  static constexpr bool op_qk(int n) {
+    if (QK8) return n < 4 || ((n >= 4 && n < 24) && ((n - 4) % 10 == 0 || (n - 4) % 10 == 5));
+    return n < 16 || (n < 48 && (n & 1) == 0);
+  }
+  template <bool QK8>
+  static constexpr int op_step(int n) {
+    if (QK8) {
+      if (op_qk<QK8>(n)) return n < 2 ? 0 : n < 4 ? 1 : n < 14 ? 2 : 3;
+      return n < 14 ? 0 : n < 24 ? 1 : n < 32 ? 2 : 3;
+    }
+    return op_qk<QK8>(n) ? (n < 8 ? 0 : n < 16 ? 1 : n < 32 ? 2 : 3) : (n < 32 ? 0 : n < 48 ? 1 : n < 56 ? 2 : 3);
+  }
+  // QK: d-slice kk (16 wide, or 64 wide for e4m3); PV: 4 r + dt
+  template <bool QK8>
+  static constexpr int op_idx(int n) {
+    if (QK8) {
+      if (n < 4) return n & 1;
+      if (n < 24) {
+        const int t = (n - 4) % 10;
+        return t == 0 ? 0 : t == 5 ? 1 : t - 1 - (t > 5 ? 1 : 0);
+      }
+      return n & 7;
+    }
+    return n < 16 ? (n & 7) : n < 48 ? ((n & 15) >> 1) : (n & 7);
+  }
+  template <bool QK8>
+  static constexpr int op_reads(int n) { return QK8 && op_qk<QK8>(n) ? 2 : 1; }
+  // index of op n's first operand read
+  template <bool QK8>
+  static constexpr int read0(int n) {
+    int r = 0;
+    for (int k = 0; k < n; ++k) r += op_reads<QK8>(k);
+    return r;
+  }
 
-  __device__ __forceinline__ const uint8_t* op_addr(int n, const uint8_t* Kt, const uint8_t* Vt, int off0,
-                                                    int off1) const {
-    const int j = op_step(n), i = op_idx(n);
-    if (op_qk(n)) return Kt + ((i & 1) ? off1 : off0) + 8 * kGS * j + 64 * (i >> 1);
+  // LDS address of read e of op n.  bf16 K / V^T: the swizzled 256-byte-row
+  // layout at the two per-lane bases off0 / off1.  e4m3 K: 128-byte rows,
+  // 1 KB per 8 rows, 16-byte chunk c of row r in slot c ^ (r % 8); off8[2 kk
+  // + e] is lane l's slot of chunk 4 kk + 2 (l/32) + e in row l%32.
+  template <bool QK8>
+  __device__ __forceinline__ const uint8_t* op_addr(int n, int e, const uint8_t* Kt, const uint8_t* Vt, int off0,
+                                                    int off1, const int (&off8)[4]) const {
+    const int j = op_step<QK8>(n), i = op_idx<QK8>(n);
+    if (op_qk<QK8>(n)) {
+      if constexpr (QK8) return Kt + off8[2 * i + e] + 4096 * j;
+      return Kt + ((i & 1) ? off1 : off0) + 8 * kGS * j + 64 * (i >> 1);
+    }
     return Vt + ((i >> 2) ? off1 : off0) + 8 * kGS * (i & 3) + 64 * j;
   }
 
@@ -461,23 +420,39 @@ struct Wave {
     }
   }
 
-  // one region: ops [n0, n0 + S), with the softmax stream of s when SOFT
-  template <int N0, int S, bool SOFT, bool MASKED, class Dma>
-  __device__ __forceinline__ void region(bf16x8 (&fr)[8], f32x16& sn, const bf16x8 (&pp)[2], Soft& st,
+  // one region: ops [region_start(R), region_start(R + 1)), with the softmax
+  // stream of s when SOFT; the next tile's DMA instructions go out one per
+  // slot in slots kDma0 .. kDma0 + 15
+  template <int R, bool SOFT, bool MASKED, bool QK8, class Dma>
+  __device__ __forceinline__ void region(bf16x8 (&fr)[kRing], f32x16& sn, const bf16x8 (&pp)[2], Soft& st,
                                          const f32x16& s, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1,
-                                         float scl, float nbm, uint32_t M, Dma& dma) {
+                                         const int (&off8)[4], float scl, float nbm, uint32_t M, Dma& dma) {
+    constexpr int N0 = region_start<QK8>(R), S = region_start<QK8>(R + 1) - N0;
+    constexpr int kDma0 = QK8 ? 4 : 8;
 #pragma unroll
     for (int t = 0; t < S; ++t) {
       const int n = N0 + t;
-      if (op_qk(n)) {
-        sn = mfma_bf16_32x32x16(fr[n & 7], qf[op_idx(n)], sn);
+      const int r0 = read0<QK8>(n) % kRing;
+      if (op_qk<QK8>(n)) {
+        if constexpr (QK8) {
+          const uint4 lo = __builtin_bit_cast(uint4, fr[r0]), hi = __builtin_bit_cast(uint4, fr[(r0 + 1) % kRing]);
+          const i32x8 ka = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          sn = mfma_fp8_32x32x64(ka, qf8[op_idx<QK8>(n)], sn);
+        } else {
+          sn = mfma_bf16_32x32x16(fr[r0], qf[op_idx<QK8>(n)], sn);
+        }
       } else {
-        const int i = op_idx(n);
-        o[i & 3] = mfma_bf16_32x32x16(fr[n & 7], pp[i >> 2], o[i & 3]);
+        const int i = op_idx<QK8>(n);
+        o[i & 3] = mfma_bf16_32x32x16(fr[r0], pp[i >> 2], o[i & 3]);
       }
-      if (n + kLA < 64) fr[(n + kLA) & 7] = *reinterpret_cast<const bf16x8*>(op_addr(n + kLA, Kt, Vt, off0, off1));
-      if (n >= kDma0 && n < kDma0 + kDmaInstr * kDmaSlotStep && (n - kDma0) % kDmaSlotStep == kDmaSlotStep - 1)
-        dma((n - kDma0) / kDmaSlotStep);
+      if (n + kLA < n_ops<QK8>()) {
+        const int nr = n + kLA;
+#pragma unroll
+        for (int e = 0; e < op_reads<QK8>(nr); ++e)
+          fr[(read0<QK8>(nr) + e) % kRing] =
+              *reinterpret_cast<const bf16x8*>(op_addr<QK8>(nr, e, Kt, Vt, off0, off1, off8));
+      }
+      if (n >= kDma0 && n < kDma0 + 16) dma(n - kDma0);
       if constexpr (SOFT) {
 #pragma unroll
         for (int g = t * kGroups / S; g < (t + 1) * kGroups / S; ++g) soft_group<MASKED>(g, st, s, scl, nbm, M);
@@ -509,15 +484,17 @@ struct Wave {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // One tile.  MASKED: mode 1 diagonal block (key > query masked), mode 2
-  // mean-token tile starting at mean token J0 (only skipped blocks' tokens
-  // count, each with weight B: lb = log2 B added to the exponent, cbs = lb /
-  // scl in score units).
-  template <bool MASKED, class Dma>
-  __device__ __forceinline__ void tile_fast(bool first, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1,
-                                            float scl, Dma&& dma, int mode, int tq, int hf, float lb, float cbs,
-                                            int J0, int diag, const uint32_t* kept) {
-    bf16x8 fr[8];
+  // One tile; scl is its logit scale (log2 units, input scales folded in).
+  // MASKED: mode 1 diagonal block (key > query masked), mode 2 mean-token
+  // tile starting at mean token J0 (only skipped blocks' tokens count, each
+  // with weight B: lb = log2 B added to the exponent, cbs = lb / scl in
+  // score units); mode 0 passes whole.  QK8: e4m3 K tile and QK on the
+  // 32x32x64 e4m3 MFMA.
+  template <bool MASKED, bool QK8, class Dma>
+  __device__ __forceinline__ void tile(bool first, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1,
+                                       const int (&off8)[4], float scl, Dma&& dma, int mode, int tq, int hf, float lb,
+                                       float cbs, int J0, int diag, const uint32_t* kept) {
+    bf16x8 fr[kRing];
     bf16x8 pp[2] = {qf[0], qf[0]}, pc[2];
     f32x16 s = f32x16{}, sn = f32x16{};
     Soft st;
@@ -540,41 +517,39 @@ struct Wave {
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int n = 0; n < kLA; ++n) fr[n] = *reinterpret_cast<const bf16x8*>(op_addr(n, Kt, Vt, off0, off1));
+    for (int n = 0; n < kLA; ++n)
+#pragma unroll
+      for (int e = 0; e < op_reads<QK8>(n); ++e)
+        fr[read0<QK8>(n) + e] = *reinterpret_cast<const bf16x8*>(op_addr<QK8>(n, e, Kt, Vt, off0, off1, off8));
     __builtin_amdgcn_sched_barrier(0);
-    region<0, 8, false, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, 0.f, 0u, dma);  // QK(0)
-    s = sn;
-    sn = f32x16{};
-    st.acc[0] = st.acc[1] = 0.f;
-    region<8, 8, true, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, nb + lb, M[0], dma);  // QK(1), softmax(0)
-    soft_close<MASKED>(st, s, scl, first, pc, M[0], cbs);
-    pp[0] = pc[0];
-    pp[1] = pc[1];
-    s = sn;
-    sn = f32x16{};
-    st.acc[0] = st.acc[1] = 0.f;
-    region<16, 16, true, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, nb + lb, M[1], dma);  // QK(2), PV(0), softmax(1)
-    soft_close<MASKED>(st, s, scl, false, pc, M[1], cbs);
-    pp[0] = pc[0];
-    pp[1] = pc[1];
-    s = sn;
-    sn = f32x16{};
-    st.acc[0] = st.acc[1] = 0.f;
-    region<32, 16, true, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, nb + lb, M[2], dma);  // QK(3), PV(1), softmax(2)
-    soft_close<MASKED>(st, s, scl, false, pc, M[2], cbs);
-    pp[0] = pc[0];
-    pp[1] = pc[1];
-    s = sn;
-    st.acc[0] = st.acc[1] = 0.f;
-    region<48, 8, true, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, nb + lb, M[3], dma);  // PV(2), softmax(3)
-    soft_close<MASKED>(st, s, scl, false, pc, M[3], cbs);
-    pp[0] = pc[0];
-    pp[1] = pc[1];
-    region<56, 8, false, MASKED>(fr, sn, pp, st, s, Kt, Vt, off0, off1, scl, 0.f, 0u, dma);  // PV(3)
+    region<0, false, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, 0.f, 0u, dma);  // QK(0)
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      s = sn;
+      sn = f32x16{};
+      st.acc[0] = st.acc[1] = 0.f;
+      // region j+1: QK(j+1) (j < 3), PV(j-1) (j > 0), softmax(j)
+      if (j == 0) region<1, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[0], dma);
+      if (j == 1) region<2, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[1], dma);
+      if (j == 2) region<3, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[2], dma);
+      if (j == 3) region<4, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[3], dma);
+      soft_close<MASKED>(st, s, scl, first && j == 0, pc, M[j], cbs);
+      pp[0] = pc[0];
+      pp[1] = pc[1];
+    }
+    region<5, false, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, 0.f, 0u, dma);  // PV(3)
   }
 };
 
-__global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a) {
+// One 1 KB LDS DMA instruction: lane i's 16 bytes at src land at dst + 16 i
+// (dst wave-uniform).  A plain function: the builtin written straight in
+// the kernel template keeps the host pass from emitting the launch stub.
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   // two K and two V^T buffers, as separate objects so that the compiler can
   // tell the DMA target from the buffers being read
   __shared__ __attribute__((aligned(1024))) uint8_t K0[kTileLds];
@@ -663,7 +638,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   ws.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt) ws.o[dt] = f32x16{};
-  {
+  float qs = 1.f;  // e4m3: the query block's scale
+  if constexpr (!FP8) {
     const uint8_t* qrow = a.q + ((int64_t)(q0 + I * kBlk + tq) * a.hq + h) * kRowBytes;
 #pragma unroll
     for (int kk = 0; kk < kD / 16; ++kk) {
@@ -671,6 +647,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
       if (q_valid) v = *reinterpret_cast<const uint4*>(qrow + (16 * kk + 8 * hf) * 2);
       ws.qf[kk] = __builtin_bit_cast(bf16x8, v);
     }
+  } else {
+    // e4m3 codes: 32 bytes at d = 64 kk + 32 (l/32) for the 32x32x64 MFMA, and
+    // the 8 at d = 16 kk + 8 (l/32) widened to bf16 (exactly) for bf16 K tiles
+    const uint8_t* qrow = a.q + ((int64_t)(q0 + I * kBlk + tq) * a.hq + h) * kD;
+#pragma unroll
+    for (int kk = 0; kk < kD / 64; ++kk) {
+      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+      if (q_valid) {
+        v0 = *reinterpret_cast<const uint4*>(qrow + 64 * kk + 32 * hf);
+        v1 = *reinterpret_cast<const uint4*>(qrow + 64 * kk + 32 * hf + 16);
+      }
+      ws.qf8[kk] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+    }
+#pragma unroll
+    for (int kk = 0; kk < kD / 16; ++kk) {
+      uint2 v = make_uint2(0, 0);
+      if (q_valid) v = *reinterpret_cast<const uint2*>(qrow + 16 * kk + 8 * hf);
+      const f32x4 lo = e4m3x4_to_f32(v.x), hi = e4m3x4_to_f32(v.y);
+      ws.qf[kk] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                                                        pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])));
+    }
+    if (wave_active) qs = a.q_scale[(int64_t)qb * a.hq + h];
   }
 
   // ---- DMA of one tile: wave w < kDmaWaves moves rows R w .. R w + R-1
@@ -687,6 +685,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   const uint32_t voff = (uint32_t)((lane >> 4) * kRowBytes + uoff);  // + 1024 p: rows of 256 bytes
   const uint32_t tok = (uint32_t)a.hkv * kRowBytes;                  // K row stride in the cache
   const uint32_t koff = (uint32_t)(lane >> 4) * tok + uoff;          // + 4 p tok
+  // e4m3 K: 128-byte rows, 8 per instruction; lane i moves row 8p + i/8,
+  // chunk (i%8) ^ (i/8)
+  const uint32_t tok8 = (uint32_t)a.hkv * kD;
+  const uint32_t koff8 = (uint32_t)(lane >> 3) * tok8 + 16 * ((lane & 7) ^ (lane >> 3));  // + 8 p tok8
   const bool pages16 = a.page_size % 16 == 0;
   // Uniform values for later tiles (block indices, page entries) come through
   // vector buffer loads: they share the vector-memory counter with the DMA,
@@ -708,12 +710,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     asm volatile("" : "+v"(v));
     return __builtin_amdgcn_readfirstlane(v);
   };
-  auto lds = [](uint8_t* p) { return (__attribute__((address_space(3))) void*)p; };
-  // the fast-path sources of one tile (instruction p: kb + p * kstep + kvo, vb + 1024 p + voff)
+  // the fast-path sources of one tile: K instruction p < nk reads kb[p/4] +
+  // (p%4) kstep + kvo into kd + p kds, V^T instruction p reads vb + 1024 p +
+  // voff
   struct DmaPlan {
     const uint8_t* kb[kDmaHalves];
     const uint8_t* vb;
+    uint8_t* kd;
     uint32_t kstep, kvo;
+    int kds, nk;
     bool fast;
   };
   // Plans the DMA of tile idx (block or mean token j, page entry pg of this
@@ -724,11 +729,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     if (!dma_wave) return pl;
     uint8_t* kd = Kd + (kDmaRows / 4) * wave * kGS;
     uint8_t* vd = Vd + (kDmaRows / 4) * wave * kGS;
+    pl.kd = kd;
+    pl.kds = kGS;
+    pl.nk = kDmaRows / 4;
     if (idx < nexact) {
       pl.vb = a.vt + (((int64_t)g * a.total_kblocks + kb0 + j) * kBlk + kDmaRows * wave) * kRowBytes;
       const int r0 = j * kBlk + kDmaRows * wave;
       pl.fast = pages16 && r0 + kDmaRows - 1 < T;
-      if (pl.fast) {
+      if (FP8 && j == diag) {
+        // the diagonal block's K codes widened to bf16 rows (zero past the end)
+        pl.fast = true;
+#pragma unroll
+        for (int hh = 0; hh < kDmaHalves; ++hh)
+          pl.kb[hh] = a.kd + ((mrow0 + j) * kBlk + kDmaRows * wave + 16 * hh) * kRowBytes;
+        pl.kstep = 1024;
+        pl.kvo = voff;
+      } else if (FP8) {
+        // e4m3 K rows (one page per block): kDmaRows/8 instructions of 8 rows
+        pl.kd = Kd + kDmaRows * wave * kD;
+        pl.kds = 1024;
+        pl.nk = kDmaRows / 8;
+        pl.fast = r0 + kDmaRows - 1 < T;
+        if (pl.fast) {
+#pragma unroll
+          for (int hh = 0; hh < kDmaHalves; ++hh)
+            pl.kb[hh] = a.k_pages + (((int64_t)pg[0] * kBlk + kDmaRows * wave) * a.hkv + g) * kD;
+          pl.kstep = 8 * tok8;
+          pl.kvo = koff8;
+        } else {
+#pragma unroll
+          for (int p = 0; p < kDmaRows / 8; ++p) {
+            const int r = min(r0 + 8 * p + (lane >> 3), T - 1);  // rows past the end repeat the last key
+            const uint8_t* ksrc = a.k_pages + (((int64_t)pt[r / kBlk] * kBlk + r % kBlk) * a.hkv + g) * kD +
+                                  16 * ((lane & 7) ^ (lane >> 3));
+            dma16(ksrc, pl.kd + p * 1024);
+          }
+#pragma unroll
+          for (int p = 0; p < kDmaRows / 4; ++p)
+            dma16(pl.vb + voff + 1024 * p, vd + p * kGS);
+        }
+      } else if (pl.fast) {
 #pragma unroll
         for (int hh = 0; hh < kDmaHalves; ++hh) {
           int pi, slot;
@@ -743,8 +783,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
           int pi, slot;
           a.pm.split(min(r0 + 4 * p + (lane >> 4), T - 1), pi, slot);  // rows past the end repeat the last key
           const uint8_t* ksrc = a.k_pages + (((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g) * kRowBytes + uoff;
-          __builtin_amdgcn_global_load_lds(ksrc, lds(kd + p * kGS), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(pl.vb + voff + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
+          dma16(ksrc, kd + p * kGS);
+          dma16(pl.vb + voff + 1024 * p, vd + p * kGS);
         }
       }
     } else {
@@ -761,21 +801,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
 #pragma unroll
         for (int p = 0; p < kDmaRows / 4; ++p) {
           const int jm = min(r0 + 4 * p + (lane >> 4), diag - 1);  // tokens past diag repeat a real one (masked)
-          __builtin_amdgcn_global_load_lds(k16 + (mrow0 + jm) * kRowBytes + uoff, lds(kd + p * kGS), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(pl.vb + voff + 1024 * p, lds(vd + p * kGS), 16, 0, 0);
+          dma16(k16 + (mrow0 + jm) * kRowBytes + uoff, kd + p * kGS);
+          dma16(pl.vb + voff + 1024 * p, vd + p * kGS);
         }
       }
     }
     return pl;
   };
   // instruction i of a fast plan: K row group i/2 (even i) or V^T row group i/2 (odd i)
-  auto issue = [&](const DmaPlan& pl, int i, uint8_t* Kd, uint8_t* Vd) __attribute__((always_inline)) {
+  auto issue = [&](const DmaPlan& pl, int i, uint8_t* Vd) __attribute__((always_inline)) {
     const int p = i >> 1;
-    const int grp = (kDmaRows / 4) * wave + p;
-    if ((i & 1) == 0)
-      __builtin_amdgcn_global_load_lds(pl.kb[p >> 2] + (p & 3) * pl.kstep + pl.kvo, lds(Kd + grp * kGS), 16, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds(pl.vb + 1024 * p + voff, lds(Vd + grp * kGS), 16, 0, 0);
+    if ((i & 1) == 0) {
+      if (p < pl.nk)
+        dma16(pl.kb[p >> 2] + (p & 3) * pl.kstep + pl.kvo, pl.kd + p * pl.kds);
+    } else {
+      dma16(pl.vb + 1024 * p + voff, Vd + ((kDmaRows / 4) * wave + p) * kGS);
+    }
   };
 
   // per-lane operand offsets (see Wave::qk / Wave::pv): row l%32 of a 32-row
@@ -784,6 +825,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   const int rbase = (c >> 2) * kGS + x * kRowBytes;
   const int off0 = rbase + 16 * (hf ^ x);
   const int off1 = rbase + 16 * ((2 + hf) ^ x);
+  // e4m3 K operand: row c, chunks 4 kk + 2 hf + e, slot = chunk ^ (c % 8)
+  int off8[4];
+#pragma unroll
+  for (int ke = 0; ke < 4; ++ke) off8[ke] = (c >> 3) * 1024 + (c & 7) * 128 + 16 * ((4 * (ke >> 1) + 2 * hf + (ke & 1)) ^ (c & 7));
 
   // Tile pipeline: at iteration i the LDS buffers i%2 hold tile i and the
   // DMA of tile i+1 into the other buffers is in flight; the block index of
@@ -797,6 +842,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   if (1 < nexact) j1 = ld_uniform(a.col_idx, kbeg + 1);
   else if (1 < ntiles) j1 = mean_of(1);
   if (2 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 2 * 4, 0, 0);
+  // e4m3: the K scale of exact tile i (one page per block) arrives with the
+  // barrier before tile i (ksv); the page entry of tile i+1 one tile earlier
+  // (pgbv)
+  const __amdgpu_buffer_rsrc_t rks =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.k_scale, (short)0, 0x7fffffff, kBufferFlags);
+  int ksv = 0, pgbv = 0;
+  if constexpr (FP8) {
+    if (0 < nexact) ksv = __builtin_amdgcn_raw_buffer_load_b32(rks, (ld_uniform(pt, j0) * a.hkv + g) * 4, 0, 0);
+    if (1 < nexact) pgbv = __builtin_amdgcn_raw_buffer_load_b32(rpt, j1 * 4, 0, 0);
+  }
   if (ntiles > 0) {
     int pg0[kDmaHalves] = {};
     if (0 < nexact && dma_wave) {
@@ -806,7 +861,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     const DmaPlan pl = plan(0, j0, pg0, K0, V0);
     if (pl.fast) {
 #pragma unroll
-      for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, K0, V0);
+      for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, V0);
     }
   }
   if (1 < nexact && dma_wave) {
@@ -815,13 +870,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  const float scl = a.scale_log2;
-  const float cb = a.log2_block / scl;  // mean-token weight log2(B) in score units
+  const float scl = a.scale_log2 * qs;  // logit scale of mean tiles (and of every bf16 tile)
 
   // MASKED_C: std::integral_constant<bool, ...>, the tile code path (see below)
   auto iter = [&](auto masked_c, int idx, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
     constexpr bool MASKED = decltype(masked_c)::value;
     const int j2 = idx + 2 < nexact ? after_barrier(j2v) : mean_of(idx + 2);
+    float sclt = scl;
+    if constexpr (FP8) {
+      if (idx < nexact) sclt = scl * __uint_as_float((uint32_t)after_barrier(ksv));
+      if (idx + 1 < nexact) ksv = __builtin_amdgcn_raw_buffer_load_b32(rks, (after_barrier(pgbv) * a.hkv + g) * 4, 0, 0);
+      if (idx + 2 < nexact) pgbv = __builtin_amdgcn_raw_buffer_load_b32(rpt, j2 * 4, 0, 0);
+    }
     DmaPlan pl;
     pl.fast = false;
     if (idx + 1 < ntiles) {
@@ -839,19 +899,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
     if (idx + 3 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, (idx + 3) * 4, 0, 0);
     const int mode = idx >= nexact ? 2 : (j0 == diag ? 1 : 0);
     auto dma = [&](int i) __attribute__((always_inline)) {
-      if (pl.fast) issue(pl, i, Kn, Vn);
+      if (pl.fast) issue(pl, i, Vn);
     };
     if (!wave_active) {
       if (pl.fast) {
 #pragma unroll
-        for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, Kn, Vn);
+        for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, Vn);
       }
     } else if constexpr (!MASKED) {
-      ws.tile_fast<false>(idx == 0, Kc, Vc, off0, off1, scl, dma, 0, tq, hf, 0.f, 0.f, 0, diag, kept);
+      ws.tile<false, FP8>(idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, 0, tq, hf, 0.f, 0.f, 0, diag, kept);
     } else {
+      // mean tiles: weight B, log2 B in the exponent (cbs in score units)
       const float lbm = mode == 2 ? a.log2_block : 0.f;
-      ws.tile_fast<true>(idx == 0, Kc, Vc, off0, off1, scl, dma, mode, tq, hf, lbm, mode == 2 ? cb : 0.f, j0, diag,
-                         kept);
+      ws.tile<true, false>(idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, mode, tq, hf, lbm, lbm / sclt, j0, diag,
+                           kept);
     }
     j0 = j1;
     j1 = j2;
@@ -860,10 +921,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   };
   // Two loops, each with one tile code path (one instance of the tile code
   // per loop keeps the register allocation of each loop separate): first the
-  // exact tiles off the diagonal, which CSR order puts ahead of the diagonal
-  // block, then everything else (diagonal, mean tiles, and any exact tile
-  // that would follow them) on the masked path, whose mask lets a plain
-  // exact tile through whole.
+  // exact tiles off the diagonal, which the ascending CSR puts ahead of the
+  // diagonal block (e4m3: on the e4m3 MFMA), then the diagonal and the mean
+  // tiles on the masked bf16 path (e4m3: the diagonal block's codes widened
+  // to bf16).
   const std::integral_constant<bool, false> plain_c;
   const std::integral_constant<bool, true> masked_c;
   int idx = 0;
@@ -911,32 +972,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_d128_kernel(AttnArgs a)
   }
 }
 
-#undef FP2_PATTERN_16V
-#undef FP2_PATTERN_8V
-#undef FP2_PATTERN_8
-#undef FP2_MD
-#undef FP2_MV
-#undef FP2_MDV
-#undef FP2_SG
-
-}  // namespace
-
-hipError_t launch_attn_bf16_d128(const AttnArgs& a_in, const float* kbar, const float* vbar, int max_kblocks,
-                                 hipStream_t stream) {
+hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const float* vbar, int max_kblocks,
+                       hipStream_t stream) {
   AttnArgs a = a_in;
-  uint16_t* kbar16 = const_cast<uint16_t*>(a.kbar16);
-  uint8_t* vbt = const_cast<uint8_t*>(a.vbt);
-  uint8_t* vt = const_cast<uint8_t*>(a.vt);
   PrepArgs p;
   p.cu_kblocks = a.cu_kblocks;
+  p.cu_seqlens_q = a.cu_seqlens_q;
   p.seqlens_k = a.seqlens_k;
   p.page_table = a.page_table;
+  p.k_pages = a.k_pages;
   p.v_pages = a.v_pages;
+  p.v_scale = a.v_scale;
   p.kbar = kbar;
   p.vbar = vbar;
-  p.kbar16 = kbar16;
-  p.vt = vt;
-  p.vbt = vbt;
+  p.kbar16 = const_cast<uint16_t*>(a.kbar16);
+  p.vt = const_cast<uint8_t*>(a.vt);
+  p.vbt = const_cast<uint8_t*>(a.vbt);
+  p.kd = const_cast<uint8_t*>(a.kd);
   p.pm = a.pm;
   p.num_seqs = a.num_seqs;
   p.hkv = a.hkv;
@@ -945,7 +997,15 @@ hipError_t launch_attn_bf16_d128(const AttnArgs& a_in, const float* kbar, const 
   p.total_kblocks = a.total_kblocks;
   p.mt_cap = a.mt_cap;
   if (a.total_kblocks > 0) {
-    hipLaunchKernelGGL(vt_exact_kernel, dim3((unsigned)a.total_kblocks, (unsigned)a.hkv), dim3(256), 0, stream, p);
+    const dim3 per_block((unsigned)a.total_kblocks, (unsigned)a.hkv);
+    if (fp8) {
+      hipLaunchKernelGGL(vt_exact_kernel<true>, per_block, dim3(256), 0, stream, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kd_kernel, per_block, dim3(256), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL(vt_exact_kernel<false>, per_block, dim3(256), 0, stream, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.correction) {
@@ -959,8 +1019,18 @@ hipError_t launch_attn_bf16_d128(const AttnArgs& a_in, const float* kbar, const 
   const int G = a.hq / a.hkv;
   a.slices = (G * kBlk + kWGRows - 1) / kWGRows;
   const unsigned grid = (unsigned)(((a.rows + 7) / 8) * 8 * a.slices);
-  hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  if (fp8)
+    hipLaunchKernelGGL(attn_d128_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_d128_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_d128(const AttnArgs& a, bool fp8, const float* kbar, const float* vbar, int max_kblocks,
+                            hipStream_t stream) {
+  return launch_impl(a, fp8, kbar, vbar, max_kblocks, stream);
 }
 
 }  // namespace fp2

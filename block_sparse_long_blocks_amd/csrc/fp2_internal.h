@@ -35,10 +35,10 @@ fp2_status check_q(const fp2_q* q, int num_kv_heads, const BatchInfo& info, int 
 fp2_status check_kv(const fp2_kv* kv, const fp2_batch* b, const BatchInfo& info);
 
 size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads);
-// fp2_prefill_run runs the DMA kernel on V^T tiles for bf16, d = 128,
-// B = 128, and the register-staged kernel otherwise.
+// fp2_prefill_run runs the DMA kernel on V^T tiles for d = 128, B = 128
+// (bf16 or e4m3), and the register-staged kernel otherwise.
 inline bool vt_path(int dtype, int head_dim, int block) {
-  return dtype == FP2_BF16 && head_dim == 128 && block == 128;
+  return (dtype == FP2_BF16 || dtype == FP2_FP8_E4M3) && head_dim == 128 && block == 128;
 }
 
 // Byte offsets of the parts of the fp2_prefill_run workspace.
@@ -46,6 +46,7 @@ struct RunLayout {
   size_t k16 = 0;      // bf16 kbar rows [Hkv, total_kblocks, d]
   size_t v16 = 0;      // fp16 vbar rows (register-staged path) or vbar^T tiles (V^T path)
   size_t vt = 0;       // V^T tiles of every KV block (V^T path)
+  size_t kd = 0;       // e4m3 V^T path: K codes as bf16 rows, [Hkv, total_kblocks, B, d]
   size_t total = 0;
   int64_t mt_cap = 0;  // vbar^T tiles per KV head (V^T path)
 };

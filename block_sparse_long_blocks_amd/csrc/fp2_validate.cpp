@@ -148,6 +148,10 @@ RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_kv_heads, int 
     L.mt_cap = (int64_t)(tkb / (size_t)block + (size_t)num_seqs + 1);
     L.vt = L.v16 + hkv * (size_t)L.mt_cap * tile;
     L.total = L.vt + hkv * tkb * tile;
+    if (dtype == FP2_FP8_E4M3) {
+      L.kd = L.total;
+      L.total = L.kd + hkv * tkb * tile;
+    }
   } else {
     L.total = L.v16 + rows;
   }

@@ -593,6 +593,7 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.vbar16 = v16;
   a.vt = wsb + L.vt;
   a.vbt = wsb + L.v16;
+  a.kd = wsb + L.kd;
   a.mt_cap = (int)L.mt_cap;
   a.out = out;
   a.out_f32 = out_f32;
@@ -611,7 +612,7 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.slices = (G * BLK + kRowsPerWG - 1) / kRowsPerWG;
   a.rows = (int)(info.total_qblocks * hkv);
   const unsigned grid = (unsigned)(((a.rows + 7) / 8) * 8 * a.slices);
-  if (vt) return launch_attn_bf16_d128(a, kbar, vbar, (int)info.max_kblocks, stream);
+  if (vt) return launch_attn_d128(a, q->dtype == FP2_FP8_E4M3, kbar, vbar, (int)info.max_kblocks, stream);
   if (q->dtype == FP2_FP8_E4M3) return launch_attn_dt<true>(D, BLK, a, grid, stream);
   return launch_attn_dt<false>(D, BLK, a, grid, stream);
 }

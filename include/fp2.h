@@ -143,26 +143,29 @@ fp2_status fp2_plan_mask(const fp2_batch *batch, const fp2_q *q, int32_t num_kv_
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes fp2_prefill_run needs for this batch, head size and KV
- * dtype (0 if the batch is empty or malformed).  For bf16 with d = 128 and
- * B = 128 it holds V^T tiles of every KV block (one bf16 128 x 128 tile per
- * block and KV head: about the size of V itself), bf16 kbar rows and vbar^T
- * tiles of the mean tokens; otherwise bf16 kbar and fp16 vbar copies. */
+ * dtype (0 if the batch is empty or malformed).  For d = 128 and B = 128 it
+ * holds V^T tiles of every KV block (one bf16 128 x 128 tile per block and
+ * KV head, e4m3 V dequantized: about the size of bf16 V), bf16 kbar rows and
+ * vbar^T tiles of the mean tokens, and for e4m3 also the K codes of every
+ * block widened to bf16 rows (another tile per block and head); otherwise
+ * bf16 kbar and fp16 vbar copies. */
 size_t fp2_run_workspace_bytes(const fp2_batch *batch, int32_t num_kv_heads, int32_t head_dim,
                                fp2_dtype dtype);
 
 /* Stage 2 - exact attention over the kept blocks plus the mean correction
  * of every skipped block (Figure 3 exact path, Figure 4 surrogate terms).
- *   row_ptr, col_idx  the CSR from fp2_plan_mask (any ascending CSR that
- *                     holds block 0 and the diagonal of every row is valid)
+ *   row_ptr, col_idx  the CSR from fp2_plan_mask (any CSR whose rows are
+ *                     ascending, lie in [0, diagonal] and hold block 0 and
+ *                     the diagonal is valid)
  *   kbar, vbar        device float32 [Hkv, total_kblocks, d]
  *   mean_correction   0: skipped blocks are dropped; 1: corrected
  *   softmax_scale     logit scale, normally 1/sqrt(d)
  *   out_dtype         FP2_OUT_BF16 (rounded to nearest even) or FP2_OUT_F32
  *   out               device [total_q, Hq, d] of out_dtype
  *   workspace         device scratch of fp2_run_workspace_bytes() bytes;
- *                     required for bf16 with d = 128 and B = 128, else only
- *                     with mean_correction (FP2_ERR_CAPACITY if too small);
- *                     its contents are overwritten */
+ *                     required with d = 128 and B = 128 (bf16 or e4m3),
+ *                     else only with mean_correction (FP2_ERR_CAPACITY if
+ *                     too small); its contents are overwritten */
 fp2_status fp2_prefill_run(const fp2_batch *batch, const fp2_q *q, const fp2_kv *kv,
                            const int32_t *row_ptr, const int32_t *col_idx,
                            const float *kbar, const float *vbar,

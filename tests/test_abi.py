@@ -53,12 +53,14 @@ def test_sizes_and_counts():
     # seq0: 8 q-blocks, diag 0..7 -> 36; seq1: prefix 128 -> P/B = 1, 1 q-block -> 2
     assert lib.fp2_plan_max_nnz(b, 3) == 3 * (36 + 2)
     assert lib.fp2_plan_workspace_bytes(b, 3) > 0
-    # fp8 (and other head sizes): bf16 kbar + fp16 vbar copies
-    assert lib.fp2_run_workspace_bytes(b, 3, 128, lib.FP2_FP8_E4M3) >= 2 * 3 * (8 + 2) * 128 * 2
-    # bf16, d = 128, B = 128: also a 128 x 128 bf16 V^T tile per KV block and head
+    # d = 128, B = 128: bf16 kbar rows plus a 128 x 128 bf16 V^T tile per KV block and head;
+    # e4m3 also the K codes of every block widened to bf16 rows (another tile each)
     tiles = 3 * (8 + 2) * 128 * 128 * 2
     assert lib.fp2_run_workspace_bytes(b, 3, 128, lib.FP2_BF16) >= tiles + 3 * (8 + 2) * 128 * 2
+    assert lib.fp2_run_workspace_bytes(b, 3, 128, lib.FP2_FP8_E4M3) >= 2 * tiles + 3 * (8 + 2) * 128 * 2
+    # other head sizes: bf16 kbar + fp16 vbar copies only
     assert lib.fp2_run_workspace_bytes(b, 3, 64, lib.FP2_BF16) < tiles
+    assert lib.fp2_run_workspace_bytes(b, 3, 64, lib.FP2_FP8_E4M3) >= 2 * 3 * (8 + 2) * 64 * 2
 
 
 def test_validation_rejects_before_launch():
