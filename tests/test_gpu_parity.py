@@ -231,7 +231,8 @@ def test_empty_batch_and_empty_sequence():
     assert int(Le.nnz.item()) == 0 and int(Le.row_ptr[0].item()) == 0
 
 
-def test_reference_max_refresh_in_every_tile_kind():
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_reference_max_refresh_in_every_tile_kind(dtype):
     """Scores that climb by far more than 64 log2 units along the keys (about 2 per
     key), and one block (2) lying far above every other, under a hand-made mask
     (block 0, block I//2 and the diagonal per query block I): the running
@@ -240,7 +241,8 @@ def test_reference_max_refresh_in_every_tile_kind():
     and the result must still match the oracle on the same mask.  Here one or two
     keys carry each row, so the kernel's one systematic error shows whole: PV
     takes the probabilities rounded to bf16 while the row sum adds them in
-    float32, which moves O by at most 2^-9 max|v|; the bound adds that term."""
+    float32, which moves O by at most 2^-9 max|v|; the bound adds that term.
+    e4m3: one scale per 128-token block and head (query block and head for Q)."""
     import block_sparse_long_blocks_amd as lib
     rng = np.random.default_rng(5)
     B, d, hq, hkv, T = 128, 128, 8, 2, 1024
@@ -249,11 +251,15 @@ def test_reference_max_refresh_in_every_tile_kind():
     k = (0.125 * pos)[:, None, None] + 0.25 * rng.standard_normal((T, hkv, d))
     k[2 * B:3 * B] += 200.0
     v = rng.standard_normal((T, hkv, d))
-    qb, kb, vb = (synth.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
     nb = T // B
     page_table = np.arange(nb, dtype=np.int32)[None, :]
-    batch, queries, kv = lib.from_arrays(B, [T], [T], qb, None, kb.reshape(nb, B, hkv, d),
-                                         vb.reshape(nb, B, hkv, d), page_table)
+    if dtype == "bf16":
+        qc, kc, vc = (synth.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+        qs = ks = vs = None
+    else:
+        (qc, qs), (kc, ks), (vc, vs) = (synth.quantize_blocks_e4m3(x.astype(np.float32), B) for x in (q, k, v))
+    batch, queries, kv = lib.from_arrays(B, [T], [T], qc, qs, kc.reshape(nb, B, hkv, d),
+                                         vc.reshape(nb, B, hkv, d), page_table, k_scale=ks, v_scale=vs)
     keep = np.zeros((hkv, nb, nb), dtype=bool)
     for i in range(nb):
         keep[:, i, [0, i // 2, i]] = True
@@ -264,7 +270,7 @@ def test_reference_max_refresh_in_every_tile_kind():
             cols = np.nonzero(keep[g, i])[0]
             ci.extend(cols.tolist())
             rp.append(len(ci))
-    dec = [synth.bf16_bits_to_f32(x).astype(np.float64) for x in (qb, kb, vb)]
+    dec = O.decode_sequence(dtype, B, qc, qs, kc, ks, vc, vs)
     for corr in (True, False):
         L = lib.PrefillLayer(batch, queries, kv, out_dtype=torch.float32)
         L.stats()
@@ -274,4 +280,4 @@ def test_reference_max_refresh_in_every_tile_kind():
         torch.cuda.synchronize()
         got = L.out[:T].cpu().numpy().astype(np.float64)
         ref = O.run_batch([tuple(dec)], B, 0.0, corr, keeps=[keep])["out"]
-        check_out(got, ref, TOL["bf16"], "f32", extra=2.0 ** -9 * float(np.abs(dec[2]).max()))
+        check_out(got, ref, TOL[dtype], "f32", extra=2.0 ** -9 * float(np.abs(dec[2]).max()))
