@@ -228,7 +228,7 @@ def main():
         "config": {"workload": "c128k_bf16: 1 seq L=131072, 32 q / 8 kv heads, d=128, block 128, band + 16 "
                                "sink columns, tau for 5% kept blocks, mean correction on",
                    "tau": bf["tau"], "density": round(bf["density"], 5), "nnz": bf["nnz"]},
-        "roofline": {"bound": "mfma", "kernel": "attn_bf16_d128_kernel (fp2_prefill_run: plus its V^T preparation "
+        "roofline": {"bound": "mfma", "kernel": "attn_d128_kernel<false> (fp2_prefill_run: plus its V^T preparation "
                                "kernels, ~1% of the call)", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
