@@ -1,4 +1,4 @@
-// Stage 2 for bf16 inputs with head_dim 128 and block 128: block-sparse
+// Stage 2 for head_dim 128 and block 128, bf16 or e4m3 inputs: block-sparse
 // causal GQA attention over the kept KV blocks plus the mean correction of
 // every skipped block, in one online softmax.
 //
@@ -12,25 +12,31 @@
 //    query heads of a KV head times B tokens); each wave owns 32 tokens of one
 //    head, so every K/V tile staged in LDS feeds 256 query rows.
 //  * V is first transposed into V^T tiles (one 128 d x 128 key tile per KV
-//    block and head, keys in the order the PV MFMA consumes them), and the
-//    vbar of the mean tokens likewise; kbar is rounded to bf16 rows.
+//    block and head, keys in the order the PV MFMA consumes them; e4m3 V
+//    dequantized), and the vbar of the mean tokens likewise; kbar is rounded
+//    to bf16 rows; e4m3 K codes of the blocks that can be diagonal are
+//    widened to bf16 rows.
 //  * Tiles stream global -> LDS by DMA (global_load_lds, 16 bytes a lane)
 //    into two LDS buffers: the next tile's DMA runs while the current tile is
 //    computed; one barrier per tile.  No staging registers, no LDS writes
 //    from the waves.
-//  * K tiles (rows = keys) and V^T tiles (rows = d) share one LDS layout:
-//    256-byte rows in groups of four (one 1 KB DMA unit), groups 1088 bytes
-//    apart, 16-byte chunk k of row r in slot k ^ (r & 3).  Every operand read
-//    is a conflict-free ds_read_b128 at one of two per-lane bases plus an
+//  * bf16 K tiles (rows = keys) and V^T tiles (rows = d) share one LDS
+//    layout: 256-byte rows in groups of four (one 1 KB DMA unit), groups 1088
+//    bytes apart, 16-byte chunk k of row r in slot k ^ (r & 3); e4m3 K tiles
+//    are 128-byte rows, chunk c of row r in slot c ^ (r % 8).  Every operand
+//    read is a conflict-free ds_read_b128 at a per-lane base plus an
 //    immediate offset.
-//  * S^T = K Q^T on the bf16 32x32x16 MFMA (a lane holds the keys of one
-//    query, so row max / row sum are in-lane plus one lane^32 exchange);
-//    O^T = V^T P^T on the same MFMA with P straight from the score registers.
-//  * Each tile runs in 32-key steps, software-pipelined: one scheduling
-//    region holds the QK^T MFMAs of step j+1, the PV MFMAs of step j-1 and
-//    the softmax of step j, so matrix cores, LDS and vector ALU overlap
-//    within a wave.  Masks enter as the score accumulator's initial value;
-//    the reference max is refreshed lazily.
+//  * S^T = K Q^T on the bf16 32x32x16 MFMA or the e4m3 32x32x64 MFMA (a lane
+//    holds the keys of one query, so row sums are in-lane plus one lane^32
+//    exchange); O^T = V^T P^T on the bf16 MFMA with P straight from the
+//    score registers.
+//  * Each tile runs in 32-key steps on a fixed instruction schedule: every
+//    MFMA is a slot closed by a scheduling barrier, the QK^T MFMAs of step
+//    j+1 and the PV MFMAs of step j-1 share a region with the softmax of
+//    step j, operand reads run a few slots ahead and the softmax values are
+//    consumed a group or more after they are produced.  Masks are applied
+//    to the exponent; the reference max is refreshed only when probabilities
+//    would reach 2^64.
 #include <type_traits>
 
 #include "attn_common.h"
