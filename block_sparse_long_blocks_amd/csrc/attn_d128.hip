@@ -53,6 +53,8 @@ constexpr int kWGRows = 32 * kWaves;    // packed query rows per workgroup
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left unconstrained
 // (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt immediate for lgkmcnt(0) with vmcnt and expcnt left unconstrained
+constexpr int kWaitLgkm0 = 0xC07F;
 // buffer resource word 3 for raw (untyped, unswizzled) 32-bit buffer loads on gfx9
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kRowBytes = kD * 2;            // a K row (d values) or a V^T row (128 keys), bf16
@@ -496,11 +498,22 @@ struct Wave {
   // with weight B: lb = log2 B added to the exponent, cbs = lb / scl in
   // score units); mode 0 passes whole.  QK8: e4m3 K tile and QK on the
   // 32x32x64 e4m3 MFMA.
+  // The operand reads of the first kLA ops, issued by the caller as early as
+  // it can (see first_reads).
+  template <bool QK8>
+  __device__ __forceinline__ void first_reads(bf16x8 (&fr)[kRing], const uint8_t* Kt, const uint8_t* Vt, int off0,
+                                              int off1, const int (&off8)[4]) const {
+#pragma unroll
+    for (int n = 0; n < kLA; ++n)
+#pragma unroll
+      for (int e = 0; e < op_reads<QK8>(n); ++e)
+        fr[read0<QK8>(n) + e] = *reinterpret_cast<const bf16x8*>(op_addr<QK8>(n, e, Kt, Vt, off0, off1, off8));
+  }
+
   template <bool MASKED, bool QK8, class Dma>
-  __device__ __forceinline__ void tile(bool first, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1,
-                                       const int (&off8)[4], float scl, Dma&& dma, int mode, int tq, int hf, float lb,
-                                       float cbs, int J0, int diag, const uint32_t* kept) {
-    bf16x8 fr[kRing];
+  __device__ __forceinline__ void tile(bf16x8 (&fr)[kRing], bool first, const uint8_t* Kt, const uint8_t* Vt,
+                                       int off0, int off1, const int (&off8)[4], float scl, Dma&& dma, int mode,
+                                       int tq, int hf, float lb, float cbs, int J0, int diag, const uint32_t* kept) {
     bf16x8 pp[2] = {qf[0], qf[0]}, pc[2];
     f32x16 s = f32x16{}, sn = f32x16{};
     Soft st;
@@ -521,12 +534,6 @@ struct Wave {
       lb = 0.f;
       cbs = 0.f;
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int n = 0; n < kLA; ++n)
-#pragma unroll
-      for (int e = 0; e < op_reads<QK8>(n); ++e)
-        fr[read0<QK8>(n) + e] = *reinterpret_cast<const bf16x8*>(op_addr<QK8>(n, e, Kt, Vt, off0, off1, off8));
     __builtin_amdgcn_sched_barrier(0);
     region<0, false, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, 0.f, 0u, dma);  // QK(0)
 #pragma unroll
@@ -606,37 +613,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   const int kend = ld_uniform(a.row_ptr, row + 1);
   const int nexact = kend - kbeg;
 
-  // ---- mean-token tiles that hold at least one skipped block
-  int nmean = 0;
-  if (a.correction && diag > 1) {
-    const int nw = (diag + 32) >> 5;
-    for (int w = t; w < nw; w += kThreads) kept[w] = 0u;
-    __syncthreads();
-    for (int i = kbeg + t; i < kend; i += kThreads) {
-      const int j = a.col_idx[i];
-      atomicOr(&kept[j >> 5], 1u << (j & 31));
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const int ncand = (diag + kBlk - 1) / kBlk;
-      int base = 0;
-      for (int m0 = 0; m0 < ncand; m0 += 64) {
-        const int mt = m0 + lane;
-        bool flag = false;
-        if (mt < ncand) {
-#pragma unroll
-          for (int w = 0; w < kBlk / 32; ++w) flag |= skipped_word(kept, mt * (kBlk / 32) + w, diag) != 0u;
-        }
-        const uint64_t bal = __ballot(flag);
-        if (flag) mtile[base + __popcll(bal & ((1ull << lane) - 1ull))] = mt * kBlk;
-        base += __popcll(bal);
-      }
-      if (lane == 0) s_nmean = base;
-    }
-    __syncthreads();
-    nmean = s_nmean;
-  }
-  const int ntiles = nexact + nmean;
 
   Wave ws;
   ws.m = -INFINITY;
@@ -841,13 +817,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   // tile i+2 and the page entries of tile i+1 arrived with the last barrier,
   // the loads of tile i+3's block index and tile i+2's page entries are in
   // flight.
-  auto mean_of = [&](int idx) -> int { return idx < ntiles ? mtile[idx - nexact] : 0; };
+  // A barrier for LDS data only: the DMA and the loads in flight are not
+  // waited for (the compiler barriers keep LDS accesses on their side).
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Tile 0 is an exact block (the CSR holds block 0): its DMA, the first
+  // page and block-index loads go out before the mean-token setup below.
   int j0 = 0, j1 = 0, j2v = 0, pgv[kDmaHalves] = {};
   if (0 < nexact) j0 = ld_uniform(a.col_idx, kbeg);
-  else if (0 < ntiles) j0 = mean_of(0);
-  if (1 < nexact) j1 = ld_uniform(a.col_idx, kbeg + 1);
-  else if (1 < ntiles) j1 = mean_of(1);
-  if (2 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 2 * 4, 0, 0);
   // e4m3: the K scale of exact tile i (one page per block) arrives with the
   // barrier before tile i (ksv); the page entry of tile i+1 one tile earlier
   // (pgbv)
@@ -856,11 +837,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   int ksv = 0, pgbv = 0;
   if constexpr (FP8) {
     if (0 < nexact) ksv = __builtin_amdgcn_raw_buffer_load_b32(rks, (ld_uniform(pt, j0) * a.hkv + g) * 4, 0, 0);
-    if (1 < nexact) pgbv = __builtin_amdgcn_raw_buffer_load_b32(rpt, j1 * 4, 0, 0);
   }
-  if (ntiles > 0) {
+  if (0 < nexact) {
     int pg0[kDmaHalves] = {};
-    if (0 < nexact && dma_wave) {
+    if (dma_wave) {
 #pragma unroll
       for (int hh = 0; hh < kDmaHalves; ++hh) pg0[hh] = __builtin_amdgcn_readfirstlane(page_of(j0, hh));
     }
@@ -869,6 +849,54 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, V0);
     }
+  }
+
+  // ---- mean-token tiles that hold at least one skipped block
+  int nmean = 0;
+  if (a.correction && diag > 1) {
+    const int nw = (diag + 32) >> 5;
+    for (int w = t; w < nw; w += kThreads) kept[w] = 0u;
+    lds_barrier();
+    for (int i = kbeg + t; i < kend; i += kThreads) {
+      const int j = a.col_idx[i];
+      atomicOr(&kept[j >> 5], 1u << (j & 31));
+    }
+    lds_barrier();
+    if (wave == 0) {
+      const int ncand = (diag + kBlk - 1) / kBlk;
+      int base = 0;
+      for (int m0 = 0; m0 < ncand; m0 += 64) {
+        const int mt = m0 + lane;
+        bool flag = false;
+        if (mt < ncand) {
+#pragma unroll
+          for (int w = 0; w < kBlk / 32; ++w) flag |= skipped_word(kept, mt * (kBlk / 32) + w, diag) != 0u;
+        }
+        const uint64_t bal = __ballot(flag);
+        if (flag) mtile[base + __popcll(bal & ((1ull << lane) - 1ull))] = mt * kBlk;
+        base += __popcll(bal);
+      }
+      if (lane == 0) s_nmean = base;
+    }
+    lds_barrier();
+    nmean = s_nmean;
+  }
+  const int ntiles = nexact + nmean;
+  auto mean_of = [&](int idx) -> int { return idx < ntiles ? mtile[idx - nexact] : 0; };
+  if (nexact == 0 && ntiles > 0) {  // (not produced by fp2_plan_mask: every row holds block 0)
+    j0 = mean_of(0);
+    const int pg0[kDmaHalves] = {};
+    const DmaPlan pl = plan(0, j0, pg0, K0, V0);
+    if (pl.fast) {
+#pragma unroll
+      for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, V0);
+    }
+  }
+  if (1 < nexact) j1 = ld_uniform(a.col_idx, kbeg + 1);
+  else if (1 < ntiles) j1 = mean_of(1);
+  if (2 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 2 * 4, 0, 0);
+  if constexpr (FP8) {
+    if (1 < nexact) pgbv = __builtin_amdgcn_raw_buffer_load_b32(rpt, j1 * 4, 0, 0);
   }
   if (1 < nexact && dma_wave) {
 #pragma unroll
@@ -881,6 +909,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   // MASKED_C: std::integral_constant<bool, ...>, the tile code path (see below)
   auto iter = [&](auto masked_c, int idx, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
     constexpr bool MASKED = decltype(masked_c)::value;
+    // the tile's first operand reads go out before the bookkeeping below
+    bf16x8 fr[Wave::kRing];
+    if (wave_active) ws.first_reads<FP8 && !MASKED>(fr, Kc, Vc, off0, off1, off8);
+    __builtin_amdgcn_sched_barrier(0);
     const int j2 = idx + 2 < nexact ? after_barrier(j2v) : mean_of(idx + 2);
     float sclt = scl;
     if constexpr (FP8) {
@@ -913,11 +945,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
         for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, Vn);
       }
     } else if constexpr (!MASKED) {
-      ws.tile<false, FP8>(idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, 0, tq, hf, 0.f, 0.f, 0, diag, kept);
+      ws.tile<false, FP8>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, 0, tq, hf, 0.f, 0.f, 0, diag, kept);
     } else {
       // mean tiles: weight B, log2 B in the exponent (cbs in score units)
       const float lbm = mode == 2 ? a.log2_block : 0.f;
-      ws.tile<true, false>(idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, mode, tq, hf, lbm, lbm / sclt, j0, diag,
+      ws.tile<true, false>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, mode, tq, hf, lbm, lbm / sclt, j0, diag,
                            kept);
     }
     j0 = j1;
