@@ -437,6 +437,8 @@ struct Wave {
                                          const int (&off8)[4], float scl, float nbm, uint32_t M, Dma& dma) {
     constexpr int N0 = region_start<QK8>(R), S = region_start<QK8>(R + 1) - N0;
     constexpr int kDma0 = QK8 ? 4 : 8;
+    // the younger wave's issue priority ends half way (see the tile loop)
+    if constexpr (R == 3) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int t = 0; t < S; ++t) {
       const int n = N0 + t;
@@ -936,6 +938,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     }
     if (idx + 3 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, (idx + 3) * 4, 0, 0);
     const int mode = idx >= nexact ? 2 : (j0 == diag ? 1 : 0);
+    // The issue arbiter serves the older wave of a SIMD first (waves 0-3,
+    // which also issue the DMA): the younger waves 4-7 get the higher issue
+    // priority until region 3 so that the two finish a tile closer together.
+    if (wave >= kDmaWaves) __builtin_amdgcn_s_setprio(1);
     auto dma = [&](int i) __attribute__((always_inline)) {
       if (pl.fast) issue(pl, i, Vn);
     };
@@ -952,6 +958,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
       ws.tile<true, false>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, mode, tq, hf, lbm, lbm / sclt, j0, diag,
                            kept);
     }
+    __builtin_amdgcn_s_setprio(0);
     j0 = j1;
     j1 = j2;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's DMA and loads for later tiles have landed
