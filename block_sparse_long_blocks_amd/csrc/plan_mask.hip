@@ -11,7 +11,8 @@
 //   score_select : one workgroup per CSR row (query block I, KV head g).
 //                  Pools qbar over the block's tokens and the G heads of the
 //                  group (float32, fixed order), scores every causal KV block
-//                  against kbar (float32 dot products), reduces the row
+//                  against kbar (float32 dot products, d/8 lanes per kbar
+//                  row so that the loads coalesce), reduces the row
 //                  maximum, applies s >= max - tau and writes a keep bitmask
 //                  and the row's kept count.
 //   scan_counts  : one workgroup; exclusive scan of the counts -> row_ptr, nnz.
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
     if (ESZ == 1) mul = a.q_scale[(int64_t)qb * a.hq + h];
     const uint8_t* base = a.q + ((int64_t)(q0 + I * a.block) * a.hq + g * G) * a.d * ESZ + c * 16;
     const int64_t tok_stride = (int64_t)a.hq * a.d * ESZ;
-    constexpr int U = 4;
+    constexpr int U = 8;
     int tok = r;
     for (; tok + (U - 1) * R < ntok; tok += U * R) {
       uint4 w[U];
@@ -125,22 +126,48 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
   }
   __syncthreads();
 
-  // ---- scores for J = 0..diag: float32 dot(qbar, kbar_J) * scale
+  // ---- scores for J = 0..diag: float32 dot(qbar, kbar_J) * scale.  LPB =
+  // d/8 lanes share a kbar row (8 floats each, so a wave's loads cover
+  // 64/LPB whole rows), then sum their partials across the lanes.
   const float* kb = a.kbar + ((int64_t)g * a.total_kblocks + a.cu_kblocks[s]) * a.d;
+  const int lpb = a.d / 8;           // 16 (d = 128) or 8 (d = 64)
+  const int bpw = 64 / lpb;          // rows per wave and load
+  const int lane = t & 63, sub = lane % lpb;
+  float qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qv[e] = s_qbar[8 * sub + e];
   float lmax = -INFINITY;
-  for (int J = t; J <= diag; J += kThreads) {
-    const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (int64_t)J * a.d);
-    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-    for (int e4 = 0; e4 < a.d / 4; ++e4) {
-      const f32x4 k4 = kr[e4];
-      p0 = fmaf(s_qbar[4 * e4 + 0], k4[0], p0);
-      p1 = fmaf(s_qbar[4 * e4 + 1], k4[1], p1);
-      p2 = fmaf(s_qbar[4 * e4 + 2], k4[2], p2);
-      p3 = fmaf(s_qbar[4 * e4 + 3], k4[3], p3);
+  constexpr int UJ = 4;  // row groups whose loads are in flight together
+  const int jstep = (kThreads / 64) * bpw;
+  for (int J0 = (t >> 6) * bpw; J0 <= diag; J0 += UJ * jstep) {
+    f32x4 k0[UJ], k1[UJ];
+#pragma unroll
+    for (int u = 0; u < UJ; ++u) {
+      const int J = J0 + u * jstep + lane / lpb;
+      k0[u] = k1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (J <= diag) {
+        const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (int64_t)J * a.d + 8 * sub);
+        k0[u] = kr[0];
+        k1[u] = kr[1];
+      }
     }
-    const float sc = ((p0 + p1) + (p2 + p3)) * a.scale;
-    s_scores[J] = sc;
-    lmax = fmaxf(lmax, sc);
+#pragma unroll
+    for (int u = 0; u < UJ; ++u) {
+      const int J = J0 + u * jstep + lane / lpb;
+      float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p0 = fmaf(qv[e], k0[u][e], p0);
+        p1 = fmaf(qv[4 + e], k1[u][e], p1);
+      }
+      float p = p0 + p1;
+      for (int m = lpb >> 1; m > 0; m >>= 1) p += __shfl_xor(p, m);
+      if (J <= diag) {
+        const float sc = p * a.scale;
+        if (sub == 0) s_scores[J] = sc;
+        lmax = fmaxf(lmax, sc);
+      }
+    }
   }
   lmax = wave_max(lmax);
   if ((t & 63) == 0) s_wmax[t >> 6] = lmax;
