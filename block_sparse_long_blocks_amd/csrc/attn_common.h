@@ -30,6 +30,7 @@ struct AttnArgs {
   const uint8_t* vt;       // V^T tiles of every KV block (bf16 d128 kernel)
   const uint8_t* vbt;      // vbar^T tiles of the mean tokens (bf16 d128 kernel)
   const uint8_t* kd;       // e4m3 d128 kernel: K codes as bf16 rows of the diagonal-capable blocks
+  int32_t* order;          // d128 kernel: CSR ranks in launch order (heaviest first), [rows]
   void* out;               // bf16 or f32 [total_q, Hq, D]
   float scale_log2;        // softmax_scale * log2(e)
   float log2_block;        // log2(B): weight B of a mean token
@@ -41,8 +42,9 @@ struct AttnArgs {
 
 // Transposes V (and vbar, and rounds kbar) into the workspace parts that
 // a.vt, a.vbt and a.kbar16 point to (e4m3: V dequantized, and the K codes of
-// the blocks that can be diagonal widened to bf16 rows at a.kd), then runs
-// the d=128 B=128 kernel.
+// the blocks that can be diagonal widened to bf16 rows at a.kd), orders the
+// CSR rows by their tile count (heaviest first, at a.order), then runs the
+// d=128 B=128 kernel.
 hipError_t launch_attn_d128(const AttnArgs& a, bool fp8, const float* kbar, const float* vbar, int max_kblocks,
                             hipStream_t stream);
 

@@ -575,15 +575,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   __shared__ int mtile[kMaxKBlocks / kBlk + 1];
   __shared__ int s_nmean;
 
-  // ---- tile decode: 8 consecutive CSR ranks form a group, the slices of
-  // one rank share blockIdx % 8 (one XCD), latest query blocks first
+  // ---- tile decode: 8 consecutive positions of the launch order form a
+  // group, the slices of one position share blockIdx % 8 (one XCD); the
+  // order holds the CSR ranks heaviest first (rank r: query block
+  // total_qblocks - 1 - r / Hkv, KV head r % Hkv)
   const int b = blockIdx.x;
   const int per_grp = 8 * a.slices;
   const int grp = b / per_grp;
   const int rem = b % per_grp;
   const int slice = rem / 8;
-  const int rank = grp * 8 + (rem % 8);
-  if (rank >= a.rows) return;
+  const int pos = grp * 8 + (rem % 8);
+  if (pos >= a.rows) return;
+  const int rank = ld_uniform(a.order, pos);
   const int qb = a.total_qblocks - 1 - rank / a.hkv;
   const int g = rank % a.hkv;
   const int row = g * a.total_qblocks + qb;
@@ -1017,6 +1020,61 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   }
 }
 
+// Tiles of CSR rank r (rank r: query block total_qblocks - 1 - r / Hkv, KV
+// head r % Hkv): its kept blocks plus, with the correction, the mean-token
+// tiles it can have (an upper bound), capped at nbins - 1.
+__device__ int rank_tiles(const AttnArgs& a, int r, int nbins) {
+  const int qb = a.total_qblocks - 1 - r / a.hkv;
+  const int row = (r % a.hkv) * a.total_qblocks + qb;
+  int w = a.row_ptr[row + 1] - a.row_ptr[row];
+  if (a.correction) {
+    const int s = find_seq(a.cu_qblocks, a.num_seqs, qb);
+    const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
+    const int diag = (a.seqlens_k[s] - n) / kBlk + qb - a.cu_qblocks[s];
+    w += (diag + kBlk - 1) / kBlk;
+  }
+  return min(max(w, 0), nbins - 1);
+}
+
+// Launch order of the CSR ranks, heaviest first (longest-processing-time
+// order: the rows' tile counts are very uneven under a max-based threshold,
+// and a heavy row started last would leave the other CUs idle).  One
+// workgroup: counting sort on the tile count; ranks of equal count land in
+// any order (each row's result does not depend on it).
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderMaxBins = 8192;  // 32 KB of LDS; heavier rows share the top bin
+__global__ __launch_bounds__(kOrderThreads) void order_rows_kernel(AttnArgs a, int nbins) {
+  extern __shared__ int hist[];  // [nbins]
+  __shared__ int part[kOrderThreads];
+  const int t = threadIdx.x;
+  for (int i = t; i < nbins; i += kOrderThreads) hist[i] = 0;
+  __syncthreads();
+  for (int r = t; r < a.rows; r += kOrderThreads) atomicAdd(&hist[rank_tiles(a, r, nbins)], 1);
+  __syncthreads();
+  // exclusive scan in descending tile count: bin w starts after every rank
+  // with more tiles; thread t owns bins nbins-1-k for k in its chunk
+  const int chunk = (nbins + kOrderThreads - 1) / kOrderThreads;
+  const int k0 = min(t * chunk, nbins), k1 = min(k0 + chunk, nbins);
+  int sum = 0;
+  for (int k = k0; k < k1; ++k) sum += hist[nbins - 1 - k];
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < kOrderThreads; off <<= 1) {
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - sum;
+  for (int k = k0; k < k1; ++k) {
+    const int c = hist[nbins - 1 - k];
+    hist[nbins - 1 - k] = run;
+    run += c;
+  }
+  __syncthreads();
+  for (int r = t; r < a.rows; r += kOrderThreads) a.order[atomicAdd(&hist[rank_tiles(a, r, nbins)], 1)] = r;
+}
+
 hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const float* vbar, int max_kblocks,
                        hipStream_t stream) {
   AttnArgs a = a_in;
@@ -1060,6 +1118,12 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
+  }
+  if (a.rows > 0) {
+    const int nbins = min(max_kblocks + (max_kblocks + kBlk - 1) / kBlk + 1, kOrderMaxBins);
+    hipLaunchKernelGGL(order_rows_kernel, dim3(1), dim3(kOrderThreads), (size_t)nbins * sizeof(int), stream, a, nbins);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   const int G = a.hq / a.hkv;
   a.slices = (G * kBlk + kWGRows - 1) / kWGRows;

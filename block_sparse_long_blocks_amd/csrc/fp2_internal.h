@@ -47,6 +47,7 @@ struct RunLayout {
   size_t v16 = 0;      // fp16 vbar rows (register-staged path) or vbar^T tiles (V^T path)
   size_t vt = 0;       // V^T tiles of every KV block (V^T path)
   size_t kd = 0;       // e4m3 V^T path: K codes as bf16 rows, [Hkv, total_kblocks, B, d]
+  size_t order = 0;    // V^T path: CSR rows in launch order, int32 [Hkv * total_qblocks]
   size_t total = 0;
   int64_t mt_cap = 0;  // vbar^T tiles per KV head (V^T path)
 };

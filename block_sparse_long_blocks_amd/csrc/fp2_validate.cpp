@@ -152,6 +152,8 @@ RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_kv_heads, int 
       L.kd = L.total;
       L.total = L.kd + hkv * tkb * tile;
     }
+    L.order = L.total;
+    L.total = L.order + up(hkv * (size_t)info.total_qblocks * 4);
   } else {
     L.total = L.v16 + rows;
   }

@@ -594,6 +594,7 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.vt = wsb + L.vt;
   a.vbt = wsb + L.v16;
   a.kd = wsb + L.kd;
+  a.order = reinterpret_cast<int32_t*>(wsb + L.order);
   a.mt_cap = (int)L.mt_cap;
   a.out = out;
   a.out_f32 = out_f32;
