@@ -146,9 +146,10 @@ fp2_status fp2_plan_mask(const fp2_batch *batch, const fp2_q *q, int32_t num_kv_
  * dtype (0 if the batch is empty or malformed).  For d = 128 and B = 128 it
  * holds V^T tiles of every KV block (one bf16 128 x 128 tile per block and
  * KV head, e4m3 V dequantized: about the size of bf16 V), bf16 kbar rows and
- * vbar^T tiles of the mean tokens, and for e4m3 also the K codes of every
- * block widened to bf16 rows (another tile per block and head); otherwise
- * bf16 kbar and fp16 vbar copies. */
+ * vbar^T tiles of the mean tokens, for e4m3 also the K codes of every
+ * block widened to bf16 rows (another tile per block and head), and the
+ * launch order of the CSR rows (one int32 per row, heaviest first);
+ * otherwise bf16 kbar and fp16 vbar copies. */
 size_t fp2_run_workspace_bytes(const fp2_batch *batch, int32_t num_kv_heads, int32_t head_dim,
                                fp2_dtype dtype);
 
