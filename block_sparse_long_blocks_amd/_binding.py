@@ -63,7 +63,8 @@ _lib.fp2_plan_max_nnz.restype = ctypes.c_int64
 _lib.fp2_plan_mask.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CQ), ctypes.c_int32, _p,
                                ctypes.c_float, _p, _p, ctypes.c_int64, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.fp2_plan_mask.restype = ctypes.c_int
-_lib.fp2_run_workspace_bytes.argtypes = [ctypes.POINTER(CBatch), ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
+_lib.fp2_run_workspace_bytes.argtypes = [ctypes.POINTER(CBatch), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int]
 _lib.fp2_run_workspace_bytes.restype = ctypes.c_size_t
 _lib.fp2_prefill_run.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CQ), ctypes.POINTER(CKV), _p, _p,
                                  _p, _p, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _p, _p, ctypes.c_size_t,
@@ -209,10 +210,10 @@ def fp2_plan_mask(batch: Batch, q: Queries, num_kv_heads: int, kbar: torch.Tenso
                               _stream(stream)))
 
 
-def fp2_run_workspace_bytes(batch: Batch, num_kv_heads: int, head_dim: int, dtype: int) -> int:
+def fp2_run_workspace_bytes(batch: Batch, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int) -> int:
     """dtype: FP2_BF16 or FP2_FP8_E4M3 (the KV cache's)."""
     b = batch.c
-    return int(_lib.fp2_run_workspace_bytes(ctypes.byref(b), num_kv_heads, head_dim, dtype))
+    return int(_lib.fp2_run_workspace_bytes(ctypes.byref(b), num_q_heads, num_kv_heads, head_dim, dtype))
 
 
 def fp2_prefill_run(batch: Batch, q: Queries, kv: KVCache, row_ptr: torch.Tensor, col_idx: torch.Tensor,

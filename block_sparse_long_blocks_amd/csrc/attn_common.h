@@ -30,7 +30,13 @@ struct AttnArgs {
   const uint8_t* vt;       // V^T tiles of every KV block (bf16 d128 kernel)
   const uint8_t* vbt;      // vbar^T tiles of the mean tokens (bf16 d128 kernel)
   const uint8_t* kd;       // e4m3 d128 kernel: K codes as bf16 rows of the diagonal-capable blocks
-  int32_t* order;          // d128 kernel: CSR ranks in launch order (heaviest first), [rows]
+  int4* items;             // d128 kernel: work items {rank, first tile, end tile, partial slot or -1},
+                           // heaviest first, [rows + extra_cap]
+  int4* splits;            // d128 kernel: split rows {rank, first slot, chunks, 0}, [extra_cap]
+  int32_t* rank_slot;      // d128 kernel: first partial slot of each split row (items kernel scratch)
+  int32_t* counters;       // d128 kernel: [0] work items, [1] split rows
+  float* part;             // d128 kernel: partial O, reference max and row sum of split-row chunks
+  int extra_cap, chunk_cap, ncu;
   void* out;               // bf16 or f32 [total_q, Hq, D]
   float scale_log2;        // softmax_scale * log2(e)
   float log2_block;        // log2(B): weight B of a mean token
@@ -42,9 +48,9 @@ struct AttnArgs {
 
 // Transposes V (and vbar, and rounds kbar) into the workspace parts that
 // a.vt, a.vbt and a.kbar16 point to (e4m3: V dequantized, and the K codes of
-// the blocks that can be diagonal widened to bf16 rows at a.kd), orders the
-// CSR rows by their tile count (heaviest first, at a.order), then runs the
-// d=128 B=128 kernel.
+// the blocks that can be diagonal widened to bf16 rows at a.kd), builds the
+// work items (the exact tiles of heavy rows split into chunks, heaviest item
+// first), runs the d=128 B=128 kernel and merges the chunks of split rows.
 hipError_t launch_attn_d128(const AttnArgs& a, bool fp8, const float* kbar, const float* vbar, int max_kblocks,
                             hipStream_t stream);
 

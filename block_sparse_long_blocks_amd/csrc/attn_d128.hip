@@ -575,18 +575,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   __shared__ int mtile[kMaxKBlocks / kBlk + 1];
   __shared__ int s_nmean;
 
-  // ---- tile decode: 8 consecutive positions of the launch order form a
-  // group, the slices of one position share blockIdx % 8 (one XCD); the
-  // order holds the CSR ranks heaviest first (rank r: query block
-  // total_qblocks - 1 - r / Hkv, KV head r % Hkv)
+  // ---- tile decode: 8 consecutive work items form a group, the slices of
+  // one item share blockIdx % 8 (one XCD); the items are in launch order,
+  // heaviest first: {CSR rank, first and end exact tile of the row, partial
+  // slot or -1} (rank r: query block total_qblocks - 1 - r / Hkv, KV head
+  // r % Hkv)
   const int b = blockIdx.x;
   const int per_grp = 8 * a.slices;
   const int grp = b / per_grp;
   const int rem = b % per_grp;
   const int slice = rem / 8;
   const int pos = grp * 8 + (rem % 8);
-  if (pos >= a.rows) return;
-  const int rank = ld_uniform(a.order, pos);
+  if (pos >= ld_uniform(a.counters, 0)) return;
+  const int32_t* item = reinterpret_cast<const int32_t*>(a.items + pos);
+  const int rank = ld_uniform(item, 0);
+  const int tile0 = ld_uniform(item, 1), tile1 = ld_uniform(item, 2), pslot = ld_uniform(item, 3);
   const int qb = a.total_qblocks - 1 - rank / a.hkv;
   const int g = rank % a.hkv;
   const int row = g * a.total_qblocks + qb;
@@ -614,9 +617,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
 
   // uniform values: later loads indexed by them become scalar loads, which
   // do not share the vector-memory counter with the tile DMA
-  const int kbeg = ld_uniform(a.row_ptr, row);
-  const int kend = ld_uniform(a.row_ptr, row + 1);
+  const int rbeg = ld_uniform(a.row_ptr, row);
+  const int rend = ld_uniform(a.row_ptr, row + 1);
+  // this item's exact tiles; the mean tiles go with the row's last item
+  const int kbeg = rbeg + tile0;
+  const int kend = rbeg + tile1;
   const int nexact = kend - kbeg;
+  const bool last_item = kend == rend;
 
 
   Wave ws;
@@ -858,11 +865,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
 
   // ---- mean-token tiles that hold at least one skipped block
   int nmean = 0;
-  if (a.correction && diag > 1) {
+  if (a.correction && diag > 1 && last_item) {
     const int nw = (diag + 32) >> 5;
     for (int w = t; w < nw; w += kThreads) kept[w] = 0u;
     lds_barrier();
-    for (int i = kbeg + t; i < kend; i += kThreads) {
+    for (int i = rbeg + t; i < rend; i += kThreads) {
       const int j = a.col_idx[i];
       atomicOr(&kept[j >> 5], 1u << (j & 31));
     }
@@ -992,8 +999,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     if (idx + 1 < ntiles) iter(masked_c, idx + 1, K1, V1, K0, V0);
   }
 
-  // ---- epilogue: O / l
-  if (q_valid) {
+  // ---- epilogue: O / l, or the chunk's partial result in register layout
+  if (pslot >= 0) {
+    if (wave_active) {
+      float* po = a.part + ((int64_t)(pslot * a.slices + slice) * kWaves + wave) * kPartFloatsPerWave;
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(po + ((dt * 4 + q4) * 64 + lane) * 4) =
+              f32x4{ws.o[dt][4 * q4 + 0], ws.o[dt][4 * q4 + 1], ws.o[dt][4 * q4 + 2], ws.o[dt][4 * q4 + 3]};
+      const float lsum = sum_halves(ws.l);
+      *reinterpret_cast<float2*>(po + 64 * 64 + 2 * lane) = make_float2(ws.m, lsum);
+    }
+  } else if (q_valid) {
     const float inv = 1.0f / sum_halves(ws.l);
     const int64_t obase = ((int64_t)(q0 + I * kBlk + tq) * a.hq + h) * kD;
     if (a.out_f32) {
@@ -1020,46 +1039,88 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   }
 }
 
-// Tiles of CSR rank r (rank r: query block total_qblocks - 1 - r / Hkv, KV
-// head r % Hkv): its kept blocks plus, with the correction, the mean-token
-// tiles it can have (an upper bound), capped at nbins - 1.
-__device__ int rank_tiles(const AttnArgs& a, int r, int nbins) {
+// Exact tiles of CSR rank r (rank r: query block total_qblocks - 1 - r / Hkv,
+// KV head r % Hkv) and, with the correction, the mean-token tiles it can have
+// (an upper bound).
+__device__ void rank_tiles(const AttnArgs& a, int r, int& nexact, int& nmean) {
   const int qb = a.total_qblocks - 1 - r / a.hkv;
   const int row = (r % a.hkv) * a.total_qblocks + qb;
-  int w = a.row_ptr[row + 1] - a.row_ptr[row];
+  nexact = max(a.row_ptr[row + 1] - a.row_ptr[row], 0);
+  nmean = 0;
   if (a.correction) {
     const int s = find_seq(a.cu_qblocks, a.num_seqs, qb);
     const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
     const int diag = (a.seqlens_k[s] - n) / kBlk + qb - a.cu_qblocks[s];
-    w += (diag + kBlk - 1) / kBlk;
+    nmean = (diag + kBlk - 1) / kBlk;
   }
-  return min(max(w, 0), nbins - 1);
 }
 
-// Launch order of the CSR ranks, heaviest first (longest-processing-time
-// order: the rows' tile counts are very uneven under a max-based threshold,
-// and a heavy row started last would leave the other CUs idle).  One
-// workgroup: counting sort on the tile count; ranks of equal count land in
-// any order (each row's result does not depend on it).
-constexpr int kOrderThreads = 1024;
-constexpr int kOrderMaxBins = 8192;  // 32 KB of LDS; heavier rows share the top bin
-__global__ __launch_bounds__(kOrderThreads) void order_rows_kernel(AttnArgs a, int nbins) {
+// Work items and their launch order.  The kept-block counts of the rows are
+// very uneven under a max-based threshold (a few rows keep most of their
+// causal blocks), so the exact tiles of a row with more than C of them are
+// split into near-equal chunks, each its own item (the row's last chunk also
+// takes its mean tiles); C is chosen so that no item holds more than a
+// quarter of a CU's share of the work, and so that the extra items stay
+// within extra_cap.  Items are launched heaviest first (longest processing
+// time first: a heavy item started last would leave the other CUs idle).  One
+// workgroup: a counting sort on the item's tile count; items of equal count
+// land in any order (no result depends on it).
+constexpr int kItemsThreads = 1024;
+constexpr int kItemsMaxBins = 8192;  // 32 KB of LDS; heavier items share the top bin
+constexpr int kMinChunkTiles = 16;
+constexpr int kItemsPerCuShare = 4;
+__global__ __launch_bounds__(kItemsThreads) void items_kernel(AttnArgs a, int nbins) {
   extern __shared__ int hist[];  // [nbins]
-  __shared__ int part[kOrderThreads];
+  __shared__ int part[kItemsThreads];
+  __shared__ int s_tot[2], s_cnt[3];
   const int t = threadIdx.x;
-  for (int i = t; i < nbins; i += kOrderThreads) hist[i] = 0;
+  for (int i = t; i < nbins; i += kItemsThreads) hist[i] = 0;
+  if (t < 2) s_tot[t] = 0;
+  if (t < 3) s_cnt[t] = 0;
   __syncthreads();
-  for (int r = t; r < a.rows; r += kOrderThreads) atomicAdd(&hist[rank_tiles(a, r, nbins)], 1);
+  int ex = 0, all = 0;
+  for (int r = t; r < a.rows; r += kItemsThreads) {
+    int ne, nm;
+    rank_tiles(a, r, ne, nm);
+    ex += ne;
+    all += ne + nm;
+  }
+  atomicAdd(&s_tot[0], ex);
+  atomicAdd(&s_tot[1], all);
   __syncthreads();
-  // exclusive scan in descending tile count: bin w starts after every rank
+  int C = 0x7fffffff;  // tiles per chunk: no split without extra items
+  if (a.extra_cap > 0) {
+    const int64_t share = ((int64_t)s_tot[1] * a.slices + a.ncu - 1) / max(a.ncu, 1);
+    C = (int)max<int64_t>(kMinChunkTiles, (share + kItemsPerCuShare - 1) / kItemsPerCuShare);
+    if (a.chunk_cap > 0) C = min(C, a.chunk_cap);
+    C = max(C, (s_tot[0] + a.extra_cap - 1) / a.extra_cap);  // sum over rows of (chunks - 1) <= extra_cap
+  }
+  // pass 1: histogram of the items' tile counts; partial slots of split rows
+  for (int r = t; r < a.rows; r += kItemsThreads) {
+    int ne, nm;
+    rank_tiles(a, r, ne, nm);
+    const int nch = ne > C ? (ne + C - 1) / C : 1;
+    if (nch > 1) {
+      const int slot0 = atomicAdd(&s_cnt[1], nch);
+      a.splits[atomicAdd(&s_cnt[2], 1)] = make_int4(r, slot0, nch, 0);
+      a.rank_slot[r] = slot0;
+    }
+    atomicAdd(&s_cnt[0], nch);
+    for (int c = 0; c < nch; ++c) {
+      const int w = (int)(((int64_t)(c + 1) * ne) / nch - ((int64_t)c * ne) / nch) + (c == nch - 1 ? nm : 0);
+      atomicAdd(&hist[min(w, nbins - 1)], 1);
+    }
+  }
+  __syncthreads();
+  // exclusive scan in descending tile count: bin w starts after every item
   // with more tiles; thread t owns bins nbins-1-k for k in its chunk
-  const int chunk = (nbins + kOrderThreads - 1) / kOrderThreads;
+  const int chunk = (nbins + kItemsThreads - 1) / kItemsThreads;
   const int k0 = min(t * chunk, nbins), k1 = min(k0 + chunk, nbins);
   int sum = 0;
   for (int k = k0; k < k1; ++k) sum += hist[nbins - 1 - k];
   part[t] = sum;
   __syncthreads();
-  for (int off = 1; off < kOrderThreads; off <<= 1) {
+  for (int off = 1; off < kItemsThreads; off <<= 1) {
     const int v = t >= off ? part[t - off] : 0;
     __syncthreads();
     part[t] += v;
@@ -1072,7 +1133,86 @@ __global__ __launch_bounds__(kOrderThreads) void order_rows_kernel(AttnArgs a, i
     run += c;
   }
   __syncthreads();
-  for (int r = t; r < a.rows; r += kOrderThreads) a.order[atomicAdd(&hist[rank_tiles(a, r, nbins)], 1)] = r;
+  // pass 2: place the items
+  for (int r = t; r < a.rows; r += kItemsThreads) {
+    int ne, nm;
+    rank_tiles(a, r, ne, nm);
+    const int nch = ne > C ? (ne + C - 1) / C : 1;
+    const int slot0 = nch > 1 ? a.rank_slot[r] : -1;
+    for (int c = 0; c < nch; ++c) {
+      const int c0 = (int)(((int64_t)c * ne) / nch), c1 = (int)(((int64_t)(c + 1) * ne) / nch);
+      const int w = c1 - c0 + (c == nch - 1 ? nm : 0);
+      a.items[atomicAdd(&hist[min(w, nbins - 1)], 1)] = make_int4(r, c0, c1, nch > 1 ? slot0 + c : -1);
+    }
+  }
+  if (t == 0) {
+    a.counters[0] = s_cnt[0];
+    a.counters[1] = s_cnt[2];
+  }
+}
+
+// Merges the chunks of each split row: O = sum_c 2^(m_c - M) O_c over
+// sum_c 2^(m_c - M) l_c, M = max_c m_c (the chunks' reference maxima, log2
+// units), then the same O / l store as the attention epilogue.  One
+// workgroup per (split row, slice), the attention kernel's lane layout.
+__global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
+  if ((int)blockIdx.x >= ld_uniform(a.counters, 1)) return;
+  const int32_t* sp = reinterpret_cast<const int32_t*>(a.splits + blockIdx.x);
+  const int rank = ld_uniform(sp, 0), slot0 = ld_uniform(sp, 1), nch = ld_uniform(sp, 2);
+  const int slice = blockIdx.y;
+  const int qb = a.total_qblocks - 1 - rank / a.hkv;
+  const int g = rank % a.hkv;
+  const int s = find_seq(a.cu_qblocks, a.num_seqs, qb);
+  const int I = qb - a.cu_qblocks[s];
+  const int q0 = a.cu_seqlens_q[s];
+  const int n = a.cu_seqlens_q[s + 1] - q0;
+  const int G = a.hq / a.hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5;
+  const int prow = slice * kWGRows + wave * 32;
+  const int h = g * G + prow / kBlk;
+  const int tq = prow % kBlk + (lane & 31);
+  if (!(prow < G * kBlk) || I * kBlk + tq >= n) return;
+  auto chunk_part = [&](int c) {
+    return a.part + ((int64_t)((slot0 + c) * a.slices + slice) * kWaves + wave) * kPartFloatsPerWave;
+  };
+  float M = -INFINITY;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, chunk_part(c)[64 * 64 + 2 * lane]);
+  f32x4 acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const float* po = chunk_part(c);
+    const float2 ml = *reinterpret_cast<const float2*>(po + 64 * 64 + 2 * lane);
+    const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+    L = fmaf(w, ml.y, L);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(po + (j * 64 + lane) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[j][e] = fmaf(w, v[e], acc[j][e]);
+    }
+  }
+  const float inv = 1.0f / L;
+  const int64_t obase = ((int64_t)(q0 + I * kBlk + tq) * a.hq + h) * kD;
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 v = acc[dt * 4 + q4];
+      const int d0 = 32 * dt + 8 * q4 + 4 * hf;
+      if (a.out_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + obase + d0) =
+            f32x4{v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv};
+      } else {
+        uint2 o;
+        o.x = pack_bf16x2(v[0] * inv, v[1] * inv);
+        o.y = pack_bf16x2(v[2] * inv, v[3] * inv);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase + d0) = o;
+      }
+    }
 }
 
 hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const float* vbar, int max_kblocks,
@@ -1119,19 +1259,28 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
       if (e != hipSuccess) return e;
     }
   }
-  if (a.rows > 0) {
-    const int nbins = min(max_kblocks + (max_kblocks + kBlk - 1) / kBlk + 1, kOrderMaxBins);
-    hipLaunchKernelGGL(order_rows_kernel, dim3(1), dim3(kOrderThreads), (size_t)nbins * sizeof(int), stream, a, nbins);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  if (a.rows <= 0) return hipSuccess;
   const int G = a.hq / a.hkv;
   a.slices = (G * kBlk + kWGRows - 1) / kWGRows;
-  const unsigned grid = (unsigned)(((a.rows + 7) / 8) * 8 * a.slices);
+  int dev = 0;
+  a.ncu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0) a.ncu = ncu;
+  }
+  const int nbins = min(max_kblocks + (max_kblocks + kBlk - 1) / kBlk + 1, kItemsMaxBins);
+  hipLaunchKernelGGL(items_kernel, dim3(1), dim3(kItemsThreads), (size_t)nbins * sizeof(int), stream, a, nbins);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int items_cap = a.rows + a.extra_cap;
+  const unsigned grid = (unsigned)(((items_cap + 7) / 8) * 8 * a.slices);
   if (fp8)
     hipLaunchKernelGGL(attn_d128_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(attn_d128_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.extra_cap <= 0) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)a.extra_cap, (unsigned)a.slices), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -87,11 +87,12 @@ fp2_status fp2_plan_mask(const fp2_batch* batch, const fp2_q* q, int32_t num_kv_
                     "fp2_plan_mask launch");
 }
 
-size_t fp2_run_workspace_bytes(const fp2_batch* batch, int32_t num_kv_heads, int32_t head_dim,
-                               fp2_dtype dtype) {
+size_t fp2_run_workspace_bytes(const fp2_batch* batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, fp2_dtype dtype) {
   BatchInfo info;
-  if (check_batch(batch, &info) != FP2_OK || num_kv_heads < 1 || head_dim < 1) return 0;
-  return run_layout(info, batch->num_seqs, num_kv_heads, head_dim, dtype, batch->block).total;
+  if (check_batch(batch, &info) != FP2_OK || num_kv_heads < 1 || num_q_heads < num_kv_heads || head_dim < 1)
+    return 0;
+  return run_layout(info, batch->num_seqs, num_q_heads, num_kv_heads, head_dim, dtype, batch->block).total;
 }
 
 fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv* kv,
@@ -117,7 +118,8 @@ fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv*
   if (mean_correction && (!kbar || !vbar)) return fail(FP2_ERR_INVALID, "mean correction needs kbar and vbar");
   if (mean_correction || vt_path(q->dtype, q->head_dim, batch->block)) {
     const size_t wneed =
-        run_layout(info, batch->num_seqs, kv->num_kv_heads, kv->head_dim, kv->dtype, batch->block).total;
+        run_layout(info, batch->num_seqs, q->num_q_heads, kv->num_kv_heads, kv->head_dim, kv->dtype, batch->block)
+            .total;
     if (!workspace || workspace_bytes < wneed)
       return fail(FP2_ERR_CAPACITY, "run workspace " + std::to_string(workspace_bytes) + " < " +
                                         std::to_string(wneed) + " bytes");

@@ -47,11 +47,23 @@ struct RunLayout {
   size_t v16 = 0;      // fp16 vbar rows (register-staged path) or vbar^T tiles (V^T path)
   size_t vt = 0;       // V^T tiles of every KV block (V^T path)
   size_t kd = 0;       // e4m3 V^T path: K codes as bf16 rows, [Hkv, total_kblocks, B, d]
-  size_t order = 0;    // V^T path: CSR rows in launch order, int32 [Hkv * total_qblocks]
+  size_t items = 0;    // V^T path: work items in launch order, int4 [rows + extra_cap]
+  size_t splits = 0;   // V^T path: rows split into chunks, int4 [extra_cap]
+  size_t rank_slot = 0;  // V^T path: first partial slot of each split row, int32 [rows]
+  size_t counters = 0;   // V^T path: item and split-row counts, int32 [4]
+  size_t part = 0;       // V^T path: partial results of the chunks of split rows
+  int64_t extra_cap = 0;  // most work items beyond one per row (chunks of split rows)
   size_t total = 0;
   int64_t mt_cap = 0;  // vbar^T tiles per KV head (V^T path)
 };
-RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_kv_heads, int head_dim, int dtype, int block);
+RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int dtype,
+                     int block);
+// Work items beyond one per CSR row that the d = 128, B = 128 path may create
+// by splitting the exact tiles of heavy rows (at most 256; fewer for small
+// batches), and the floats of one partial result (per slot, slice and wave:
+// O as 16 float4 per lane, then the reference max and row sum per lane).
+constexpr int64_t kMaxExtraItems = 256;
+constexpr int64_t kPartFloatsPerWave = 64 * 64 + 2 * 64;
 inline int plan_words(const BatchInfo& info) { return int((info.max_kblocks + 31) / 32); }
 
 }  // namespace fp2

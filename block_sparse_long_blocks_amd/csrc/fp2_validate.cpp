@@ -1,5 +1,6 @@
 // Host-only argument checks for the C ABI.  Plain C++: no HIP call is made
 // here, so every rejection happens before anything is enqueued.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -135,7 +136,8 @@ size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads) {
   return (bytes + 255) & ~size_t(255);
 }
 
-RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_kv_heads, int head_dim, int dtype, int block) {
+RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int dtype,
+                     int block) {
   auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
   RunLayout L;
   const size_t tkb = (size_t)info.total_kblocks, hkv = (size_t)num_kv_heads;
@@ -152,8 +154,19 @@ RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_kv_heads, int 
       L.kd = L.total;
       L.total = L.kd + hkv * tkb * tile;
     }
-    L.order = L.total;
-    L.total = L.order + up(hkv * (size_t)info.total_qblocks * 4);
+    // work items: one per CSR row plus the extra chunks of split rows (at
+    // most one per 4 causal tiles, and kMaxExtraItems); a split row holds at
+    // least two chunks, so the partial slots are at most twice the extras
+    const size_t nrows = hkv * (size_t)info.total_qblocks;
+    const int64_t causal_tiles = info.causal_pairs * (int64_t)num_kv_heads;
+    L.extra_cap = std::min<int64_t>(kMaxExtraItems, (causal_tiles + 3) / 4);
+    const size_t slices = (size_t)((std::max(num_q_heads / std::max(num_kv_heads, 1), 1) * block + 255) / 256);
+    L.items = L.total;
+    L.splits = L.items + up((nrows + (size_t)L.extra_cap) * 16);
+    L.rank_slot = L.splits + up((size_t)L.extra_cap * 16 + 16);
+    L.counters = L.rank_slot + up(nrows * 4);
+    L.part = L.counters + 256;
+    L.total = L.part + up(2 * (size_t)L.extra_cap * slices * 8 * (size_t)kPartFloatsPerWave * 4);
   } else {
     L.total = L.v16 + rows;
   }

@@ -28,6 +28,9 @@
 //    and non-causal blocks, through the same MFMA code path.
 //  * fp8: logits carry q_scale * k_scale, and each block's v_scale is folded
 //    into its probabilities before the PV product.
+#include <algorithm>
+#include <cstdlib>
+
 #include "attn_common.h"
 
 namespace fp2 {
@@ -564,7 +567,7 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   if (info.total_qblocks == 0) return hipSuccess;
   const int D = q->head_dim, BLK = b->block, hkv = kv->num_kv_heads;
   const bool vt = vt_path(q->dtype, D, BLK);
-  const RunLayout L = run_layout(info, b->num_seqs, hkv, D, q->dtype, BLK);
+  const RunLayout L = run_layout(info, b->num_seqs, q->num_q_heads, hkv, D, q->dtype, BLK);
   uint8_t* wsb = static_cast<uint8_t*>(workspace);
   uint16_t* k16 = reinterpret_cast<uint16_t*>(wsb + L.k16);
   uint16_t* v16 = reinterpret_cast<uint16_t*>(wsb + L.v16);
@@ -594,7 +597,16 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.vt = wsb + L.vt;
   a.vbt = wsb + L.v16;
   a.kd = wsb + L.kd;
-  a.order = reinterpret_cast<int32_t*>(wsb + L.order);
+  a.items = reinterpret_cast<int4*>(wsb + L.items);
+  a.splits = reinterpret_cast<int4*>(wsb + L.splits);
+  a.rank_slot = reinterpret_cast<int32_t*>(wsb + L.rank_slot);
+  a.counters = reinterpret_cast<int32_t*>(wsb + L.counters);
+  a.part = reinterpret_cast<float*>(wsb + L.part);
+  a.extra_cap = (int)L.extra_cap;
+  // FP2_MAX_CHUNK_TILES (optional, > 0): upper bound on the exact tiles of one
+  // work item, below the one chosen from the batch (tuning and tests)
+  a.chunk_cap = 0;
+  if (const char* env = std::getenv("FP2_MAX_CHUNK_TILES")) a.chunk_cap = std::max(0, std::atoi(env));
   a.mt_cap = (int)L.mt_cap;
   a.out = out;
   a.out_f32 = out_f32;

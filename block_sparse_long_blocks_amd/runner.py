@@ -29,7 +29,7 @@ class PrefillLayer:
         self.col_idx = torch.empty(max(1, fp2_plan_max_nnz(batch, hkv)), **i32)
         self.nnz = torch.zeros(1, **i32)
         self.plan_ws = torch.empty(max(1, fp2_plan_workspace_bytes(batch, hkv)), dtype=torch.uint8, device=dev)
-        self.run_ws = torch.empty(max(1, fp2_run_workspace_bytes(batch, hkv, d, kv.dtype)), dtype=torch.uint8, device=dev)
+        self.run_ws = torch.empty(max(1, fp2_run_workspace_bytes(batch, q.q.shape[1], hkv, d, kv.dtype)), dtype=torch.uint8, device=dev)
         self.out = torch.empty((max(1, batch.total_q), q.q.shape[1], d), dtype=out_dtype, device=dev)
         self.scores = torch.empty((rows, max(1, batch.max_kblocks)), **f32) if with_scores else None
 

@@ -148,10 +148,13 @@ fp2_status fp2_plan_mask(const fp2_batch *batch, const fp2_q *q, int32_t num_kv_
  * KV head, e4m3 V dequantized: about the size of bf16 V), bf16 kbar rows and
  * vbar^T tiles of the mean tokens, for e4m3 also the K codes of every
  * block widened to bf16 rows (another tile per block and head), and the
- * launch order of the CSR rows (one int32 per row, heaviest first);
- * otherwise bf16 kbar and fp16 vbar copies. */
-size_t fp2_run_workspace_bytes(const fp2_batch *batch, int32_t num_kv_heads, int32_t head_dim,
-                               fp2_dtype dtype);
+ * work items in launch order (one per CSR row plus up to 256 chunks of
+ * rows split for balance, heaviest first) with the float32 partial results
+ * of split rows (about 132 KB per chunk and 256 packed query rows, so it
+ * depends on num_q_heads); otherwise bf16 kbar and fp16 vbar copies.  0 also
+ * when num_q_heads < num_kv_heads. */
+size_t fp2_run_workspace_bytes(const fp2_batch *batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, fp2_dtype dtype);
 
 /* Stage 2 - exact attention over the kept blocks plus the mean correction
  * of every skipped block (Figure 3 exact path, Figure 4 surrogate terms).

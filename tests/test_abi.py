@@ -54,13 +54,19 @@ def test_sizes_and_counts():
     assert lib.fp2_plan_max_nnz(b, 3) == 3 * (36 + 2)
     assert lib.fp2_plan_workspace_bytes(b, 3) > 0
     # d = 128, B = 128: bf16 kbar rows plus a 128 x 128 bf16 V^T tile per KV block and head;
-    # e4m3 also the K codes of every block widened to bf16 rows (another tile each)
+    # e4m3 also the K codes of every block widened to bf16 rows (another tile each); and
+    # the float32 partials of split rows: up to 2 * extra slots (extra = min(256, causal
+    # tiles / 4, rounded up) = 29 here) of 8 waves x 4224 floats per 256 packed query rows
     tiles = 3 * (8 + 2) * 128 * 128 * 2
-    assert lib.fp2_run_workspace_bytes(b, 3, 128, lib.FP2_BF16) >= tiles + 3 * (8 + 2) * 128 * 2
-    assert lib.fp2_run_workspace_bytes(b, 3, 128, lib.FP2_FP8_E4M3) >= 2 * tiles + 3 * (8 + 2) * 128 * 2
+    parts = 2 * 29 * 2 * 8 * 4224 * 4  # 12 q heads / 3 kv heads: 512 packed rows = 2 slices
+    assert lib.fp2_run_workspace_bytes(b, 12, 3, 128, lib.FP2_BF16) >= tiles + 3 * (8 + 2) * 128 * 2 + parts
+    assert lib.fp2_run_workspace_bytes(b, 12, 3, 128, lib.FP2_FP8_E4M3) >= 2 * tiles + 3 * (8 + 2) * 128 * 2 + parts
+    assert lib.fp2_run_workspace_bytes(b, 24, 3, 128, lib.FP2_BF16) >= \
+        lib.fp2_run_workspace_bytes(b, 12, 3, 128, lib.FP2_BF16) + parts
+    assert lib.fp2_run_workspace_bytes(b, 2, 3, 128, lib.FP2_BF16) == 0
     # other head sizes: bf16 kbar + fp16 vbar copies only
-    assert lib.fp2_run_workspace_bytes(b, 3, 64, lib.FP2_BF16) < tiles
-    assert lib.fp2_run_workspace_bytes(b, 3, 64, lib.FP2_FP8_E4M3) >= 2 * 3 * (8 + 2) * 64 * 2
+    assert lib.fp2_run_workspace_bytes(b, 12, 3, 64, lib.FP2_BF16) < tiles
+    assert lib.fp2_run_workspace_bytes(b, 12, 3, 64, lib.FP2_FP8_E4M3) >= 2 * 3 * (8 + 2) * 64 * 2
 
 
 def test_validation_rejects_before_launch():

@@ -151,6 +151,30 @@ def test_attention_parity(name, corr, out_dtype):
         check_out(got, ref, TOL[w.cfg.dtype], out_dtype)
 
 
+@pytest.mark.parametrize("corr", [True, False])
+@pytest.mark.parametrize("name", ["varlen_p64", "fp8_varlen"])
+def test_split_rows_match_oracle(name, corr, monkeypatch):
+    """Rows whose exact tiles are cut into chunks (FP2_MAX_CHUNK_TILES caps the
+    chunk; the batch bounds it below by its tiles over its extra-item budget,
+    4 tiles here) run as separate work items whose float32 partials (O, the
+    reference max, the row sum) a combine kernel merges: the result stays
+    within the bar of the oracle, and differs in its last bits from the
+    unsplit run (so the split path really ran)."""
+    for tau in (math.inf, 0.5):
+        monkeypatch.delenv("FP2_MAX_CHUNK_TILES", raising=False)
+        whole, ref, w, L = _attention_case(name, tau, corr, out_dtype="f32")
+        rp, _ = L.csr_host()
+        extra_cap = min(256, -(-w.causal_pairs() // 4))
+        chunk = max(2, -(-int(rp[-1]) // extra_cap))
+        assert int(np.max(np.diff(rp))) > chunk  # some row is split
+        monkeypatch.setenv("FP2_MAX_CHUNK_TILES", "2")
+        split, ref2, _, _ = _attention_case(name, tau, corr, out_dtype="f32")
+        assert np.array_equal(ref, ref2)
+        check_out(split, ref, TOL[w.cfg.dtype], "f32")
+        check_out(whole, ref, TOL[w.cfg.dtype], "f32")
+        assert not np.array_equal(split, whole)
+
+
 @pytest.mark.parametrize("name", ["tiny", "varlen_p64", "d128_b64_g8"])
 def test_dense_mode_is_causal_attention(name):
     got, _, w, _ = _attention_case(name, math.inf, True, out_dtype="f32")
