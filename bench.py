@@ -38,6 +38,11 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the tau=+inf comparison run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=96, help="(q-block, KV head) rows timed on the CPU")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the 128K line: latency against kept-block density at 64K (bf16 and e4m3), "
+                         "with and without mean correction, beside the ideal density x dense line")
+    ap.add_argument("--sweep-densities", default="0.01,0.02,0.05,0.1,0.2,0.5")
+    ap.add_argument("--sweep-out", default="", help="also write the sweep as a markdown table to this path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -194,6 +199,161 @@ def cpu_baseline(w, tau, rows_wanted):
                 blas_threads=os.environ.get("OMP_NUM_THREADS", "default"))
 
 
+def sweep_config(dtype):
+    """A 64K single-sequence layer of the 128K workload's shape and structure
+    (32 query / 8 KV heads, d = 128, block 128, band + 16 sink columns)."""
+    import synth
+    return synth.Config(name=f"sweep64k_{dtype}", seqlens=(65536,), prefixes=(0,), hq=32, hkv=8, d=128, block=128,
+                        page_size=128, dtype=dtype, structure="band_sinks", tau=0.0, seed=6,
+                        description="L=65536, 32q/8kv, d=128, B=128, band + 16 sinks (density sweep)")
+
+
+def calibrate_tau(L, causal_pairs, target, torch):
+    """Smallest tau (bisection, 40 steps) whose plan keeps at least `target` of the
+    causal block pairs; the density grows with tau."""
+    lo, hi = 0.0, 64.0
+    for _ in range(40):
+        mid = 0.5 * (lo + hi)
+        L.plan(mid)
+        torch.cuda.synchronize()
+        if int(L.nnz.item()) >= target * causal_pairs:
+            hi = mid
+        else:
+            lo = mid
+    return hi
+
+
+def time_layer(L, tau, corr, steps, warmup, torch):
+    """ms per layer (stats + plan + run) and ms of fp2_prefill_run, HIP events on the stream."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        L(tau, corr)
+    torch.cuda.synchronize()
+    e = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        e[k][0].record(stream)
+        L.stats()
+        L.plan(tau)
+        e[k][1].record(stream)
+        L.attend(corr)
+        e[k][2].record(stream)
+    torch.cuda.synchronize()
+    layer = sum(x[0].elapsed_time(x[2]) for x in e) / steps
+    run = sum(x[1].elapsed_time(x[2]) for x in e) / steps
+    return layer, run
+
+
+def chunked_prefill_case(args, torch, lib, synth):
+    """One 128-token query chunk after a 130944-token cached prefix (1 query
+    block, so 8 CSR rows of up to 1024 blocks): fp2_prefill_run with the heavy
+    rows split into chunks (the default) and with FP2_MAX_CHUNK_TILES=-1."""
+    rows = []
+    for dtype in ("bf16", "fp8"):
+        log(f"chunked prefill case: generating the {dtype} layer ...")
+        cfg = synth.Config(name=f"chunk128_after_128k_{dtype}", seqlens=(131072,), prefixes=(131072 - 128,),
+                           hq=32, hkv=8, d=128, block=128, page_size=128, dtype=dtype, structure="band_sinks",
+                           tau=0.0, seed=7)
+        w = synth.make_custom(cfg)
+        L = lib.PrefillLayer(*lib.from_workload(w))
+        for tau in (math.inf, 3.0):
+            L.stats()
+            L.plan(tau)
+            torch.cuda.synchronize()
+            res = {}
+            for key, env in (("ms_split", None), ("ms_nosplit", "-1")):
+                if env is None:
+                    os.environ.pop("FP2_MAX_CHUNK_TILES", None)
+                else:
+                    os.environ["FP2_MAX_CHUNK_TILES"] = env
+                for _ in range(args.warmup):
+                    L.attend(True)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(args.steps):
+                    L.attend(True)
+                e1.record()
+                torch.cuda.synchronize()
+                res[key] = round(e0.elapsed_time(e1) / args.steps, 4)
+            os.environ.pop("FP2_MAX_CHUNK_TILES", None)
+            rows.append(dict(dtype=dtype, tau=tau if math.isfinite(tau) else "inf", nnz=int(L.nnz.item()), **res,
+                             ratio=round(res["ms_nosplit"] / res["ms_split"], 2)))
+            log("chunked prefill:", json.dumps(rows[-1]))
+        del L, w
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return rows
+
+
+def density_sweep(args, torch, lib, synth):
+    """Latency against kept-block density at 64K, with and without the mean
+    correction, beside the ideal line (density x the same kernel's dense time)."""
+    dens = [float(x) for x in args.sweep_densities.split(",") if x]
+    table = []
+    for dtype in ("bf16", "fp8"):
+        log(f"sweep: generating the 64K {dtype} layer ...")
+        w = synth.make_custom(sweep_config(dtype))
+        batch, q, kv = lib.from_workload(w)
+        L = lib.PrefillLayer(batch, q, kv)
+        causal = w.causal_pairs()
+        dense_layer, dense_run = time_layer(L, math.inf, False, args.dense_steps, 1, torch)
+        L.plan(math.inf)
+        torch.cuda.synchronize()
+        fl_dense = flop_counts(w, int(L.nnz.item()))
+        for rho in dens:
+            tau = calibrate_tau(L, causal, rho, torch)
+            L.plan(tau)
+            torch.cuda.synchronize()
+            nnz = int(L.nnz.item())
+            fl = flop_counts(w, nnz)
+            row_len = (L.row_ptr[1:] - L.row_ptr[:-1]).cpu()
+            row = dict(dtype=dtype, target=rho, tau=round(tau, 6), density=round(nnz / causal, 5), nnz=nnz,
+                       max_row_blocks=int(row_len.max()), mean_row_blocks=round(float(row_len.float().mean()), 2))
+            for corr in (True, False):
+                layer, run = time_layer(L, tau, corr, args.steps, args.warmup, torch)
+                k = "corr" if corr else "nocorr"
+                row[f"ms_layer_{k}"] = round(layer, 4)
+                row[f"ms_run_{k}"] = round(run, 4)
+            row["ideal_run_ms"] = round(nnz / causal * dense_run, 4)
+            row["run_over_ideal"] = round(row["ms_run_nocorr"] / row["ideal_run_ms"], 3)
+            row["corr_overhead"] = round(row["ms_run_corr"] / row["ms_run_nocorr"] - 1.0, 4)
+            row["speedup_vs_dense_layer"] = round(dense_layer / row["ms_layer_corr"], 2)
+            row["corr_flops_share"] = round(fl["corr"] / (fl["kept"] + fl["corr"]), 4)
+            log("sweep:", json.dumps(row))
+            table.append(row)
+        table.append(dict(dtype=dtype, target=1.0, density=1.0, nnz=fl_dense["causal_pairs"],
+                          ms_layer_nocorr=round(dense_layer, 4), ms_run_nocorr=round(dense_run, 4),
+                          ideal_run_ms=round(dense_run, 4), run_over_ideal=1.0))
+        del L, batch, q, kv, w
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    chunk = chunked_prefill_case(args, torch, lib, synth)
+    out = {"metric": "density sweep at 64K: ms per layer and per fp2_prefill_run against kept-block density",
+           "workload": "1 seq L=65536, 32 q / 8 kv heads, d=128, block 128, band + 16 sink columns, "
+                       "tau calibrated on the GPU plan to each target density",
+           "steps": args.steps, "warmup": args.warmup, "n_gpus": 1, "points": table, "chunked_prefill": chunk}
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            f.write("| dtype | density | tau | kept blocks per row (mean / max) | run ms (corr) | run ms (no corr) "
+                    "| ideal ms | no corr / ideal | corr overhead | corr share of FLOPs | layer ms (corr) "
+                    "| layer speedup vs dense |\n")
+            f.write("|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+            for r in table:
+                f.write(f"| {r['dtype']} | {r['density']} | {r.get('tau', 'inf')} "
+                        f"| {r.get('mean_row_blocks', '-')} / {r.get('max_row_blocks', '-')} | {r.get('ms_run_corr', '-')} "
+                        f"| {r['ms_run_nocorr']} | {r['ideal_run_ms']} | {r['run_over_ideal']} "
+                        f"| {r.get('corr_overhead', '-')} | {r.get('corr_flops_share', '-')} "
+                        f"| {r.get('ms_layer_corr', r['ms_layer_nocorr'])} | {r.get('speedup_vs_dense_layer', 1.0)} |\n")
+            f.write("\nChunked prefill: one 128-token query chunk after a 130944-token cached prefix "
+                    "(8 CSR rows), fp2_prefill_run ms with mean correction, rows split into chunks or not:\n\n")
+            f.write("| dtype | tau | kept blocks | split rows (default) ms | no splitting ms | ratio |\n")
+            f.write("|---|---|---|---|---|---|\n")
+            for r in chunk:
+                f.write(f"| {r['dtype']} | {r['tau']} | {r['nnz']} | {r['ms_split']} | {r['ms_nosplit']} "
+                        f"| {r['ratio']} |\n")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -203,6 +363,9 @@ def main():
     import torch
     import block_sparse_long_blocks_amd as lib
     import synth
+    if args.sweep:
+        density_sweep(args, torch, lib, synth)
+        return
     taus = load_taus()
     w, bf = run_workload("c128k_bf16", taus["c128k_bf16"]["tau"], args, torch, lib, synth)
     fl = bf["flops"]

@@ -603,10 +603,14 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.counters = reinterpret_cast<int32_t*>(wsb + L.counters);
   a.part = reinterpret_cast<float*>(wsb + L.part);
   a.extra_cap = (int)L.extra_cap;
-  // FP2_MAX_CHUNK_TILES (optional, > 0): upper bound on the exact tiles of one
-  // work item, below the one chosen from the batch (tuning and tests)
+  // FP2_MAX_CHUNK_TILES (optional): > 0 caps the exact tiles of one work item
+  // below the batch's own choice, < 0 turns the splitting of rows off
   a.chunk_cap = 0;
-  if (const char* env = std::getenv("FP2_MAX_CHUNK_TILES")) a.chunk_cap = std::max(0, std::atoi(env));
+  if (const char* env = std::getenv("FP2_MAX_CHUNK_TILES")) {
+    const int v = std::atoi(env);
+    if (v < 0) a.extra_cap = 0;
+    a.chunk_cap = std::max(0, v);
+  }
   a.mt_cap = (int)L.mt_cap;
   a.out = out;
   a.out_f32 = out_f32;

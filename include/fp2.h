@@ -169,7 +169,13 @@ size_t fp2_run_workspace_bytes(const fp2_batch *batch, int32_t num_q_heads, int3
  *   workspace         device scratch of fp2_run_workspace_bytes() bytes;
  *                     required with d = 128 and B = 128 (bf16 or e4m3),
  *                     else only with mean_correction (FP2_ERR_CAPACITY if
- *                     too small); its contents are overwritten */
+ *                     too small); its contents are overwritten
+ * With d = 128 and B = 128 the rows run as work items launched heaviest
+ * first; the exact tiles of a row heavier than a quarter of a CU's share
+ * of the batch are cut into chunks whose float32 partials a second kernel
+ * merges (at most 256 extra items).  The environment variable
+ * FP2_MAX_CHUNK_TILES, read at each call, caps the tiles of a chunk
+ * (> 0) or turns the splitting off (< 0). */
 fp2_status fp2_prefill_run(const fp2_batch *batch, const fp2_q *q, const fp2_kv *kv,
                            const int32_t *row_ptr, const int32_t *col_idx,
                            const float *kbar, const float *vbar,
