@@ -42,6 +42,10 @@ def parse():
                     help="instead of the 128K line: latency against kept-block density at 64K (bf16 and e4m3), "
                          "with and without mean correction, beside the ideal density x dense line")
     ap.add_argument("--sweep-densities", default="0.01,0.02,0.05,0.1,0.2,0.5")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the 128K line: time the other named workloads (llama32k, qwen_paged, "
+                         "extreme_fp8 with and without correction) against their own dense runs")
+    ap.add_argument("--configs-out", default="", help="also write the --configs table as markdown to this path")
     ap.add_argument("--sweep-out", default="", help="also write the sweep as a markdown table to this path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
@@ -103,7 +107,7 @@ def measured_traffic(workload, launch_flops):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_workload(name, tau, args, torch, lib, synth):
+def run_workload(name, tau, args, torch, lib, synth, corr=True):
     log(f"generating {name} (tau={tau:.6g}) ...")
     t0 = time.time()
     w = synth.make(name, tau=tau)
@@ -112,7 +116,7 @@ def run_workload(name, tau, args, torch, lib, synth):
     L = lib.PrefillLayer(batch, q, kv)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        L(tau, True)
+        L(tau, corr)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -124,7 +128,7 @@ def run_workload(name, tau, args, torch, lib, synth):
         e[1].record(stream)
         L.plan(tau)
         e[2].record(stream)
-        L.attend(True)
+        L.attend(corr)
         e[3].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
@@ -132,7 +136,7 @@ def run_workload(name, tau, args, torch, lib, synth):
     step_ms = sum(ev[k][0].elapsed_time(ev[k][3]) for k in range(args.steps)) / args.steps
     nnz = int(L.nnz.item())
     fl = flop_counts(w, nnz)
-    res = dict(name=name, tau=tau, ms_per_layer=step_ms, wall_ms_per_layer=wall_ms,
+    res = dict(name=name, tau=tau, corr=corr, ms_per_layer=step_ms, wall_ms_per_layer=wall_ms,
                stages_ms={"block_stats": st[0], "plan_mask": st[1], "prefill_run": st[2]},
                nnz=nnz, density=nnz / fl["causal_pairs"], flops=fl)
     # dense comparison: the same three calls at tau = +inf
@@ -148,7 +152,7 @@ def run_workload(name, tau, args, torch, lib, synth):
         torch.cuda.synchronize()
         res["dense_ms_per_layer"] = e0.elapsed_time(e1) / args.dense_steps
         res["speedup_vs_dense"] = res["dense_ms_per_layer"] / step_ms
-        L(tau, True)  # leave the sparse plan in place
+        L(tau, corr)  # leave the sparse plan in place
         torch.cuda.synchronize()
     # HBM-side figures of the two stage-1 kernels (algorithmic bytes)
     kv_bytes = 2 * w.k_pages.nbytes
@@ -354,6 +358,48 @@ def density_sweep(args, torch, lib, synth):
     print(json.dumps(out), flush=True)
 
 
+def config_runs(args, torch, lib, synth):
+    """The named workloads besides the 128K one, each against its own dense
+    (tau = +inf) run of the same three calls."""
+    taus = load_taus()
+    rows = []
+    for name, corr in (("llama32k", True), ("qwen_paged", True), ("extreme_fp8", True), ("extreme_fp8", False)):
+        w, r = run_workload(name, taus[name]["tau"], args, torch, lib, synth, corr=corr)
+        fl = r["flops"]
+        dt = w.cfg.dtype
+        t_run = r["stages_ms"]["prefill_run"] * 1e-3
+        attn = fl["kept"] + (fl["corr"] if corr else 0)
+        if dt == "fp8":  # QK^T on e4m3 MFMA, PV and the correction on bf16 MFMA
+            busy = fl["kept"] / 2 / (PEAK_TFLOPS["fp8"] * 1e12) + \
+                (fl["kept"] / 2 + (fl["corr"] if corr else 0)) / (PEAK_TFLOPS["bf16"] * 1e12)
+        else:
+            busy = attn / (PEAK_TFLOPS["bf16"] * 1e12)
+        row = dict(workload=name, dtype=dt, correction=corr, tau=round(r["tau"], 6), density=round(r["density"], 5),
+                   ms_per_layer=round(r["ms_per_layer"], 4),
+                   stages_ms={k: round(v, 4) for k, v in r["stages_ms"].items()},
+                   dense_equiv_tflops=round(fl["dense"] / (r["ms_per_layer"] * 1e-3) / 1e12, 2),
+                   mfma_frac_run=round(busy / t_run, 4),
+                   dense_ms_per_layer=round(r.get("dense_ms_per_layer", float("nan")), 3),
+                   speedup_vs_dense=round(r.get("speedup_vs_dense", float("nan")), 2))
+        log("configs:", json.dumps(row))
+        rows.append(row)
+        del w
+    out = {"metric": "ms per layer of the named workloads against their own dense runs", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "runs": rows}
+    if args.configs_out:
+        with open(args.configs_out, "w") as f:
+            f.write("| workload | dtype | correction | tau | density | ms/layer | block_stats | plan_mask "
+                    "| prefill_run | dense-equiv TFLOP/s | MFMA fraction of prefill_run | dense ms/layer "
+                    "| speedup vs dense |\n|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+            for r in rows:
+                st = r["stages_ms"]
+                f.write(f"| {r['workload']} | {r['dtype']} | {'on' if r['correction'] else 'off'} | {r['tau']} "
+                        f"| {r['density']} | {r['ms_per_layer']} | {st['block_stats']} | {st['plan_mask']} "
+                        f"| {st['prefill_run']} | {r['dense_equiv_tflops']} | {r['mfma_frac_run']} "
+                        f"| {r['dense_ms_per_layer']} | {r['speedup_vs_dense']} |\n")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -365,6 +411,9 @@ def main():
     import synth
     if args.sweep:
         density_sweep(args, torch, lib, synth)
+        return
+    if args.configs:
+        config_runs(args, torch, lib, synth)
         return
     taus = load_taus()
     w, bf = run_workload("c128k_bf16", taus["c128k_bf16"]["tau"], args, torch, lib, synth)
