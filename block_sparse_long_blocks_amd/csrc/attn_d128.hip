@@ -60,6 +60,11 @@ constexpr int kBufferFlags = 0x00020000;
 constexpr int kRowBytes = kD * 2;            // a K row (d values) or a V^T row (128 keys), bf16
 constexpr int kGS = 4 * kRowBytes + 64;      // LDS stride of a 4-row group
 constexpr int kTileLds = (kBlk / 4) * kGS;   // one K or V^T tile in LDS
+// bf16 output staging in the epilogue: 32 rows of 256 bytes per wave, rows
+// 272 bytes apart, four waves per tile buffer
+constexpr int kStageRow = kRowBytes + 16;
+constexpr int kStageBytes = 32 * kStageRow;
+static_assert(4 * kStageBytes <= kTileLds, "epilogue staging must fit one tile buffer");
 constexpr int kTileGlobal = kBlk * kRowBytes;  // one V^T tile in global memory
 // tile DMA: waves 0 .. kDmaWaves-1 each move kDmaRows rows of the K and the
 // V^T tile (kDmaInstr instructions, K and V^T alternating)
@@ -1011,6 +1016,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
               f32x4{ws.o[dt][4 * q4 + 0], ws.o[dt][4 * q4 + 1], ws.o[dt][4 * q4 + 2], ws.o[dt][4 * q4 + 3]};
       const float lsum = sum_halves(ws.l);
       *reinterpret_cast<float2*>(po + 64 * 64 + 2 * lane) = make_float2(ws.m, lsum);
+    }
+  } else if (!a.out_f32) {
+    // bf16: the wave's 32 x 128 output tile goes through LDS (the tile
+    // buffers are free after the last barrier; 272-byte rows), so that each
+    // store writes whole 256-byte rows, 16 lanes a row: a lane's own values
+    // are 4-element pieces of one row, and storing them directly takes 16
+    // instructions of 32 scattered pieces each, whose draining held the
+    // workgroup's slot for several microseconds.
+    if (wave_active) {
+      const float inv = 1.0f / sum_halves(ws.l);  // rows past the sequence end are never stored
+      uint8_t* stg = (wave < 4 ? K0 : V0) + (wave & 3) * kStageBytes;
+      const int r = lane & 31;
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          uint2 w;
+          w.x = pack_bf16x2(ws.o[dt][4 * q4 + 0] * inv, ws.o[dt][4 * q4 + 1] * inv);
+          w.y = pack_bf16x2(ws.o[dt][4 * q4 + 2] * inv, ws.o[dt][4 * q4 + 3] * inv);
+          *reinterpret_cast<uint2*>(stg + r * kStageRow + (32 * dt + 8 * q4 + 4 * hf) * 2) = w;
+        }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rr = 4 * i + (lane >> 4);
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + rr * kStageRow + (lane & 15) * 16);
+        const int tqr = prow % kBlk + rr;
+        if (I * kBlk + tqr < n)
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + ((int64_t)(q0 + I * kBlk + tqr) * a.hq + h) * kD +
+                                    (lane & 15) * 8) = v;
+      }
     }
   } else if (q_valid) {
     const float inv = 1.0f / sum_halves(ws.l);
