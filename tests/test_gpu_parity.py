@@ -58,10 +58,16 @@ SMALL = {
     # head per KV head (half of each workgroup idle) and eight (four slices per query block)
     "d128_p24_g1": _cfg("d128_p24_g1", (900, 260), (128, 0), 2, 2, 128, 128, 24),
     "d128_p8_g8": _cfg("d128_p8_g8", (700,), (384,), 16, 2, 128, 128, 8),
+    # chunked prefill: one query block after a 6016-token cached prefix (4 CSR rows of up to 48
+    # blocks, so the default work-item builder splits them), bf16 and e4m3
+    "chunk_after_prefix": _cfg("chunk_after_prefix", (6144,), (6016,), 8, 4, 128, 128, 128),
+    "chunk_after_prefix_fp8": _cfg("chunk_after_prefix_fp8", (6144,), (6016,), 8, 4, 128, 128, 128,
+                                   dtype="fp8"),
 }
 TAUS = {"tiny": (0.0, 0.005, 0.01, 0.02, 2.0), "varlen_p64": (0.0, 0.5, 3.0),
         "d64_b128_p16": (0.3, 3.0), "d128_b64_g8": (0.2, 2.0), "single_token": (0.0, 1.0),
-        "fp8_varlen": (0.0, 0.5, 3.0), "d128_p24_g1": (0.0, 1.0), "d128_p8_g8": (0.0, 1.0)}
+        "fp8_varlen": (0.0, 0.5, 3.0), "d128_p24_g1": (0.0, 1.0), "d128_p8_g8": (0.0, 1.0),
+        "chunk_after_prefix": (0.5, 1e9), "chunk_after_prefix_fp8": (0.5, 1e9)}
 
 _cache = {}
 
