@@ -107,7 +107,7 @@ def measured_traffic(workload, launch_flops):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_workload(name, tau, args, torch, lib, synth, corr=True):
+def run_workload(name, tau, args, torch, lib, synth, corr=True, stats_cache=False):
     log(f"generating {name} (tau={tau:.6g}) ...")
     t0 = time.time()
     w = synth.make(name, tau=tau)
@@ -154,6 +154,8 @@ def run_workload(name, tau, args, torch, lib, synth, corr=True):
         res["speedup_vs_dense"] = res["dense_ms_per_layer"] / step_ms
         L(tau, corr)  # leave the sparse plan in place
         torch.cuda.synchronize()
+    if stats_cache:
+        res.update(stats_cache_timing(L, args, torch, lib))
     # HBM-side figures of the two stage-1 kernels (algorithmic bytes)
     kv_bytes = 2 * w.k_pages.nbytes
     kbar_bytes = 2 * w.cfg.hkv * w.total_kblocks * w.cfg.d * 4
@@ -247,6 +249,33 @@ def time_layer(L, tau, corr, steps, warmup, torch):
     return layer, run
 
 
+def stats_cache_timing(L, args, torch, lib):
+    """ms of fp2_block_stats (every block) against fp2_block_stats_cached without
+    refreshing the cached prefix plus fp2_gather_block_stats (the rows of
+    prefix blocks computed once beforehand)."""
+    rows = lib.fp2_block_stats_cache_rows(L.batch, L.kv)
+    kc = torch.empty((rows, L.kbar.shape[0], L.kbar.shape[2]), dtype=torch.float32, device=L.kbar.device)
+    vc = torch.empty_like(kc)
+    lib.fp2_block_stats_cached(L.batch, L.kv, kc, vc, True)
+    res = {}
+    for key, fn in (("stats_full_ms", lambda: L.stats()),
+                    ("stats_cached_ms", lambda: (lib.fp2_block_stats_cached(L.batch, L.kv, kc, vc, False),
+                                                 lib.fp2_gather_block_stats(L.batch, L.kv, kc, vc, L.kbar,
+                                                                            L.vbar)))):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[key] = round(e0.elapsed_time(e1) / args.steps, 4)
+    del kc, vc
+    return res
+
+
 def chunked_prefill_case(args, torch, lib, synth):
     """One 128-token query chunk after a 130944-token cached prefix (1 query
     block, so 8 CSR rows of up to 1024 blocks): fp2_prefill_run with the heavy
@@ -281,7 +310,7 @@ def chunked_prefill_case(args, torch, lib, synth):
                 res[key] = round(e0.elapsed_time(e1) / args.steps, 4)
             os.environ.pop("FP2_MAX_CHUNK_TILES", None)
             rows.append(dict(dtype=dtype, tau=tau if math.isfinite(tau) else "inf", nnz=int(L.nnz.item()), **res,
-                             ratio=round(res["ms_nosplit"] / res["ms_split"], 2)))
+                             ratio=round(res["ms_nosplit"] / res["ms_split"], 2), **stats_cache_timing(L, args, torch, lib)))
             log("chunked prefill:", json.dumps(rows[-1]))
         del L, w
         torch.cuda.synchronize()
@@ -350,11 +379,12 @@ def density_sweep(args, torch, lib, synth):
                         f"| {r.get('ms_layer_corr', r['ms_layer_nocorr'])} | {r.get('speedup_vs_dense_layer', 1.0)} |\n")
             f.write("\nChunked prefill: one 128-token query chunk after a 130944-token cached prefix "
                     "(8 CSR rows), fp2_prefill_run ms with mean correction, rows split into chunks or not:\n\n")
-            f.write("| dtype | tau | kept blocks | split rows (default) ms | no splitting ms | ratio |\n")
-            f.write("|---|---|---|---|---|---|\n")
+            f.write("| dtype | tau | kept blocks | split rows (default) ms | no splitting ms | ratio "
+                    "| fp2_block_stats ms | cached stats + gather ms |\n")
+            f.write("|---|---|---|---|---|---|---|---|\n")
             for r in chunk:
                 f.write(f"| {r['dtype']} | {r['tau']} | {r['nnz']} | {r['ms_split']} | {r['ms_nosplit']} "
-                        f"| {r['ratio']} |\n")
+                        f"| {r['ratio']} | {r['stats_full_ms']} | {r['stats_cached_ms']} |\n")
     print(json.dumps(out), flush=True)
 
 
@@ -364,7 +394,8 @@ def config_runs(args, torch, lib, synth):
     taus = load_taus()
     rows = []
     for name, corr in (("llama32k", True), ("qwen_paged", True), ("extreme_fp8", True), ("extreme_fp8", False)):
-        w, r = run_workload(name, taus[name]["tau"], args, torch, lib, synth, corr=corr)
+        w, r = run_workload(name, taus[name]["tau"], args, torch, lib, synth, corr=corr,
+                            stats_cache=name == "qwen_paged")
         fl = r["flops"]
         dt = w.cfg.dtype
         t_run = r["stages_ms"]["prefill_run"] * 1e-3
@@ -381,6 +412,9 @@ def config_runs(args, torch, lib, synth):
                    mfma_frac_run=round(busy / t_run, 4),
                    dense_ms_per_layer=round(r.get("dense_ms_per_layer", float("nan")), 3),
                    speedup_vs_dense=round(r.get("speedup_vs_dense", float("nan")), 2))
+        for k in ("stats_full_ms", "stats_cached_ms"):
+            if k in r:
+                row[k] = r[k]
         log("configs:", json.dumps(row))
         rows.append(row)
         del w
@@ -397,6 +431,11 @@ def config_runs(args, torch, lib, synth):
                         f"| {r['density']} | {r['ms_per_layer']} | {st['block_stats']} | {st['plan_mask']} "
                         f"| {st['prefill_run']} | {r['dense_equiv_tflops']} | {r['mfma_frac_run']} "
                         f"| {r['dense_ms_per_layer']} | {r['speedup_vs_dense']} |\n")
+            for r in rows:
+                if "stats_cached_ms" in r:
+                    f.write(f"\n{r['workload']}: fp2_block_stats {r['stats_full_ms']} ms; with the block means of "
+                            f"the cached prefixes kept beside the KV pages, fp2_block_stats_cached (new blocks only) "
+                            f"+ fp2_gather_block_stats {r['stats_cached_ms']} ms.\n")
     print(json.dumps(out), flush=True)
 
 

@@ -29,7 +29,8 @@ FP2_OUT_BF16, FP2_OUT_F32 = 0, 1
 STATUS_NAMES = {0: "FP2_OK", 1: "FP2_ERR_INVALID", 2: "FP2_ERR_UNSUPPORTED", 3: "FP2_ERR_CAPACITY",
                 4: "FP2_ERR_HIP"}
 
-SYMBOLS = ("fp2_block_stats", "fp2_plan_workspace_bytes", "fp2_plan_max_nnz", "fp2_plan_mask",
+SYMBOLS = ("fp2_block_stats", "fp2_block_stats_cache_rows", "fp2_block_stats_cached", "fp2_gather_block_stats",
+           "fp2_plan_workspace_bytes", "fp2_plan_max_nnz", "fp2_plan_mask",
            "fp2_run_workspace_bytes", "fp2_prefill_run", "fp2_last_error")
 
 _p = ctypes.c_void_p
@@ -56,6 +57,12 @@ class CKV(ctypes.Structure):
 
 _lib.fp2_block_stats.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CKV), _p, _p, _p]
 _lib.fp2_block_stats.restype = ctypes.c_int
+_lib.fp2_block_stats_cache_rows.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CKV)]
+_lib.fp2_block_stats_cache_rows.restype = ctypes.c_int64
+_lib.fp2_block_stats_cached.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CKV), _p, _p, ctypes.c_int32, _p]
+_lib.fp2_block_stats_cached.restype = ctypes.c_int
+_lib.fp2_gather_block_stats.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CKV), _p, _p, _p, _p, _p]
+_lib.fp2_gather_block_stats.restype = ctypes.c_int
 _lib.fp2_plan_workspace_bytes.argtypes = [ctypes.POINTER(CBatch), ctypes.c_int32]
 _lib.fp2_plan_workspace_bytes.restype = ctypes.c_size_t
 _lib.fp2_plan_max_nnz.argtypes = [ctypes.POINTER(CBatch), ctypes.c_int32]
@@ -188,6 +195,25 @@ def fp2_block_stats(batch: Batch, kv: KVCache, kbar: torch.Tensor, vbar: torch.T
     b, k = batch.c, kv.c
     _check(_lib.fp2_block_stats(ctypes.byref(b), ctypes.byref(k), _ptr(kbar), _ptr(vbar),
                                 _stream(stream)))
+
+
+def fp2_block_stats_cache_rows(batch: Batch, kv: KVCache) -> int:
+    b, k = batch.c, kv.c
+    return int(_lib.fp2_block_stats_cache_rows(ctypes.byref(b), ctypes.byref(k)))
+
+
+def fp2_block_stats_cached(batch: Batch, kv: KVCache, kbar_cache: torch.Tensor, vbar_cache: torch.Tensor,
+                           refresh_prefix: bool, stream=None):
+    b, k = batch.c, kv.c
+    _check(_lib.fp2_block_stats_cached(ctypes.byref(b), ctypes.byref(k), _ptr(kbar_cache), _ptr(vbar_cache),
+                                       int(bool(refresh_prefix)), _stream(stream)))
+
+
+def fp2_gather_block_stats(batch: Batch, kv: KVCache, kbar_cache: torch.Tensor, vbar_cache: torch.Tensor,
+                           kbar: torch.Tensor, vbar: torch.Tensor, stream=None):
+    b, k = batch.c, kv.c
+    _check(_lib.fp2_gather_block_stats(ctypes.byref(b), ctypes.byref(k), _ptr(kbar_cache), _ptr(vbar_cache),
+                                       _ptr(kbar), _ptr(vbar), _stream(stream)))
 
 
 def fp2_plan_workspace_bytes(batch: Batch, num_kv_heads: int) -> int:

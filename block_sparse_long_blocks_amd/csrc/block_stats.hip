@@ -8,6 +8,12 @@
 // with 16-byte loads (CH chunks per row, R token lanes side by side), sums in
 // float32 per thread, then reduces the R token lanes through LDS in a fixed
 // order.  HBM-bound: every K/V byte is read exactly once.
+//
+// The same kernel also writes a cache kept alongside the KV pages (chunked
+// prefill: the blocks of a cached prefix keep their means from the call that
+// computed them, so only the blocks holding new tokens are read again); a
+// gather then lays the cache rows out as the dense [Hkv, total_kblocks, d]
+// arrays the plan and the attention take, bit for bit the same values.
 #include "fp2_device.h"
 #include "fp2_internal.h"
 
@@ -57,9 +63,19 @@ struct StatsArgs {
   const float* v_scale;
   float* kbar;
   float* vbar;
+  const int32_t* cu_seqlens_q;
   PageMap pm;
   int num_seqs, max_pages, page_size, hkv, d, block, total_kblocks;
+  int cached;   // 1: kbar / vbar are the paged caches [cache rows, Hkv, d]
+  int refresh;  // cached: 1 also recomputes the blocks of the cached prefix
+  int bpp;      // cached: KV blocks per page, max(1, page_size / block)
 };
+
+// Cache row of block J of a sequence with page table pt: the block's first
+// page, times the blocks a page holds, plus the block's place in its page.
+__device__ __forceinline__ int64_t cache_row(const StatsArgs& a, const int32_t* pt, int J) {
+  return (int64_t)pt[(int64_t)J * a.block / a.page_size] * a.bpp + J % a.bpp;
+}
 
 template <int ESZ>
 __global__ __launch_bounds__(kThreads) void block_stats_kernel(StatsArgs a) {
@@ -72,6 +88,10 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(StatsArgs a) {
   const int s = find_seq(a.cu_kblocks, a.num_seqs, kb);
   const int J = kb - a.cu_kblocks[s];
   const int T = a.seqlens_k[s];
+  if (a.cached && !a.refresh) {
+    const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
+    if (J < (T - n) / a.block) return;  // a block of the cached prefix: its cache row stands
+  }
   const int count = min(a.block, T - J * a.block);
   const int row_bytes = a.hkv * a.d * ESZ;
   const int CH = row_bytes / 16;                  // 16-byte chunks per token row
@@ -144,8 +164,9 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(StatsArgs a) {
         mv = a.v_scale[page * a.hkv + g];
       }
       const float inv = (float)count;
-      float* ok = a.kbar + ((int64_t)g * a.total_kblocks + kb) * a.d + dim;
-      float* ov = a.vbar + ((int64_t)g * a.total_kblocks + kb) * a.d + dim;
+      const int64_t orow = a.cached ? cache_row(a, pt, J) * a.hkv + g : (int64_t)g * a.total_kblocks + kb;
+      float* ok = a.kbar + orow * a.d + dim;
+      float* ov = a.vbar + orow * a.d + dim;
 #pragma unroll
       for (int e = 0; e < N; e += 4) {
         f32x4 vk, vv;
@@ -162,14 +183,28 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(StatsArgs a) {
   }
 }
 
-}  // namespace
+// kbar / vbar [g, kb, :] <- the cache rows of block kb (one workgroup per
+// global KV block, float4 copies).
+__global__ __launch_bounds__(kThreads) void gather_stats_kernel(StatsArgs a, const float* kc, const float* vc) {
+  const int kb = blockIdx.x;
+  const int s = find_seq(a.cu_kblocks, a.num_seqs, kb);
+  const int J = kb - a.cu_kblocks[s];
+  const int64_t crow = cache_row(a, a.page_table + (int64_t)s * a.max_pages, J);
+  const int n4 = a.hkv * a.d / 4;
+  for (int i = threadIdx.x; i < n4; i += kThreads) {
+    const int g = (4 * i) / a.d, dim = (4 * i) % a.d;
+    const int64_t src = (crow * a.hkv + g) * a.d + dim;
+    const int64_t dst = ((int64_t)g * a.total_kblocks + kb) * a.d + dim;
+    *reinterpret_cast<f32x4*>(a.kbar + dst) = *reinterpret_cast<const f32x4*>(kc + src);
+    *reinterpret_cast<f32x4*>(a.vbar + dst) = *reinterpret_cast<const f32x4*>(vc + src);
+  }
+}
 
-hipError_t launch_block_stats(const fp2_batch* b, const fp2_kv* kv, const BatchInfo& info,
-                              float* kbar, float* vbar, hipStream_t stream) {
-  if (info.total_kblocks == 0) return hipSuccess;
+StatsArgs stats_args(const fp2_batch* b, const fp2_kv* kv, const BatchInfo& info, float* kbar, float* vbar) {
   StatsArgs a;
   a.cu_kblocks = b->cu_kblocks;
   a.seqlens_k = b->seqlens_k;
+  a.cu_seqlens_q = b->cu_seqlens_q;
   a.page_table = kv->page_table;
   a.k_pages = static_cast<const uint8_t*>(kv->k_pages);
   a.v_pages = static_cast<const uint8_t*>(kv->v_pages);
@@ -185,12 +220,45 @@ hipError_t launch_block_stats(const fp2_batch* b, const fp2_kv* kv, const BatchI
   a.d = kv->head_dim;
   a.block = b->block;
   a.total_kblocks = (int)info.total_kblocks;
-  dim3 grid((unsigned)info.total_kblocks);
-  if (kv->dtype == FP2_BF16)
+  a.cached = 0;
+  a.refresh = 1;
+  a.bpp = kv->page_size >= b->block ? kv->page_size / b->block : 1;
+  return a;
+}
+
+hipError_t launch_stats(const StatsArgs& a, int dtype, int64_t total_kblocks, hipStream_t stream) {
+  dim3 grid((unsigned)total_kblocks);
+  if (dtype == FP2_BF16)
     hipLaunchKernelGGL(block_stats_kernel<2>, grid, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(block_stats_kernel<1>, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_block_stats_cached(const fp2_batch* b, const fp2_kv* kv, const BatchInfo& info, float* kcache,
+                                     float* vcache, int refresh, hipStream_t stream) {
+  if (info.total_kblocks == 0) return hipSuccess;
+  StatsArgs a = stats_args(b, kv, info, kcache, vcache);
+  a.cached = 1;
+  a.refresh = refresh;
+  return launch_stats(a, kv->dtype, info.total_kblocks, stream);
+}
+
+hipError_t launch_gather_stats(const fp2_batch* b, const fp2_kv* kv, const BatchInfo& info, const float* kcache,
+                               const float* vcache, float* kbar, float* vbar, hipStream_t stream) {
+  if (info.total_kblocks == 0) return hipSuccess;
+  StatsArgs a = stats_args(b, kv, info, kbar, vbar);
+  hipLaunchKernelGGL(gather_stats_kernel, dim3((unsigned)info.total_kblocks), dim3(kThreads), 0, stream, a, kcache,
+                     vcache);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_stats(const fp2_batch* b, const fp2_kv* kv, const BatchInfo& info,
+                              float* kbar, float* vbar, hipStream_t stream) {
+  if (info.total_kblocks == 0) return hipSuccess;
+  return launch_stats(stats_args(b, kv, info, kbar, vbar), kv->dtype, info.total_kblocks, stream);
 }
 
 }  // namespace fp2

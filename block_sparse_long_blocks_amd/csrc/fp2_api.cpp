@@ -11,6 +11,10 @@
 namespace fp2 {
 hipError_t launch_block_stats(const fp2_batch* b, const fp2_kv* kv, const BatchInfo& info,
                               float* kbar, float* vbar, hipStream_t stream);
+hipError_t launch_block_stats_cached(const fp2_batch* b, const fp2_kv* kv, const BatchInfo& info, float* kcache,
+                                     float* vcache, int refresh, hipStream_t stream);
+hipError_t launch_gather_stats(const fp2_batch* b, const fp2_kv* kv, const BatchInfo& info, const float* kcache,
+                               const float* vcache, float* kbar, float* vbar, hipStream_t stream);
 hipError_t launch_plan(const fp2_batch* b, const fp2_q* q, int hkv, const BatchInfo& info,
                        const float* kbar, float tau, int32_t* row_ptr, int32_t* col_idx,
                        int32_t* nnz, float* scores, void* workspace, hipStream_t stream);
@@ -38,6 +42,44 @@ fp2_status fp2_block_stats(const fp2_batch* batch, const fp2_kv* kv, float* kbar
   if (info.total_kblocks > 0 && (!kbar || !vbar)) return fail(FP2_ERR_INVALID, "kbar/vbar is NULL");
   return hip_status(launch_block_stats(batch, kv, info, kbar, vbar, (hipStream_t)stream),
                     "fp2_block_stats launch");
+}
+
+int64_t fp2_block_stats_cache_rows(const fp2_batch* batch, const fp2_kv* kv) {
+  BatchInfo info;
+  if (check_batch(batch, &info) != FP2_OK || check_kv(kv, batch, info) != FP2_OK) return 0;
+  const int ps = kv->page_size, B = batch->block;
+  if (ps % B != 0 && B % ps != 0) return 0;
+  return (int64_t)kv->num_pages * (ps >= B ? ps / B : 1);
+}
+
+fp2_status fp2_block_stats_cached(const fp2_batch* batch, const fp2_kv* kv, float* kbar_cache, float* vbar_cache,
+                                  int32_t refresh_prefix, void* stream) {
+  BatchInfo info;
+  fp2_status st = check_batch(batch, &info);
+  if (st != FP2_OK) return st;
+  if ((st = check_kv(kv, batch, info)) != FP2_OK) return st;
+  if (kv->page_size % batch->block != 0 && batch->block % kv->page_size != 0)
+    return fail(FP2_ERR_UNSUPPORTED, "the block stats cache needs page_size and block to divide one another");
+  if (refresh_prefix != 0 && refresh_prefix != 1) return fail(FP2_ERR_INVALID, "refresh_prefix must be 0 or 1");
+  if (info.total_kblocks > 0 && (!kbar_cache || !vbar_cache))
+    return fail(FP2_ERR_INVALID, "kbar_cache/vbar_cache is NULL");
+  return hip_status(launch_block_stats_cached(batch, kv, info, kbar_cache, vbar_cache, refresh_prefix,
+                                              (hipStream_t)stream),
+                    "fp2_block_stats_cached launch");
+}
+
+fp2_status fp2_gather_block_stats(const fp2_batch* batch, const fp2_kv* kv, const float* kbar_cache,
+                                  const float* vbar_cache, float* kbar, float* vbar, void* stream) {
+  BatchInfo info;
+  fp2_status st = check_batch(batch, &info);
+  if (st != FP2_OK) return st;
+  if ((st = check_kv(kv, batch, info)) != FP2_OK) return st;
+  if (kv->page_size % batch->block != 0 && batch->block % kv->page_size != 0)
+    return fail(FP2_ERR_UNSUPPORTED, "the block stats cache needs page_size and block to divide one another");
+  if (info.total_kblocks > 0 && (!kbar_cache || !vbar_cache || !kbar || !vbar))
+    return fail(FP2_ERR_INVALID, "a cache or output pointer is NULL");
+  return hip_status(launch_gather_stats(batch, kv, info, kbar_cache, vbar_cache, kbar, vbar, (hipStream_t)stream),
+                    "fp2_gather_block_stats launch");
 }
 
 size_t fp2_plan_workspace_bytes(const fp2_batch* batch, int32_t num_kv_heads) {

@@ -115,6 +115,33 @@ typedef struct {
 fp2_status fp2_block_stats(const fp2_batch *batch, const fp2_kv *kv,
                            float *kbar, float *vbar, void *stream);
 
+/* Stage 1a for chunked prefill (Table 6 serves with chunked prefill; the
+ * pooled statistics are Figure 3's), with the block means kept in a cache
+ * beside the KV pages.  The pages do not say how the statistics of a cached
+ * prefix are kept; this cache is the library's own design: the means of a
+ * block whose tokens are all in the cached prefix do not change between
+ * calls, so only the blocks holding new tokens are read again.  The cache has one row per KV block a page holds:
+ * fp2_block_stats_cache_rows() = num_pages * max(1, page_size / B) rows
+ * (0 when page_size and B do not divide one another: unsupported).  Block J
+ * of sequence s lives in row page_table[s][J*B/page_size] * max(1,
+ * page_size/B) + J % max(1, page_size/B).
+ *   kbar_cache, vbar_cache  device float32 [cache_rows, Hkv, d], owned by the
+ *                   caller alongside its KV pages
+ *   refresh_prefix  1: compute every block of the batch; 0: only blocks
+ *                   J >= prefix/B (their rows are overwritten), the rows of
+ *                   prefix blocks are used as an earlier call left them
+ * The values are bit for bit those of fp2_block_stats. */
+int64_t fp2_block_stats_cache_rows(const fp2_batch *batch, const fp2_kv *kv);
+fp2_status fp2_block_stats_cached(const fp2_batch *batch, const fp2_kv *kv,
+                                  float *kbar_cache, float *vbar_cache,
+                                  int32_t refresh_prefix, void *stream);
+
+/* Lays the cache rows of the batch's blocks out as the kbar, vbar arrays
+ * [Hkv, total_kblocks, d] that fp2_plan_mask and fp2_prefill_run take. */
+fp2_status fp2_gather_block_stats(const fp2_batch *batch, const fp2_kv *kv,
+                                  const float *kbar_cache, const float *vbar_cache,
+                                  float *kbar, float *vbar, void *stream);
+
 /* Workspace bytes fp2_plan_mask needs for this batch (0 if empty). */
 size_t fp2_plan_workspace_bytes(const fp2_batch *batch, int32_t num_kv_heads);
 

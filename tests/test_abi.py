@@ -69,6 +69,22 @@ def test_sizes_and_counts():
     assert lib.fp2_run_workspace_bytes(b, 12, 3, 64, lib.FP2_FP8_E4M3) >= 2 * 3 * (8 + 2) * 64 * 2
 
 
+def test_block_stats_cache_rows_and_checks():
+    """The paged block-stats cache: one row per KV block a page holds; page sizes that do not
+    divide B (or the reverse) are unsupported; bad arguments are rejected before any launch."""
+    b = _batch([256], [256])
+    assert lib.fp2_block_stats_cache_rows(b, _kv(page=64)) == 4          # a block spans 2 pages: keyed by its first
+    assert lib.fp2_block_stats_cache_rows(b, _kv(page=128)) == 4
+    assert lib.fp2_block_stats_cache_rows(b, _kv(page=256, pages=2)) == 4  # 2 blocks per page
+    assert lib.fp2_block_stats_cache_rows(b, _kv(page=96)) == 0
+    f32 = torch.zeros(16)
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_block_stats_cached, b, _kv(page=96), f32, f32, True, match="page_size")
+    _expect(lib.FP2_ERR_INVALID, lib.fp2_block_stats_cached, b, _kv(), None, f32, False, match="NULL")
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_gather_block_stats, b, _kv(page=96), f32, f32, f32, f32,
+            match="page_size")
+    _expect(lib.FP2_ERR_INVALID, lib.fp2_gather_block_stats, b, _kv(), f32, f32, None, f32, match="NULL")
+
+
 def test_validation_rejects_before_launch():
     f32 = torch.zeros(16)
     i32 = torch.zeros(16, dtype=torch.int32)

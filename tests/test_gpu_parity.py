@@ -63,11 +63,13 @@ SMALL = {
     "chunk_after_prefix": _cfg("chunk_after_prefix", (6144,), (6016,), 8, 4, 128, 128, 128),
     "chunk_after_prefix_fp8": _cfg("chunk_after_prefix_fp8", (6144,), (6016,), 8, 4, 128, 128, 128,
                                    dtype="fp8"),
+    # pages that hold two blocks each (B = 64, page 128)
+    "d128_b64_p128": _cfg("d128_b64_p128", (700, 300), (256, 0), 8, 2, 128, 64, 128),
 }
 TAUS = {"tiny": (0.0, 0.005, 0.01, 0.02, 2.0), "varlen_p64": (0.0, 0.5, 3.0),
         "d64_b128_p16": (0.3, 3.0), "d128_b64_g8": (0.2, 2.0), "single_token": (0.0, 1.0),
         "fp8_varlen": (0.0, 0.5, 3.0), "d128_p24_g1": (0.0, 1.0), "d128_p8_g8": (0.0, 1.0),
-        "chunk_after_prefix": (0.5, 1e9), "chunk_after_prefix_fp8": (0.5, 1e9)}
+        "chunk_after_prefix": (0.5, 1e9), "chunk_after_prefix_fp8": (0.5, 1e9), "d128_b64_p128": (0.0, 1.0)}
 
 _cache = {}
 
@@ -155,6 +157,47 @@ def test_attention_parity(name, corr, out_dtype):
     for tau in TAUS[name]:
         got, ref, w, _ = _attention_case(name, tau, corr, out_dtype=out_dtype)
         check_out(got, ref, TOL[w.cfg.dtype], out_dtype)
+
+
+@pytest.mark.parametrize("name", ["varlen_p64", "fp8_varlen", "chunk_after_prefix", "d128_b64_p128", "d64_b128_p16"])
+def test_cached_block_stats(name):
+    """The block means kept in a cache beside the KV pages: with refresh_prefix the gathered
+    kbar / vbar equal fp2_block_stats bit for bit; without it, the rows of blocks holding new
+    tokens are computed again (planted NaNs vanish) and the rows of cached-prefix blocks are left
+    as they were (a planted sentinel comes back from the gather)."""
+    import block_sparse_long_blocks_amd as lib
+    w, _ = workload(name)
+    L = layer(w)
+    L.stats()
+    rows = lib.fp2_block_stats_cache_rows(L.batch, L.kv)
+    B, ps = w.cfg.block, w.cfg.page_size
+    bpp = max(1, ps // B)
+    assert rows == w.k_pages.shape[0] * bpp
+    kc = torch.full((rows, w.cfg.hkv, w.cfg.d), float("nan"), device="cuda")
+    vc = kc.clone()
+    lib.fp2_block_stats_cached(L.batch, L.kv, kc, vc, True)
+    kb, vb = torch.empty_like(L.kbar), torch.empty_like(L.vbar)
+    lib.fp2_gather_block_stats(L.batch, L.kv, kc, vc, kb, vb)
+    torch.cuda.synchronize()
+    assert torch.equal(kb, L.kbar) and torch.equal(vb, L.vbar)
+    prefix, new = [], []
+    for s in range(w.num_seqs):
+        T, n = int(w.seqlens_k[s]), int(w.n_q[s])
+        for J in range(-(-T // B)):
+            row = int(w.page_table[s, J * B // ps]) * bpp + J % bpp
+            (prefix if J < (T - n) // B else new).append((int(w.cu_kblocks[s]) + J, row))
+    assert prefix and new
+    kc[[r for _, r in new]] = float("nan")
+    vc[[r for _, r in new]] = float("nan")
+    kc[[r for _, r in prefix]] = 7.0
+    vc[[r for _, r in prefix]] = -3.0
+    lib.fp2_block_stats_cached(L.batch, L.kv, kc, vc, False)
+    lib.fp2_gather_block_stats(L.batch, L.kv, kc, vc, kb, vb)
+    torch.cuda.synchronize()
+    nk = [k for k, _ in new]
+    pk = [k for k, _ in prefix]
+    assert torch.equal(kb[:, nk], L.kbar[:, nk]) and torch.equal(vb[:, nk], L.vbar[:, nk])
+    assert bool((kb[:, pk] == 7.0).all()) and bool((vb[:, pk] == -3.0).all())
 
 
 @pytest.mark.parametrize("corr", [True, False])
