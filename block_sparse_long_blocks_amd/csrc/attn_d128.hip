@@ -18,8 +18,8 @@
 //    widened to bf16 rows.
 //  * Tiles stream global -> LDS by DMA (global_load_lds, 16 bytes a lane)
 //    into two LDS buffers: the next tile's DMA runs while the current tile is
-//    computed; one barrier per tile.  No staging registers, no LDS writes
-//    from the waves.
+//    computed; one barrier per tile.  No staging registers; the waves write
+//    LDS only in the epilogue (bf16 output rows).
 //  * bf16 K tiles (rows = keys) and V^T tiles (rows = d) share one LDS
 //    layout: 256-byte rows in groups of four (one 1 KB DMA unit), groups 1088
 //    bytes apart, 16-byte chunk k of row r in slot k ^ (r & 3); e4m3 K tiles
@@ -36,7 +36,12 @@
 //    step j, operand reads run a few slots ahead and the softmax values are
 //    consumed a group or more after they are produced.  Masks are applied
 //    to the exponent; the reference max is refreshed only when probabilities
-//    would reach 2^64.
+//    would reach 2^64.  The younger wave of each SIMD takes the higher issue
+//    priority for the first half of a tile (the arbiter otherwise serves the
+//    older one first).
+//  * The workgroups run work items built on the device (items_kernel):
+//    heaviest first, with the exact tiles of rows much heavier than the rest
+//    cut into chunks whose float32 partials combine_kernel merges.
 #include <type_traits>
 
 #include "attn_common.h"
