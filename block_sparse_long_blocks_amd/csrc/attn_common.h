@@ -33,7 +33,8 @@ struct AttnArgs {
   int4* items;             // d128 kernel: work items {rank, first tile, end tile, partial slot or -1},
                            // heaviest first, [rows + extra_cap]
   int4* splits;            // d128 kernel: split rows {rank, first slot, chunks, 0}, [extra_cap]
-  int32_t* rank_slot;      // d128 kernel: first partial slot of each split row (items kernel scratch)
+  int4* rank_slot;         // d128 kernel: per CSR rank {exact tiles, mean tiles, first partial slot, 0}
+                           // (items kernel scratch)
   int32_t* counters;       // d128 kernel: [0] work items, [1] split rows
   float* part;             // d128 kernel: partial O, reference max and row sum of split-row chunks
   int extra_cap, chunk_cap, ncu;

@@ -1097,6 +1097,17 @@ __device__ void rank_tiles(const AttnArgs& a, int r, int& nexact, int& nmean) {
   }
 }
 
+// Tile counts of every CSR rank, one thread each, into a.rank_slot for
+// items_kernel: {exact tiles, mean tiles (an upper bound), first partial slot
+// (-1 until items_kernel splits the row), 0}.
+__global__ __launch_bounds__(256) void rank_tiles_kernel(AttnArgs a) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= a.rows) return;
+  int ne, nm;
+  rank_tiles(a, r, ne, nm);
+  a.rank_slot[r] = make_int4(ne, nm, -1, 0);
+}
+
 // Work items and their launch order.  The kept-block counts of the rows are
 // very uneven under a max-based threshold (a few rows keep most of their
 // causal blocks), so the exact tiles of a row with more than C of them are
@@ -1111,6 +1122,7 @@ constexpr int kItemsThreads = 1024;
 constexpr int kItemsMaxBins = 8192;  // 32 KB of LDS; heavier items share the top bin
 constexpr int kMinChunkTiles = 16;
 constexpr int kItemsPerCuShare = 4;
+constexpr int kRankCache = 8;  // rank records a thread keeps in registers (8192 ranks with 1024 threads)
 __global__ __launch_bounds__(kItemsThreads) void items_kernel(AttnArgs a, int nbins) {
   extern __shared__ int hist[];  // [nbins]
   __shared__ int part[kItemsThreads];
@@ -1120,13 +1132,31 @@ __global__ __launch_bounds__(kItemsThreads) void items_kernel(AttnArgs a, int nb
   if (t < 2) s_tot[t] = 0;
   if (t < 3) s_cnt[t] = 0;
   __syncthreads();
-  int ex = 0, all = 0;
-  for (int r = t; r < a.rows; r += kItemsThreads) {
-    int ne, nm;
-    rank_tiles(a, r, ne, nm);
-    ex += ne;
-    all += ne + nm;
+  // the records of this thread's ranks r = t + k kItemsThreads: the first
+  // kRankCache in registers (loaded at once), the rest from memory
+  int4 rc[kRankCache];
+#pragma unroll
+  for (int k = 0; k < kRankCache; ++k) {
+    const int r = t + k * kItemsThreads;
+    rc[k] = r < a.rows ? a.rank_slot[r] : make_int4(0, 0, -1, 0);
   }
+  auto each_rank = [&](auto&& body) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kRankCache; ++k) {
+      const int r = t + k * kItemsThreads;
+      if (r < a.rows) body(r, rc[k]);
+    }
+    for (int r = t + kRankCache * kItemsThreads; r < a.rows; r += kItemsThreads) {
+      int4 rt = a.rank_slot[r];
+      body(r, rt);
+      a.rank_slot[r] = rt;
+    }
+  };
+  int ex = 0, all = 0;
+  each_rank([&](int, int4& rt) {
+    ex += rt.x;
+    all += rt.x + rt.y;
+  });
   atomicAdd(&s_tot[0], ex);
   atomicAdd(&s_tot[1], all);
   __syncthreads();
@@ -1138,21 +1168,21 @@ __global__ __launch_bounds__(kItemsThreads) void items_kernel(AttnArgs a, int nb
     C = max(C, (s_tot[0] + a.extra_cap - 1) / a.extra_cap);  // sum over rows of (chunks - 1) <= extra_cap
   }
   // pass 1: histogram of the items' tile counts; partial slots of split rows
-  for (int r = t; r < a.rows; r += kItemsThreads) {
-    int ne, nm;
-    rank_tiles(a, r, ne, nm);
+  int nitems = 0;
+  each_rank([&](int r, int4& rt) {
+    const int ne = rt.x, nm = rt.y;
     const int nch = ne > C ? (ne + C - 1) / C : 1;
     if (nch > 1) {
-      const int slot0 = atomicAdd(&s_cnt[1], nch);
-      a.splits[atomicAdd(&s_cnt[2], 1)] = make_int4(r, slot0, nch, 0);
-      a.rank_slot[r] = slot0;
+      rt.z = atomicAdd(&s_cnt[1], nch);
+      a.splits[atomicAdd(&s_cnt[2], 1)] = make_int4(r, rt.z, nch, 0);
     }
-    atomicAdd(&s_cnt[0], nch);
+    nitems += nch;
     for (int c = 0; c < nch; ++c) {
       const int w = (int)(((int64_t)(c + 1) * ne) / nch - ((int64_t)c * ne) / nch) + (c == nch - 1 ? nm : 0);
       atomicAdd(&hist[min(w, nbins - 1)], 1);
     }
-  }
+  });
+  atomicAdd(&s_cnt[0], nitems);
   __syncthreads();
   // exclusive scan in descending tile count: bin w starts after every item
   // with more tiles; thread t owns bins nbins-1-k for k in its chunk
@@ -1176,17 +1206,15 @@ __global__ __launch_bounds__(kItemsThreads) void items_kernel(AttnArgs a, int nb
   }
   __syncthreads();
   // pass 2: place the items
-  for (int r = t; r < a.rows; r += kItemsThreads) {
-    int ne, nm;
-    rank_tiles(a, r, ne, nm);
+  each_rank([&](int r, int4& rt) {
+    const int ne = rt.x, nm = rt.y;
     const int nch = ne > C ? (ne + C - 1) / C : 1;
-    const int slot0 = nch > 1 ? a.rank_slot[r] : -1;
     for (int c = 0; c < nch; ++c) {
       const int c0 = (int)(((int64_t)c * ne) / nch), c1 = (int)(((int64_t)(c + 1) * ne) / nch);
       const int w = c1 - c0 + (c == nch - 1 ? nm : 0);
-      a.items[atomicAdd(&hist[min(w, nbins - 1)], 1)] = make_int4(r, c0, c1, nch > 1 ? slot0 + c : -1);
+      a.items[atomicAdd(&hist[min(w, nbins - 1)], 1)] = make_int4(r, c0, c1, nch > 1 ? rt.z + c : -1);
     }
-  }
+  });
   if (t == 0) {
     a.counters[0] = s_cnt[0];
     a.counters[1] = s_cnt[2];
@@ -1311,6 +1339,8 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0) a.ncu = ncu;
   }
   const int nbins = min(max_kblocks + (max_kblocks + kBlk - 1) / kBlk + 1, kItemsMaxBins);
+  hipLaunchKernelGGL(rank_tiles_kernel, dim3((unsigned)((a.rows + 255) / 256)), dim3(256), 0, stream, a);
+  if (hipError_t e0 = hipGetLastError(); e0 != hipSuccess) return e0;
   hipLaunchKernelGGL(items_kernel, dim3(1), dim3(kItemsThreads), (size_t)nbins * sizeof(int), stream, a, nbins);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -49,7 +49,7 @@ struct RunLayout {
   size_t kd = 0;       // e4m3 V^T path: K codes as bf16 rows, [Hkv, total_kblocks, B, d]
   size_t items = 0;    // V^T path: work items in launch order, int4 [rows + extra_cap]
   size_t splits = 0;   // V^T path: rows split into chunks, int4 [extra_cap]
-  size_t rank_slot = 0;  // V^T path: first partial slot of each split row, int32 [rows]
+  size_t rank_slot = 0;  // V^T path: per row {exact tiles, mean tiles, first partial slot, 0}, int4 [rows]
   size_t counters = 0;   // V^T path: item and split-row counts, int32 [4]
   size_t part = 0;       // V^T path: partial results of the chunks of split rows
   int64_t extra_cap = 0;  // most work items beyond one per row (chunks of split rows)

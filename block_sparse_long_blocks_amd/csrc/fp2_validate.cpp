@@ -164,7 +164,7 @@ RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int n
     L.items = L.total;
     L.splits = L.items + up((nrows + (size_t)L.extra_cap) * 16);
     L.rank_slot = L.splits + up((size_t)L.extra_cap * 16 + 16);
-    L.counters = L.rank_slot + up(nrows * 4);
+    L.counters = L.rank_slot + up(nrows * 16);
     L.part = L.counters + 256;
     L.total = L.part + up(2 * (size_t)L.extra_cap * slices * 8 * (size_t)kPartFloatsPerWave * 4);
   } else {

@@ -599,7 +599,7 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.kd = wsb + L.kd;
   a.items = reinterpret_cast<int4*>(wsb + L.items);
   a.splits = reinterpret_cast<int4*>(wsb + L.splits);
-  a.rank_slot = reinterpret_cast<int32_t*>(wsb + L.rank_slot);
+  a.rank_slot = reinterpret_cast<int4*>(wsb + L.rank_slot);
   a.counters = reinterpret_cast<int32_t*>(wsb + L.counters);
   a.part = reinterpret_cast<float*>(wsb + L.part);
   a.extra_cap = (int)L.extra_cap;
