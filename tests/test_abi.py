@@ -69,6 +69,13 @@ def test_sizes_and_counts():
     assert lib.fp2_run_workspace_bytes(b, 12, 3, 64, lib.FP2_FP8_E4M3) >= 2 * 3 * (8 + 2) * 64 * 2
 
 
+def test_sequence_length_limits():
+    """2^21 keys (16,384 blocks of 128) is the largest sequence accepted; one block more is
+    rejected on the host (the kept-block bitmask and the plan's score row live in LDS)."""
+    assert lib.fp2_plan_max_nnz(_batch([1 << 21], [256]), 1) == 16383 + 16384  # diagonals 16382, 16383
+    assert lib.fp2_plan_max_nnz(_batch([(1 << 21) + 128], [256]), 1) == -1
+
+
 def test_block_stats_cache_rows_and_checks():
     """The paged block-stats cache: one row per KV block a page holds; page sizes that do not
     divide B (or the reverse) are unsupported; bad arguments are rejected before any launch."""

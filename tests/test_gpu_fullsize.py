@@ -125,3 +125,42 @@ def test_fullsize_extreme_with_and_without_correction():
     print(f"extreme_fp8 mean abs error vs dense attention (last query block, all heads): "
           f"with correction {err[True]:.4f}, without {err[False]:.4f}")
     assert err[True] < err[False]
+
+
+def test_max_kv_blocks():
+    """The largest sequence the library accepts: 2^21 keys = 16,384 KV blocks of 128 (the kept-block
+    bitmask, the score row of the plan and the mean-token list at their limits), two query blocks at
+    the end of a 2,096,896-token cached prefix, 4 query / 1 KV head, d 128, bf16, unstructured
+    N(0,1) data with tau for a few percent: block means, kept lists and attention (with and without
+    the correction, whose mean-token tiles then span all 16,383 skippable blocks) against the oracle."""
+    import block_sparse_long_blocks_amd as lib
+    T = 1 << 21
+    cfg = synth.Config(name="max_kv_blocks", seqlens=(T,), prefixes=(T - 256,), hq=4, hkv=1, d=128, block=128,
+                       page_size=128, dtype="bf16", structure="plain", tau=0.008, seed=13)
+    w = synth.make_custom(cfg)
+    assert w.total_kblocks == 16384
+    print("\nmax_kv_blocks: inputs generated", flush=True)
+    L = lib.PrefillLayer(*lib.from_workload(w), out_dtype=torch.float32)
+    L.stats()
+    L.plan(cfg.tau)
+    torch.cuda.synchronize()
+    rp, ci = L.csr_host()
+    kb = L.kbar.cpu().numpy().astype(np.float64)
+    vb = L.vbar.cpu().numpy().astype(np.float64)
+    outs = {}
+    for corr in (True, False):
+        L.attend(corr)
+        torch.cuda.synchronize()
+        outs[corr] = L.out[:w.total_q].float().cpu().numpy().astype(np.float64)
+    del L
+    torch.cuda.empty_cache()
+    print("max_kv_blocks: GPU calls done", flush=True)
+    seqs = decoded_seqs(w)
+    plan = O.plan_batch(seqs, cfg.block, cfg.tau)
+    print("max_kv_blocks: oracle plan done", flush=True)
+    check_stats_and_plan(w, seqs, plan, (rp, ci, kb, vb))
+    assert 0 < rp[-1] < w.causal_pairs()  # sparse: the correction has skipped blocks to cover
+    rows = [(0, 0, 0), (0, 0, 1)]
+    for corr in (True, False):
+        worst = check_rows(w, seqs, (rp, ci), outs[corr], corr, rows, TOL["bf16"], out_dtype="f32")
+        print(f"max_kv_blocks correction={corr}: max abs err {worst:.4f}")
