@@ -26,6 +26,14 @@ exact definition followed here is:
      B * exp(q . kbar_J / sqrt(d) - m) * (vbar_J, 1), merged into the same
      softmax normaliser.
 
+Query blocks hold B tokens and KV blocks BK tokens (BK = B unless given; BK
+must divide B).  Table 7 pairs 128-token query tiles with 64-token KV tiles.
+With BK < B the diagonal of query block I is the run of KV blocks that hold
+one of its own positions, [diag_lo(I), diag_hi(I)]: all of them are forced,
+scores and keys reach up to diag_hi, the surrogate covers skipped J in
+[1, diag_lo) and its weight is the KV block size BK.  With BK = B the run is
+the single block diag(I) = P/B + I.
+
 Every input is the exact value the GPU sees: bfloat16 bits widened, or
 OCP E4M3 codes times their float32 block scale.
 """
@@ -38,7 +46,7 @@ import numpy as np
 
 __all__ = [
     "decode_bf16", "decode_e4m3", "E4M3_VALUES", "dequant_blocks", "decode_sequence",
-    "block_means", "pooled_query_means", "block_scores", "select_blocks",
+    "block_means", "pooled_query_means", "diag_range", "block_scores", "select_blocks",
     "attend", "dense", "plan_batch", "run_batch", "NEAR_TIE",
 ]
 
@@ -86,13 +94,19 @@ def dequant_blocks(codes: np.ndarray, scales: np.ndarray, block: int) -> np.ndar
     return x * scales.astype(np.float64)[tok_block][:, :, None]
 
 
-def decode_sequence(dtype: str, block: int, q, q_scale, k, k_scale, v, v_scale):
-    """Storage codes of one sequence -> float64 (Q[n,Hq,d], K[T,Hkv,d], V[T,Hkv,d])."""
+def decode_sequence(dtype: str, block: int, q, q_scale, k, k_scale, v, v_scale,
+                    kv_block: Optional[int] = None):
+    """Storage codes of one sequence -> float64 (Q[n,Hq,d], K[T,Hkv,d], V[T,Hkv,d]).
+
+    e4m3: one query scale per (query block, head), one K / V scale per (KV
+    block, head); kv_block = block unless given.
+    """
     if dtype == "bf16":
         return decode_bf16(q), decode_bf16(k), decode_bf16(v)
     if dtype == "fp8":
-        return (dequant_blocks(q, q_scale, block), dequant_blocks(k, k_scale, block),
-                dequant_blocks(v, v_scale, block))
+        kb = kv_block or block
+        return (dequant_blocks(q, q_scale, block), dequant_blocks(k, k_scale, kb),
+                dequant_blocks(v, v_scale, kb))
     raise ValueError(dtype)
 
 
@@ -126,15 +140,32 @@ def pooled_query_means(Q: np.ndarray, B: int, G: int) -> np.ndarray:
     return out
 
 
-def block_scores(qbar: np.ndarray, kbar: np.ndarray, P: int, B: int, d: int) -> np.ndarray:
-    """float32 scores s[g, I, J] = (qbar_I . kbar_J) / sqrt(d) for J <= diag(I); -inf above.
+def diag_range(P: int, n: int, i: int, B: int, BK: Optional[int] = None) -> Tuple[int, int]:
+    """First and last KV block (BK tokens) holding a position of query block i (B tokens).
+
+    Query block i covers the absolute positions P + i*B .. P + min((i+1)*B, n) - 1.
+    """
+    BK = B if BK is None else BK
+    first = P + i * B
+    last = P + min((i + 1) * B, n) - 1
+    return first // BK, last // BK
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray, P: int, B: int, d: int,
+                 n: Optional[int] = None, BK: Optional[int] = None) -> np.ndarray:
+    """float32 scores s[g, I, J] = (qbar_I . kbar_J) / sqrt(d) for J <= diag_hi(I); -inf above.
 
     The pooled means are held as float32 (the precision the scores are
     defined in); the dot product of those float32 values is formed in
-    float64 and rounded once to float32.  diag(I) = P/B + I.
+    float64 and rounded once to float32.  n (new tokens) is needed when
+    BK < B; with BK = B, diag(I) = P/B + I.
     """
     nqb, Hkv, _ = qbar.shape
     nkb = kbar.shape[0]
+    if n is None:
+        if BK is not None and BK != B:
+            raise ValueError("n is needed when the KV block differs from the query block")
+        n = nqb * B
     q32 = qbar.astype(np.float32).astype(np.float64)
     k32 = kbar.astype(np.float32).astype(np.float64)
     c = 1.0 / math.sqrt(d)
@@ -142,29 +173,34 @@ def block_scores(qbar: np.ndarray, kbar: np.ndarray, P: int, B: int, d: int) -> 
     for g in range(Hkv):
         full = (q32[:, g, :] @ k32[:, g, :].T) * c  # [nqb, nkb]
         for i in range(nqb):
-            diag = P // B + i
-            s[g, i, :diag + 1] = full[i, :diag + 1].astype(np.float32)
+            _, hi = diag_range(P, n, i, B, BK)
+            s[g, i, :hi + 1] = full[i, :hi + 1].astype(np.float32)
     return s
 
 
-def select_blocks(s: np.ndarray, P: int, B: int, tau: float):
+def select_blocks(s: np.ndarray, P: int, B: int, tau: float, n: Optional[int] = None,
+                  BK: Optional[int] = None):
     """Max-based dynamic threshold with forced blocks.
 
     thr[g, I] = float32(max_J s[g, I, J] - tau); keep J iff s >= thr, or
-    J == 0, or J == diag(I).  Returns (keep[g, I, J] bool, thr[g, I] float32,
-    rowmax[g, I] float32).
+    J == 0, or J is on the diagonal of I (diag_range).  Returns (keep[g, I, J]
+    bool, thr[g, I] float32, rowmax[g, I] float32).
     """
     Hkv, nqb, nkb = s.shape
+    if n is None:
+        if BK is not None and BK != B:
+            raise ValueError("n is needed when the KV block differs from the query block")
+        n = nqb * B
     t32 = np.float32(tau)
     rowmax = s.max(axis=2)
     with np.errstate(invalid="ignore", over="ignore"):
         thr = (rowmax - t32).astype(np.float32)
     keep = s >= thr[:, :, None]
     for i in range(nqb):
-        diag = P // B + i
-        keep[:, i, diag + 1:] = False
+        lo, hi = diag_range(P, n, i, B, BK)
+        keep[:, i, hi + 1:] = False
         keep[:, i, 0] = True
-        keep[:, i, diag] = True
+        keep[:, i, lo:hi + 1] = True
     return keep, thr, rowmax
 
 
@@ -175,15 +211,16 @@ def select_blocks(s: np.ndarray, P: int, B: int, tau: float):
 def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, keep: np.ndarray, B: int,
            correction: bool, kbar: Optional[np.ndarray] = None,
            vbar: Optional[np.ndarray] = None,
-           rows: Optional[Sequence[Tuple[int, int]]] = None):
+           rows: Optional[Sequence[Tuple[int, int]]] = None, BK: Optional[int] = None):
     """Block-sparse causal GQA attention with optional mean correction, one sequence.
 
     Q[n, Hq, d]; K, V[T, Hkv, d]; the n queries sit at absolute positions
     P..T-1 with P = T - n (a cached prefix of P tokens).  keep[g, I, J]
-    selects KV blocks per (KV head, query block).  A query at position p
-    sees a key at position u of a kept block iff u <= p.  With correction,
-    every J in [1, diag(I)) that is not kept adds the surrogate logit
-    q . kbar_J / sqrt(d) with weight B and value vbar_J.
+    selects KV blocks (BK tokens, BK = B unless given) per (KV head, query
+    block of B tokens).  A query at position p sees a key at position u of a
+    kept block iff u <= p.  With correction, every J in [1, diag_lo(I)) that
+    is not kept adds the surrogate logit q . kbar_J / sqrt(d) with weight BK
+    and value vbar_J.
 
     rows: optional list of (g, I) to compute; other outputs stay NaN.
     Returns (O[n, Hq, d], lse[n, Hq]) with lse = log of the softmax
@@ -193,20 +230,21 @@ def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, keep: np.ndarray, B: int
     T, Hkv, _ = K.shape
     G = Hq // Hkv
     P = T - n
+    BK = B if BK is None else BK
     c = 1.0 / math.sqrt(d)
     if correction and (kbar is None or vbar is None):
-        kbar, vbar = block_means(K, B), block_means(V, B)
+        kbar, vbar = block_means(K, BK), block_means(V, BK)
     nqb = -(-n // B)
     O = np.full((n, Hq, d), np.nan, dtype=np.float64)
     lse = np.full((n, Hq), np.nan, dtype=np.float64)
     if rows is None:
         rows = [(g, i) for g in range(Hkv) for i in range(nqb)]
-    logB = math.log(B)
+    logB = math.log(BK)
     for g, i in rows:
         t0, t1 = i * B, min((i + 1) * B, n)
-        diag = P // B + i
-        kept = np.nonzero(keep[g, i, :diag + 1])[0]
-        keys = np.concatenate([np.arange(j * B, min((j + 1) * B, T)) for j in kept])
+        dlo, dhi = diag_range(P, n, i, B, BK)
+        kept = np.nonzero(keep[g, i, :dhi + 1])[0]
+        keys = np.concatenate([np.arange(j * BK, min((j + 1) * BK, T)) for j in kept])
         qpos = P + np.arange(t0, t1)                       # absolute query positions
         Qb = Q[t0:t1, g * G:(g + 1) * G, :]               # [nt, G, d]
         logit = np.einsum("tgd,kd->tgk", Qb, K[keys, g, :]) * c
@@ -215,7 +253,7 @@ def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, keep: np.ndarray, B: int
         parts_l = [logit]
         parts_v = [V[keys, g, :]]
         if correction:
-            skipped = np.array([j for j in range(1, diag) if not keep[g, i, j]], dtype=np.int64)
+            skipped = np.array([j for j in range(1, dlo) if not keep[g, i, j]], dtype=np.int64)
             if skipped.size:
                 lbar = np.einsum("tgd,kd->tgk", Qb, kbar[skipped, g, :]) * c + logB
                 parts_l.append(lbar)
@@ -261,8 +299,9 @@ def dense(Q: np.ndarray, K: np.ndarray, V: np.ndarray,
 # Batch level: CSR plan and outputs in the library's layouts
 # ---------------------------------------------------------------------------
 
-def plan_batch(seqs: List[Tuple[np.ndarray, np.ndarray, np.ndarray]], B: int, tau: float) -> Dict:
-    """Stage 1 over a variable-length batch.
+def plan_batch(seqs: List[Tuple[np.ndarray, np.ndarray, np.ndarray]], B: int, tau: float,
+               BK: Optional[int] = None) -> Dict:
+    """Stage 1 over a variable-length batch (query blocks of B tokens, KV blocks of BK = B unless given).
 
     seqs: per sequence (Q[n,Hq,d], K[T,Hkv,d], V[T,Hkv,d]) in float64.
     Returns a dict with
@@ -280,10 +319,10 @@ def plan_batch(seqs: List[Tuple[np.ndarray, np.ndarray, np.ndarray]], B: int, ta
     for Q, K, V in seqs:
         n, T = Q.shape[0], K.shape[0]
         P = T - n
-        kbar, vbar = block_means(K, B), block_means(V, B)
+        kbar, vbar = block_means(K, BK or B), block_means(V, BK or B)
         qbar = pooled_query_means(Q, B, G)
-        s = block_scores(qbar, kbar, P, B, d)
-        keep, thr, rowmax = select_blocks(s, P, B, tau)
+        s = block_scores(qbar, kbar, P, B, d, n, BK)
+        keep, thr, rowmax = select_blocks(s, P, B, tau, n, BK)
         with np.errstate(invalid="ignore"):
             tie = np.abs(s.astype(np.float64) - thr.astype(np.float64)[:, :, None]) <= NEAR_TIE
         kb_list.append(kbar)
@@ -336,18 +375,19 @@ __all__.append("keep_from_csr")
 
 
 def run_batch(seqs: List[Tuple[np.ndarray, np.ndarray, np.ndarray]], B: int, tau: float,
-              correction: bool, keeps: Optional[List[np.ndarray]] = None) -> Dict:
+              correction: bool, keeps: Optional[List[np.ndarray]] = None,
+              BK: Optional[int] = None) -> Dict:
     """Whole path over a batch: plan (unless keeps is given) then attention.
 
     Returns the plan dict plus out: [total_q, Hq, d] float64 and lse [total_q, Hq].
     """
-    plan = plan_batch(seqs, B, tau)
+    plan = plan_batch(seqs, B, tau, BK)
     if keeps is None:
         keeps = plan["keep"]
     outs, lses = [], []
     for (Q, K, V), keep in zip(seqs, keeps):
-        kbar, vbar = block_means(K, B), block_means(V, B)
-        O, lse = attend(Q, K, V, keep, B, correction, kbar, vbar)
+        kbar, vbar = block_means(K, BK or B), block_means(V, BK or B)
+        O, lse = attend(Q, K, V, keep, B, correction, kbar, vbar, BK=BK)
         outs.append(O)
         lses.append(lse)
     plan["out"] = np.concatenate(outs, axis=0)

@@ -31,21 +31,23 @@ def _rand_seq(rng, T, n, Hq, Hkv, d, scale=1.0):
 # brute force: every step per query in plain Python
 # ---------------------------------------------------------------------------
 
-def brute_force(Q, K, V, B, tau, correction):
+def brute_force(Q, K, V, B, tau, correction, BK=None):
+    """B: query block size; BK: KV block size (B unless given)."""
+    BK = B if BK is None else BK
     n, Hq, d = Q.shape
     T, Hkv, _ = K.shape
     G = Hq // Hkv
     P = T - n
     c = 1.0 / math.sqrt(d)
-    nkb = -(-T // B)
+    nkb = -(-T // BK)
     nqb = -(-n // B)
 
     def mean_rows(rows):
         return [sum(r[e] for r in rows) / len(rows) for e in range(d)]
 
-    kbar = [[mean_rows([K[t, g] for t in range(j * B, min(j * B + B, T))]) for g in range(Hkv)]
+    kbar = [[mean_rows([K[t, g] for t in range(j * BK, min(j * BK + BK, T))]) for g in range(Hkv)]
             for j in range(nkb)]
-    vbar = [[mean_rows([V[t, g] for t in range(j * B, min(j * B + B, T))]) for g in range(Hkv)]
+    vbar = [[mean_rows([V[t, g] for t in range(j * BK, min(j * BK + BK, T))]) for g in range(Hkv)]
             for j in range(nkb)]
     qbar = [[mean_rows([Q[t, h] for t in range(i * B, min(i * B + B, n))
                         for h in range(g * G, g * G + G)]) for g in range(Hkv)]
@@ -54,29 +56,33 @@ def brute_force(Q, K, V, B, tau, correction):
     keep_all = {}
     for g in range(Hkv):
         for i in range(nqb):
-            diag = P // B + i
+            # the query block's own positions; its diagonal = the KV blocks
+            # that hold one of them; causal blocks = those with a visible key
+            own = set(range(P + i * B, P + min(i * B + B, n)))
+            diag = [j for j in range(nkb) if own & set(range(j * BK, min(j * BK + BK, T)))]
+            causal = [j for j in range(nkb) if j * BK <= max(own)]
             s = []
-            for j in range(diag + 1):
+            for j in causal:
                 dot = sum(float(np.float32(qbar[i][g][e])) * float(np.float32(kbar[j][g][e]))
                           for e in range(d))
                 s.append(np.float32(dot * c))
             thr = np.float32(max(s) - np.float32(tau))
-            keep = [j for j in range(diag + 1) if s[j] >= thr or j == 0 or j == diag]
+            keep = [j for j in causal if s[j] >= thr or j == 0 or j in diag]
             keep_all[(g, i)] = keep
             for t in range(i * B, min(i * B + B, n)):
                 p = P + t
                 for h in range(g * G, g * G + G):
                     terms = []
                     for j in keep:
-                        for u in range(j * B, min(j * B + B, T)):
+                        for u in range(j * BK, min(j * BK + BK, T)):
                             if u <= p:
                                 lg = sum(Q[t, h, e] * K[u, g, e] for e in range(d)) * c
                                 terms.append((lg, 1.0, V[u, g]))
                     if correction:
-                        for j in range(1, diag):
+                        for j in range(1, min(diag)):
                             if j not in keep:
                                 lg = sum(Q[t, h, e] * kbar[j][g][e] for e in range(d)) * c
-                                terms.append((lg, float(B), vbar[j][g]))
+                                terms.append((lg, float(BK), vbar[j][g]))
                     m = max(lg for lg, _, _ in terms)
                     den = sum(w * math.exp(lg - m) for lg, w, _ in terms)
                     for e in range(d):
@@ -109,6 +115,57 @@ def test_oracle_matches_brute_force(T, n, Hq, Hkv, d, B, tau, corr, seed):
     np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
     if tau < 1.0 and T >= 96:
         assert nskipped > 0, "case should exercise skipped blocks"
+
+
+@pytest.mark.parametrize("T,n,Hq,Hkv,d,B,BK,tau,corr,seed", [
+    (128, 128, 2, 1, 8, 32, 16, 0.3, True, 11),
+    (160, 96, 4, 2, 8, 32, 16, 0.2, True, 12),    # prefix 64, ragged: last query block 1 KV block
+    (150, 86, 4, 1, 8, 32, 16, 0.25, True, 13),   # prefix 64, T and n ragged inside a KV block
+    (176, 112, 2, 2, 8, 64, 16, 0.3, False, 14),  # four KV blocks per query block
+])
+def test_oracle_matches_brute_force_decoupled(T, n, Hq, Hkv, d, B, BK, tau, corr, seed):
+    """Query blocks of B tokens scored against KV blocks of BK < B tokens."""
+    rng = np.random.default_rng(seed)
+    Q, K, V = _rand_seq(rng, T, n, Hq, Hkv, d)
+    for j in range(-(-T // BK)):
+        K[j * BK:(j + 1) * BK] += rng.standard_normal((1, Hkv, d)) * 0.7
+    for i in range(-(-n // B)):
+        Q[i * B:(i + 1) * B] += rng.standard_normal((1, Hq, d)) * 0.7
+    res = O.run_batch([(Q, K, V)], B, tau, corr, BK=BK)
+    ref, keep_ref = brute_force(Q, K, V, B, tau, corr, BK=BK)
+    keep = res["keep"][0]
+    nskipped = 0
+    for (g, i), js in keep_ref.items():
+        assert list(np.nonzero(keep[g, i])[0]) == js, (g, i)
+        nskipped += O.diag_range(T - n, n, i, B, BK)[1] + 1 - len(js)
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+    assert nskipped > 0, "case should exercise skipped blocks"
+
+
+def test_decoupled_scores_average_to_coupled():
+    """Linearity of the means: a full 2BK-token KV block's mean is the average
+    of its two BK halves, so its score is the average of theirs."""
+    rng = np.random.default_rng(21)
+    T, n, Hq, Hkv, d, B = 256, 256, 4, 2, 16, 32
+    Q, K, V = _rand_seq(rng, T, n, Hq, Hkv, d)
+    G = Hq // Hkv
+    qbar = O.pooled_query_means(Q, B, G)
+    s32 = O.block_scores(qbar, O.block_means(K, B), 0, B, d)
+    s16 = O.block_scores(qbar, O.block_means(K, B // 2), 0, B, d, n, B // 2)
+    for i in range(n // B):
+        for J in range(i + 1):
+            np.testing.assert_allclose(s32[:, i, J], 0.5 * (s16[:, i, 2 * J] + s16[:, i, 2 * J + 1]),
+                                       rtol=0, atol=1e-5)
+        assert np.all(np.isinf(s16[:, i, 2 * i + 2:]))
+
+
+@pytest.mark.parametrize("corr", [False, True])
+def test_tau_inf_is_dense_attention_decoupled(corr):
+    rng = np.random.default_rng(31)
+    T, n = 200, 136
+    Q, K, V = _rand_seq(rng, T, n, 4, 2, 8)
+    res = O.run_batch([(Q, K, V)], 32, float("inf"), corr, BK=16)
+    np.testing.assert_allclose(res["out"], _torch_sdpa(Q, K, V), rtol=0, atol=1e-12)
 
 
 # ---------------------------------------------------------------------------

@@ -70,18 +70,63 @@ def pin_prefix(mod):
     np.testing.assert_allclose(part["out"], full["out"][96:], rtol=0, atol=1e-12)
 
 
-PINS = [pin_brute, pin_dense, pin_identical_keys, pin_tau_zero, pin_prefix]
+def pin_brute_decoupled(mod):
+    rng = np.random.default_rng(12)
+    T, n, Hq, Hkv, d, B, BK = 160, 96, 4, 2, 8, 32, 16
+    Q, K, V = _rand_seq(rng, T, n, Hq, Hkv, d)
+    for j in range(-(-T // BK)):
+        K[j * BK:(j + 1) * BK] += rng.standard_normal((1, Hkv, d)) * 0.7
+    res = mod.run_batch([(Q, K, V)], B, 0.2, True, BK=BK)
+    ref, keep_ref = brute_force(Q, K, V, B, 0.2, True, BK=BK)
+    for (g, i), js in keep_ref.items():
+        assert list(np.nonzero(res["keep"][0][g, i])[0]) == js
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+
+
+def pin_threshold_decoupled(mod):
+    rng = np.random.default_rng(17)
+    T, n, Hq, Hkv, d, B, BK = 192, 128, 4, 2, 8, 32, 16
+    Q, K, V = _rand_seq(rng, T, n, Hq, Hkv, d)
+    # tau = 0 on random scores: block 0, the diagonal run and the row's argmax
+    res = mod.run_batch([(Q, K, V)], B, 0.0, True, BK=BK)
+    ref, keep_ref = brute_force(Q, K, V, B, 0.0, True, BK=BK)
+    for (g, i), js in keep_ref.items():
+        assert list(np.nonzero(res["keep"][0][g, i])[0]) == js
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+    # scores rising with J (a direction shared by Q and, growing, by the KV
+    # blocks): the row max sits on the last diagonal block and tau spans
+    # about one block's step
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    Q2 = Q + 2.0 * u
+    K2 = K.copy()
+    for j in range(-(-T // BK)):
+        K2[j * BK:(j + 1) * BK] += 0.5 * j * u
+    res = mod.run_batch([(Q2, K2, V)], B, 0.5, True, BK=BK)
+    ref, keep_ref = brute_force(Q2, K2, V, B, 0.5, True, BK=BK)
+    for (g, i), js in keep_ref.items():
+        assert list(np.nonzero(res["keep"][0][g, i])[0]) == js
+
+
+PINS = [pin_brute, pin_dense, pin_identical_keys, pin_tau_zero, pin_prefix, pin_brute_decoupled,
+        pin_threshold_decoupled]
 
 MUTATIONS = [
     ("surrogate weight 1 instead of B", "* c + logB", "* c"),
     ("causal mask off by one", "keys[None, :] <= qpos[:, None]", "keys[None, :] < qpos[:, None] + 1 - 1"),
-    ("kept blocks also corrected", "for j in range(1, diag) if not keep[g, i, j]", "for j in range(1, diag) if True"),
+    ("kept blocks also corrected", "for j in range(1, dlo) if not keep[g, i, j]", "for j in range(1, dlo) if True"),
     ("strict threshold", "keep = s >= thr[:, :, None]", "keep = s > thr[:, :, None]"),
     ("score scale dropped", "full = (q32[:, g, :] @ k32[:, g, :].T) * c", "full = (q32[:, g, :] @ k32[:, g, :].T)"),
-    ("diag ignores prefix in attend", "        diag = P // B + i\n        kept", "        diag = i\n        kept"),
+    ("diag ignores prefix in attend", "dlo, dhi = diag_range(P, n, i, B, BK)\n        kept",
+     "dlo, dhi = diag_range(0, n, i, B, BK)\n        kept"),
     ("pooled over tokens only", "out[i] = blk.mean(axis=(0, 2))", "out[i] = blk[:, :, 0].mean(axis=0)"),
-    ("value mean taken from keys", "kbar, vbar = block_means(K, B), block_means(V, B)\n        O, lse",
-     "kbar, vbar = block_means(K, B), block_means(K, B)\n        O, lse"),
+    ("value mean taken from keys", "kbar, vbar = block_means(K, BK or B), block_means(V, BK or B)\n        O, lse",
+     "kbar, vbar = block_means(K, BK or B), block_means(K, BK or B)\n        O, lse"),
+    ("diagonal run ignores the prefix", "first = P + i * B", "first = i * B"),
+    ("diagonal taken as one KV block", "return first // BK, last // BK", "return last // BK, last // BK"),
+    ("surrogate weight of the query block", "logB = math.log(BK)", "logB = math.log(B)"),
+    ("scores stop at the first diagonal block", "s[g, i, :hi + 1] = full[i, :hi + 1]",
+     "s[g, i, :hi] = full[i, :hi]"),
     ("exp base 2", "w = np.exp(L - m)", "w = np.exp2(L - m)"),
 ]
 
