@@ -40,7 +40,7 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 class CBatch(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("cu_seqlens_q", _p), ("seqlens_k", _p), ("cu_qblocks", _p), ("cu_kblocks", _p),
-                ("h_cu_seqlens_q", _i32p), ("h_seqlens_k", _i32p)]
+                ("h_cu_seqlens_q", _i32p), ("h_seqlens_k", _i32p), ("kv_block", ctypes.c_int32)]
 
 
 class CQ(ctypes.Structure):
@@ -112,24 +112,30 @@ def _cdiv(a: int, b: int) -> int:
 
 @dataclass
 class Batch:
-    """Variable-length batch descriptors: device int32 arrays plus host mirrors."""
+    """Variable-length batch descriptors: device int32 arrays plus host mirrors.
+
+    block: query block tokens; kv_block: KV block tokens (0: the same as block;
+    64 with block 128 pairs 128-token query blocks with 64-token KV blocks).
+    """
     block: int
     seqlens_k: Sequence[int]
     n_q: Sequence[int]
     device: str = "cuda"
+    kv_block: int = 0
 
     def __post_init__(self):
         S = len(self.seqlens_k)
+        kb = self.kv_block or self.block
         cu_q = [0]
         cu_qb = [0]
         cu_kb = [0]
         for T, n in zip(self.seqlens_k, self.n_q):
             cu_q.append(cu_q[-1] + int(n))
             cu_qb.append(cu_qb[-1] + _cdiv(int(n), self.block))
-            cu_kb.append(cu_kb[-1] + _cdiv(int(T), self.block))
+            cu_kb.append(cu_kb[-1] + _cdiv(int(T), kb))
         self.num_seqs = S
         self.total_q, self.total_qblocks, self.total_kblocks = cu_q[-1], cu_qb[-1], cu_kb[-1]
-        self.max_kblocks = max((_cdiv(int(T), self.block) for T in self.seqlens_k), default=0)
+        self.max_kblocks = max((_cdiv(int(T), kb) for T in self.seqlens_k), default=0)
         i32 = dict(dtype=torch.int32)
         self.h_cu_seqlens_q = torch.tensor(cu_q, **i32)
         self.h_seqlens_k = torch.tensor([int(t) for t in self.seqlens_k] or [0], **i32)
@@ -140,7 +146,7 @@ class Batch:
         self._c = CBatch(S, self.block, self.cu_seqlens_q.data_ptr(), self.seqlens_k_dev.data_ptr(),
                          self.cu_qblocks.data_ptr(), self.cu_kblocks.data_ptr(),
                          ctypes.cast(self.h_cu_seqlens_q.data_ptr(), _i32p),
-                         ctypes.cast(self.h_seqlens_k.data_ptr(), _i32p))
+                         ctypes.cast(self.h_seqlens_k.data_ptr(), _i32p), int(self.kv_block))
 
     @property
     def c(self) -> CBatch:

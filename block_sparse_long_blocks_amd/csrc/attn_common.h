@@ -40,10 +40,11 @@ struct AttnArgs {
   int extra_cap, chunk_cap, ncu;
   void* out;               // bf16 or f32 [total_q, Hq, D]
   float scale_log2;        // softmax_scale * log2(e)
-  float log2_block;        // log2(B): weight B of a mean token
+  float log2_block;        // log2 of the KV block size: the weight of a mean token
   PageMap pm;
   int num_seqs, hq, hkv, max_pages, page_size, total_qblocks, total_kblocks;
   int correction, slices, rows, out_f32, mt_cap;
+  int qblk;                // query block tokens (register-staged kernel; the d128 kernel's is 128)
 };
 
 

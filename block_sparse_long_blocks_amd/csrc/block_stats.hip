@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(StatsArgs a) {
       const int g = elem0 / a.d;      // a chunk never straddles two heads (d % N == 0)
       const int dim = elem0 % a.d;
       float mk = 1.f, mv = 1.f;
-      if (ESZ == 1) {  // e4m3: one scale per (page, head); page_size == block
+      if (ESZ == 1) {  // e4m3: one scale per (page, head); page_size == KV block
         const int64_t page = pt[J];
         mk = a.k_scale[page * a.hkv + g];
         mv = a.v_scale[page * a.hkv + g];
@@ -218,11 +218,11 @@ StatsArgs stats_args(const fp2_batch* b, const fp2_kv* kv, const BatchInfo& info
   a.pm = PageMap::make(kv->page_size);
   a.hkv = kv->num_kv_heads;
   a.d = kv->head_dim;
-  a.block = b->block;
+  a.block = info.kvblock;
   a.total_kblocks = (int)info.total_kblocks;
   a.cached = 0;
   a.refresh = 1;
-  a.bpp = kv->page_size >= b->block ? kv->page_size / b->block : 1;
+  a.bpp = kv->page_size >= info.kvblock ? kv->page_size / info.kvblock : 1;
   return a;
 }
 

@@ -47,7 +47,7 @@ fp2_status fp2_block_stats(const fp2_batch* batch, const fp2_kv* kv, float* kbar
 int64_t fp2_block_stats_cache_rows(const fp2_batch* batch, const fp2_kv* kv) {
   BatchInfo info;
   if (check_batch(batch, &info) != FP2_OK || check_kv(kv, batch, info) != FP2_OK) return 0;
-  const int ps = kv->page_size, B = batch->block;
+  const int ps = kv->page_size, B = info.kvblock;
   if (ps % B != 0 && B % ps != 0) return 0;
   return (int64_t)kv->num_pages * (ps >= B ? ps / B : 1);
 }
@@ -58,8 +58,8 @@ fp2_status fp2_block_stats_cached(const fp2_batch* batch, const fp2_kv* kv, floa
   fp2_status st = check_batch(batch, &info);
   if (st != FP2_OK) return st;
   if ((st = check_kv(kv, batch, info)) != FP2_OK) return st;
-  if (kv->page_size % batch->block != 0 && batch->block % kv->page_size != 0)
-    return fail(FP2_ERR_UNSUPPORTED, "the block stats cache needs page_size and block to divide one another");
+  if (kv->page_size % info.kvblock != 0 && info.kvblock % kv->page_size != 0)
+    return fail(FP2_ERR_UNSUPPORTED, "the block stats cache needs page_size and the KV block to divide one another");
   if (refresh_prefix != 0 && refresh_prefix != 1) return fail(FP2_ERR_INVALID, "refresh_prefix must be 0 or 1");
   if (info.total_kblocks > 0 && (!kbar_cache || !vbar_cache))
     return fail(FP2_ERR_INVALID, "kbar_cache/vbar_cache is NULL");
@@ -74,8 +74,8 @@ fp2_status fp2_gather_block_stats(const fp2_batch* batch, const fp2_kv* kv, cons
   fp2_status st = check_batch(batch, &info);
   if (st != FP2_OK) return st;
   if ((st = check_kv(kv, batch, info)) != FP2_OK) return st;
-  if (kv->page_size % batch->block != 0 && batch->block % kv->page_size != 0)
-    return fail(FP2_ERR_UNSUPPORTED, "the block stats cache needs page_size and block to divide one another");
+  if (kv->page_size % info.kvblock != 0 && info.kvblock % kv->page_size != 0)
+    return fail(FP2_ERR_UNSUPPORTED, "the block stats cache needs page_size and the KV block to divide one another");
   if (info.total_kblocks > 0 && (!kbar_cache || !vbar_cache || !kbar || !vbar))
     return fail(FP2_ERR_INVALID, "a cache or output pointer is NULL");
   return hip_status(launch_gather_stats(batch, kv, info, kbar_cache, vbar_cache, kbar, vbar, (hipStream_t)stream),
@@ -134,7 +134,7 @@ size_t fp2_run_workspace_bytes(const fp2_batch* batch, int32_t num_q_heads, int3
   BatchInfo info;
   if (check_batch(batch, &info) != FP2_OK || num_kv_heads < 1 || num_q_heads < num_kv_heads || head_dim < 1)
     return 0;
-  return run_layout(info, batch->num_seqs, num_q_heads, num_kv_heads, head_dim, dtype, batch->block).total;
+  return run_layout(info, batch->num_seqs, num_q_heads, num_kv_heads, head_dim, dtype).total;
 }
 
 fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv* kv,
@@ -158,10 +158,9 @@ fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv*
   if (info.total_qblocks == 0) return FP2_OK;
   if (!row_ptr || !col_idx || !out) return fail(FP2_ERR_INVALID, "row_ptr/col_idx/out is NULL");
   if (mean_correction && (!kbar || !vbar)) return fail(FP2_ERR_INVALID, "mean correction needs kbar and vbar");
-  if (mean_correction || vt_path(q->dtype, q->head_dim, batch->block)) {
+  if (mean_correction || vt_path(q->dtype, q->head_dim, info)) {
     const size_t wneed =
-        run_layout(info, batch->num_seqs, q->num_q_heads, kv->num_kv_heads, kv->head_dim, kv->dtype, batch->block)
-            .total;
+        run_layout(info, batch->num_seqs, q->num_q_heads, kv->num_kv_heads, kv->head_dim, kv->dtype).total;
     if (!workspace || workspace_bytes < wneed)
       return fail(FP2_ERR_CAPACITY, "run workspace " + std::to_string(workspace_bytes) + " < " +
                                         std::to_string(wneed) + " bytes");

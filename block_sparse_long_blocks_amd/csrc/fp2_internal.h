@@ -23,7 +23,9 @@ struct BatchInfo {
   int64_t total_qblocks = 0;
   int64_t total_kblocks = 0;
   int64_t max_kblocks = 0;
-  int64_t causal_pairs = 0;  // sum over query blocks of (diag + 1), one KV head
+  int64_t causal_pairs = 0;  // sum over query blocks of (last diagonal KV block + 1), one KV head
+  int qblock = 0;            // B: query block tokens
+  int kvblock = 0;           // KV block tokens (B, or 64 with B = 128)
 };
 
 // Sets the calling thread's error text and returns `st`.
@@ -35,10 +37,11 @@ fp2_status check_q(const fp2_q* q, int num_kv_heads, const BatchInfo& info, int 
 fp2_status check_kv(const fp2_kv* kv, const fp2_batch* b, const BatchInfo& info);
 
 size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads);
-// fp2_prefill_run runs the DMA kernel on V^T tiles for d = 128, B = 128
-// (bf16 or e4m3), and the register-staged kernel otherwise.
-inline bool vt_path(int dtype, int head_dim, int block) {
-  return (dtype == FP2_BF16 || dtype == FP2_FP8_E4M3) && head_dim == 128 && block == 128;
+// fp2_prefill_run runs the DMA kernel on V^T tiles for d = 128 and query and
+// KV blocks of 128 (bf16 or e4m3), and the register-staged kernel otherwise.
+inline bool vt_path(int dtype, int head_dim, const BatchInfo& info) {
+  return (dtype == FP2_BF16 || dtype == FP2_FP8_E4M3) && head_dim == 128 && info.qblock == 128 &&
+         info.kvblock == 128;
 }
 
 // Byte offsets of the parts of the fp2_prefill_run workspace.
@@ -56,8 +59,8 @@ struct RunLayout {
   size_t total = 0;
   int64_t mt_cap = 0;  // vbar^T tiles per KV head (V^T path)
 };
-RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int dtype,
-                     int block);
+RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                     int dtype);
 // Work items beyond one per CSR row that the d = 128, B = 128 path may create
 // by splitting the exact tiles of heavy rows (at most 256; fewer for small
 // batches), and the floats of one partial result (per slot, slice and wave:

@@ -34,8 +34,13 @@ fp2_status check_batch(const fp2_batch* b, BatchInfo* info) {
       return fail(FP2_ERR_INVALID, "batch host mirrors must not be NULL");
     if (b->h_cu_seqlens_q[0] != 0) return fail(FP2_ERR_INVALID, "cu_seqlens_q[0] must be 0");
   }
-  BatchInfo r;
   const int B = b->block;
+  const int KB = b->kv_block == 0 ? B : b->kv_block;
+  if (KB != B && !(B == 128 && KB == 64))
+    return fail(FP2_ERR_UNSUPPORTED, "kv_block must be 0, block, or 64 with block 128; got " + S(b->kv_block));
+  BatchInfo r;
+  r.qblock = B;
+  r.kvblock = KB;
   for (int s = 0; s < b->num_seqs; ++s) {
     const long long n = (long long)b->h_cu_seqlens_q[s + 1] - b->h_cu_seqlens_q[s];
     const long long T = b->h_seqlens_k[s];
@@ -49,13 +54,16 @@ fp2_status check_batch(const fp2_batch* b, BatchInfo* info) {
     if (P % B != 0)
       return fail(FP2_ERR_UNSUPPORTED, "sequence " + S(s) + ": cached prefix " + S(P) +
                                            " is not a multiple of block " + S(B));
-    const long long nqb = (n + B - 1) / B, nkb = (T + B - 1) / B;
+    const long long nqb = (n + B - 1) / B, nkb = (T + KB - 1) / KB;
     r.total_q += n;
     r.total_qblocks += nqb;
     r.total_kblocks += nkb;
     if (nkb > r.max_kblocks) r.max_kblocks = nkb;
-    // diag(I) = P/B + I  ->  sum_{I<nqb} (P/B + I + 1)
-    r.causal_pairs += nqb * (P / B) + nqb * (nqb + 1) / 2;
+    // the last diagonal KV block of query block I holds its last position:
+    // (P + B(I+1) - 1)/KB = P/KB + (B/KB)(I+1) - 1 for a full block, (P +
+    // n - 1)/KB for the last one; causal pairs = sum over I of that + 1
+    if (nqb > 0)
+      r.causal_pairs += (nqb - 1) * (P / KB) + (long long)(B / KB) * (nqb - 1) * nqb / 2 + (P + n - 1) / KB + 1;
   }
   if (r.max_kblocks > kMaxKBlocks)
     return fail(FP2_ERR_UNSUPPORTED, "a sequence has " + S(r.max_kblocks) +
@@ -103,10 +111,10 @@ fp2_status check_kv(const fp2_kv* kv, const fp2_batch* b, const BatchInfo& info)
   if (kv->page_size < 1) return fail(FP2_ERR_INVALID, "page_size < 1");
   if (kv->num_pages < 0 || kv->max_pages_per_seq < 0)
     return fail(FP2_ERR_INVALID, "negative page counts");
-  if (kv->dtype == FP2_FP8_E4M3 && kv->page_size != b->block)
+  if (kv->dtype == FP2_FP8_E4M3 && kv->page_size != info.kvblock)
     return fail(FP2_ERR_UNSUPPORTED, "e4m3 KV scales are per page: page_size (" +
-                                         S(kv->page_size) + ") must equal block (" +
-                                         S(b->block) + ")");
+                                         S(kv->page_size) + ") must equal the KV block (" +
+                                         S(info.kvblock) + ")");
   long long need_pages = 0;
   for (int s = 0; s < b->num_seqs; ++s) {
     const long long np = ((long long)b->h_seqlens_k[s] + kv->page_size - 1) / kv->page_size;
@@ -136,8 +144,8 @@ size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads) {
   return (bytes + 255) & ~size_t(255);
 }
 
-RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int dtype,
-                     int block) {
+RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                     int dtype) {
   auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
   RunLayout L;
   const size_t tkb = (size_t)info.total_kblocks, hkv = (size_t)num_kv_heads;
@@ -145,9 +153,10 @@ RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int n
   const size_t rows = up(hkv * tkb * (size_t)head_dim * 2);  // one bf16/fp16 copy of kbar or vbar
   L.k16 = 0;
   L.v16 = rows;
-  if (vt_path(dtype, head_dim, block)) {
-    const size_t tile = (size_t)block * (size_t)head_dim * 2;  // one 128 x 128 bf16 tile
-    L.mt_cap = (int64_t)(tkb / (size_t)block + (size_t)num_seqs + 1);
+  if (vt_path(dtype, head_dim, info)) {
+    const size_t block = (size_t)info.kvblock;
+    const size_t tile = block * (size_t)head_dim * 2;  // one 128 x 128 bf16 tile
+    L.mt_cap = (int64_t)(tkb / block + (size_t)num_seqs + 1);
     L.vt = L.v16 + hkv * (size_t)L.mt_cap * tile;
     L.total = L.vt + hkv * tkb * tile;
     if (dtype == FP2_FP8_E4M3) {
@@ -160,7 +169,7 @@ RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int n
     const size_t nrows = hkv * (size_t)info.total_qblocks;
     const int64_t causal_tiles = info.causal_pairs * (int64_t)num_kv_heads;
     L.extra_cap = std::min<int64_t>(kMaxExtraItems, (causal_tiles + 3) / 4);
-    const size_t slices = (size_t)((std::max(num_q_heads / std::max(num_kv_heads, 1), 1) * block + 255) / 256);
+    const size_t slices = (size_t)((std::max(num_q_heads / std::max(num_kv_heads, 1), 1) * (int)block + 255) / 256);
     L.items = L.total;
     L.splits = L.items + up((nrows + (size_t)L.extra_cap) * 16);
     L.rank_slot = L.splits + up((size_t)L.extra_cap * 16 + 16);

@@ -5,7 +5,9 @@
 // FlashPrefill V2 (metallab.ai paper page): Figure 3 (pack queries with
 // PackGQA, pool block means, CSR index of selected blocks), the abstract
 // ("instantaneous pattern discovery and max-based dynamic thresholding") and
-// Table 7 (CSR per KV head).  Block 0 and the diagonal block are always kept.
+// Table 7 (CSR per KV head).  Block 0 and the diagonal block are always kept
+// (with 64-token KV blocks under 128-token query blocks, Table 7's pairing,
+// the diagonal is the run of KV blocks holding the query block's positions).
 //
 // Three launches, no host synchronisation:
 //   score_select : one workgroup per CSR row (query block I, KV head g).
@@ -39,7 +41,8 @@ struct PlanArgs {
   int32_t* counts;      // [rows]
   float* scores_out;    // optional [rows, max_kblocks]
   float tau, scale;
-  int num_seqs, hq, hkv, d, block, total_qblocks, total_kblocks, W, max_kblocks;
+  int num_seqs, hq, hkv, d, total_qblocks, total_kblocks, W, max_kblocks;
+  int qblock, kvblock;  // query block and KV block tokens (kvblock divides qblock)
 };
 
 template <int ESZ>
@@ -79,8 +82,10 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
   const int n = a.cu_seqlens_q[s + 1] - q0;
   const int T = a.seqlens_k[s];
   const int P = T - n;
-  const int diag = P / a.block + I;
-  const int ntok = min(a.block, n - I * a.block);
+  const int ntok = min(a.qblock, n - I * a.qblock);
+  // the diagonal: the KV blocks holding one of the query block's positions
+  const int dlo = (P + I * a.qblock) / a.kvblock;
+  const int diag = (P + I * a.qblock + ntok - 1) / a.kvblock;  // the last causal KV block
   const int G = a.hq / a.hkv;
 
   // ---- pool qbar over ntok tokens x G heads (the group's heads are adjacent)
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
     const int h = g * G + elem0 / a.d;  // a chunk stays within one head
     float mul = 1.f;
     if (ESZ == 1) mul = a.q_scale[(int64_t)qb * a.hq + h];
-    const uint8_t* base = a.q + ((int64_t)(q0 + I * a.block) * a.hq + g * G) * a.d * ESZ + c * 16;
+    const uint8_t* base = a.q + ((int64_t)(q0 + I * a.qblock) * a.hq + g * G) * a.d * ESZ + c * 16;
     const int64_t tok_stride = (int64_t)a.hq * a.d * ESZ;
     constexpr int U = 8;
     int tok = r;
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
   for (int w = 1; w < kThreads / 64; ++w) rmax = fmaxf(rmax, s_wmax[w]);
   const float thr = rmax - a.tau;
 
-  // ---- keep bitmask (forced: block 0 and the diagonal) and kept count
+  // ---- keep bitmask (forced: block 0 and the diagonal run) and kept count
   const int row = g * a.total_qblocks + qb;
   int cnt = 0;
   for (int w = t; w < a.W; w += kThreads) {
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
     const int j0 = w * 32;
     for (int b = 0; b < 32; ++b) {
       const int J = j0 + b;
-      if (J <= diag && (s_scores[J] >= thr || J == 0 || J == diag)) word |= 1u << b;
+      if (J <= diag && (s_scores[J] >= thr || J == 0 || J >= dlo)) word |= 1u << b;
     }
     a.bits[(int64_t)row * a.W + w] = word;
     cnt += __popc(word);
@@ -300,7 +305,8 @@ hipError_t launch_plan(const fp2_batch* b, const fp2_q* q, int hkv, const BatchI
   a.hq = q->num_q_heads;
   a.hkv = hkv;
   a.d = q->head_dim;
-  a.block = b->block;
+  a.qblock = info.qblock;
+  a.kvblock = info.kvblock;
   a.total_qblocks = (int)info.total_qblocks;
   a.total_kblocks = (int)info.total_kblocks;
   a.W = W;

@@ -275,12 +275,14 @@ struct WaveState {
     }
   }
 
-  // MODE 0: exact block (causal mask when diagonal); MODE 1: mean-token tile
-  // scl: logit scale to log2 units; pscale multiplies the probabilities fed
-  // to PV (fp8 v_scale), not the denominator.
+  // MODE 0: exact block (on the diagonal, keys k > qoff are masked: qoff is
+  // the query's position minus the block's first key position); MODE 1:
+  // mean-token tile of tokens J0.., those of skipped blocks in [1, jend)
+  // count.  scl: logit scale to log2 units; pscale multiplies the
+  // probabilities fed to PV (fp8 v_scale), not the denominator.
   template <int MODE>
   __device__ __forceinline__ void tile(const uint8_t* Kl, const uint16_t* Vt, int lane, float scl,
-                                       float pscale, bool diagonal, int tq, int J0, int diag,
+                                       float pscale, bool diagonal, int qoff, int J0, int jend,
                                        const uint32_t* kept, float bias) {
     const int c = lane & 31, hf = lane >> 5;
 #pragma nounroll
@@ -296,10 +298,10 @@ struct WaveState {
           const int k = 64 * sub + 32 * st + 8 * (i >> 2) + 4 * hf + (i & 3);
           float x = s[st][i] * scl;
           if (MODE == 0) {
-            if (diagonal && k > tq) x = -INFINITY;
+            if (diagonal && k > qoff) x = -INFINITY;
           } else {
             const int j = J0 + k;
-            const bool skipped = j >= 1 && j < diag && !((kept[j >> 5] >> (j & 31)) & 1u);
+            const bool skipped = j >= 1 && j < jend && !((kept[j >> 5] >> (j & 31)) & 1u);
             x = skipped ? x + bias : -INFINITY;
           }
           s[st][i] = x;
@@ -379,7 +381,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const int n = a.cu_seqlens_q[s + 1] - q0;
   const int T = a.seqlens_k[s];
   const int P = T - n;
-  const int diag = P / BLK + I;
+  const int QB = a.qblk;  // query block tokens: BLK, or 2 BLK (128-token query blocks over 64-token KV blocks)
+  // the diagonal: KV blocks dlo..dhi hold the query block's own positions
+  // (a single block when the query and KV blocks have one size)
+  const int qpos0 = P + I * QB;  // absolute position of the block's first query
+  const int dlo = qpos0 / BLK;
+  const int dhi = (qpos0 + min(QB, n - I * QB) - 1) / BLK;
   const int G = a.hq / a.hkv;
   const int32_t* pt = a.page_table + (int64_t)s * a.max_pages;
   const int64_t mrow0 = (int64_t)g * a.total_kblocks + a.cu_kblocks[s];
@@ -389,17 +396,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const int wave = t >> 6;
   const int hf = lane >> 5;
   const int prow = slice * kRowsPerWG + wave * 32;  // first packed row of this wave
-  const bool wave_active = prow < G * BLK;
-  const int h = g * G + prow / BLK;                 // query head of this wave
-  const int t0 = prow % BLK;                        // first token (within the block)
+  const bool wave_active = prow < G * QB;
+  const int h = g * G + prow / QB;                  // query head of this wave
+  const int t0 = prow % QB;                         // first token (within the block)
   const int tq = t0 + (lane & 31);                  // this lane's query token
-  const bool q_valid = wave_active && (I * BLK + tq < n);
+  const bool q_valid = wave_active && (I * QB + tq < n);
 
   const int kbeg = a.row_ptr[row], kend = a.row_ptr[row + 1];
 
   // kept-block bitmask for the correction tiles
   if (a.correction) {
-    const int nw = (diag + 32) >> 5;
+    const int nw = (dhi + 32) >> 5;
     for (int w = t; w < nw; w += kThreads) kept[w] = 0u;
     __syncthreads();
     for (int i = kbeg + t; i < kend; i += kThreads) {
@@ -415,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   for (int dt = 0; dt < TL::DT; ++dt) ws.o[dt] = f32x16{};
   float qscale = 1.f;
   {
-    const uint8_t* qrow = a.q + ((int64_t)(q0 + I * BLK + tq) * a.hq + h) * (D * TL::ESZ);
+    const uint8_t* qrow = a.q + ((int64_t)(q0 + I * QB + tq) * a.hq + h) * (D * TL::ESZ);
     if constexpr (!FP8) {
 #pragma unroll
       for (int kk = 0; kk < TL::KK; ++kk) {
@@ -454,12 +461,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     stg.commit_block(Kl, Vt, t);
     __syncthreads();
     if (i + 1 < kend) stg.load_block(a, pt, g, T, a.col_idx[i + 1], t);
+    // on the diagonal, keys past the query's own position are masked: its
+    // offset from the block's first key
     if (wave_active)
-      ws.template tile<0>(Kl, Vt, lane, scl, pscale, J == diag, tq, 0, diag, kept, 0.f);
+      ws.template tile<0>(Kl, Vt, lane, scl, pscale, J >= dlo, qpos0 + tq - J * BLK, 0, dlo, kept, 0.f);
   }
 
-  // ---- mean correction: tiles of BLK mean tokens over [1, diag)
-  if (a.correction && diag > 1) {
+  // ---- mean correction: tiles of BLK mean tokens over [1, dlo)
+  if (a.correction && dlo > 1) {
     if constexpr (FP8) {
       // bf16 copy of the e4m3 query codes (exact); its scale goes into the logit scale
 #pragma unroll
@@ -475,23 +484,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     }
     const float scl_mean = a.scale_log2 * qscale;
     auto has_skipped = [&](int J0) {
-      const int lo = max(1, J0), hi = min(J0 + BLK, diag);
+      const int lo = max(1, J0), hi = min(J0 + BLK, dlo);
       int nk = 0;
       for (int j = lo; j < hi; ++j) nk += (kept[j >> 5] >> (j & 31)) & 1u;
       return hi - lo - nk > 0;
     };
     int J0 = 0;
-    while (J0 < diag && !has_skipped(J0)) J0 += BLK;
-    if (J0 < diag) stg.load_means(a, mrow0, J0, diag, t);
-    while (J0 < diag) {
+    while (J0 < dlo && !has_skipped(J0)) J0 += BLK;
+    if (J0 < dlo) stg.load_means(a, mrow0, J0, dlo, t);
+    while (J0 < dlo) {
       int Jn = J0 + BLK;
-      while (Jn < diag && !has_skipped(Jn)) Jn += BLK;
+      while (Jn < dlo && !has_skipped(Jn)) Jn += BLK;
       __syncthreads();
       stg.commit_means(Kl, Vt, t);
       __syncthreads();
-      if (Jn < diag) stg.load_means(a, mrow0, Jn, diag, t);
+      if (Jn < dlo) stg.load_means(a, mrow0, Jn, dlo, t);
       if (wave_active)
-        ws.template tile<1>(Kl, Vt, lane, scl_mean, 1.f, false, tq, J0, diag, kept, a.log2_block);
+        ws.template tile<1>(Kl, Vt, lane, scl_mean, 1.f, false, tq, J0, dlo, kept, a.log2_block);
       J0 = Jn;
     }
   }
@@ -500,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   if (q_valid) {
     const float lt = ws.l + swap_halves(ws.l);
     const float inv = 1.0f / lt;
-    const int64_t obase = ((int64_t)(q0 + I * BLK + tq) * a.hq + h) * D;
+    const int64_t obase = ((int64_t)(q0 + I * QB + tq) * a.hq + h) * D;
     if (a.out_f32) {
       float* orow = static_cast<float*>(a.out) + obase;
 #pragma unroll
@@ -565,9 +574,9 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
                           const float* vbar, int correction, float softmax_scale, int out_f32,
                           void* out, void* workspace, hipStream_t stream) {
   if (info.total_qblocks == 0) return hipSuccess;
-  const int D = q->head_dim, BLK = b->block, hkv = kv->num_kv_heads;
-  const bool vt = vt_path(q->dtype, D, BLK);
-  const RunLayout L = run_layout(info, b->num_seqs, q->num_q_heads, hkv, D, q->dtype, BLK);
+  const int D = q->head_dim, BLK = info.kvblock, QB = info.qblock, hkv = kv->num_kv_heads;
+  const bool vt = vt_path(q->dtype, D, info);
+  const RunLayout L = run_layout(info, b->num_seqs, q->num_q_heads, hkv, D, q->dtype);
   uint8_t* wsb = static_cast<uint8_t*>(workspace);
   uint16_t* k16 = reinterpret_cast<uint16_t*>(wsb + L.k16);
   uint16_t* v16 = reinterpret_cast<uint16_t*>(wsb + L.v16);
@@ -625,8 +634,9 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.total_qblocks = (int)info.total_qblocks;
   a.total_kblocks = (int)info.total_kblocks;
   a.correction = correction;
+  a.qblk = QB;
   const int G = q->num_q_heads / hkv;
-  a.slices = (G * BLK + kRowsPerWG - 1) / kRowsPerWG;
+  a.slices = (G * QB + kRowsPerWG - 1) / kRowsPerWG;
   a.rows = (int)(info.total_qblocks * hkv);
   const unsigned grid = (unsigned)(((a.rows + 7) / 8) * 8 * a.slices);
   if (vt) return launch_attn_d128(a, q->dtype == FP2_FP8_E4M3, kbar, vbar, (int)info.max_kblocks, stream);

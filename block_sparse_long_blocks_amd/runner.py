@@ -56,9 +56,9 @@ class PrefillLayer:
 
 
 def from_arrays(block: int, seqlens_k, n_q, q, q_scale, k_pages, v_pages, page_table,
-                k_scale=None, v_scale=None, device: str = "cuda"):
+                k_scale=None, v_scale=None, device: str = "cuda", kv_block: int = 0):
     """Device descriptors from host arrays (numpy): bf16 data as uint16 bit patterns,
-    e4m3 data as uint8 codes with float32 scales."""
+    e4m3 data as uint8 codes with float32 scales; kv_block 0 = block."""
     def dev_codes(x):
         t = torch.from_numpy(np.ascontiguousarray(x))
         if x.dtype == np.uint16:
@@ -68,7 +68,7 @@ def from_arrays(block: int, seqlens_k, n_q, q, q_scale, k_pages, v_pages, page_t
     def dev_f32(x):
         return None if x is None else torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
 
-    batch = Batch(block, [int(t) for t in seqlens_k], [int(n) for n in n_q], device)
+    batch = Batch(block, [int(t) for t in seqlens_k], [int(n) for n in n_q], device, kv_block)
     queries = Queries(dev_codes(q), dev_f32(q_scale))
     kv = KVCache(dev_codes(k_pages), dev_codes(v_pages),
                  torch.from_numpy(np.ascontiguousarray(page_table, dtype=np.int32)).to(device),
@@ -79,4 +79,4 @@ def from_arrays(block: int, seqlens_k, n_q, q, q_scale, k_pages, v_pages, page_t
 def from_workload(w, device: str = "cuda"):
     """Device descriptors of a generated workload (anything with the attribute names below)."""
     return from_arrays(w.cfg.block, w.seqlens_k, w.n_q, w.q, w.q_scale, w.k_pages, w.v_pages, w.page_table,
-                       w.k_scale, w.v_scale, device)
+                       w.k_scale, w.v_scale, device, getattr(w.cfg, "kv_block", 0) or 0)

@@ -26,6 +26,14 @@
  *                   the numerator.
  *   diag(I) = P/B + I for a sequence with a cached prefix of P tokens.
  *
+ * Decoupled tiles (fp2_batch.kv_block = 64 with block = 128): query blocks
+ * of 128 tokens are scored against KV blocks of 64 tokens, the pairing
+ * Table 7 describes (its CSR index holds selected 64-token tiles).  kbar,
+ * vbar and the CSR columns then count 64-token blocks, the diagonal of
+ * query block I is the run of KV blocks holding one of its positions
+ * (two, or one for a short last block), all of it forced, and the surrogate
+ * covers the skipped J before that run with weight 64.
+ *
  * Conventions for every entry point:
  *  - All device buffers are allocated and owned by the caller.  The library
  *    never allocates, frees or synchronises; it only enqueues kernels on the
@@ -67,9 +75,10 @@ typedef enum { FP2_OUT_BF16 = 0, FP2_OUT_F32 = 1 } fp2_out_dtype;
  * holds seqlens_k[s] key tokens, of which the last n_s =
  * cu_seqlens_q[s+1]-cu_seqlens_q[s] are new queries; the first
  * P_s = seqlens_k[s]-n_s are a cached prefix (P_s must be a multiple of
- * block).  Query blocks and KV blocks are counted per sequence:
+ * block).  Query blocks and KV blocks are counted per sequence, with
+ * KB = kv_block (or block when kv_block is 0):
  * cu_qblocks[s+1]-cu_qblocks[s] = ceil(n_s/block),
- * cu_kblocks[s+1]-cu_kblocks[s] = ceil(seqlens_k[s]/block).
+ * cu_kblocks[s+1]-cu_kblocks[s] = ceil(seqlens_k[s]/KB).
  * The device arrays and the host mirrors must hold the same values. */
 typedef struct {
   int32_t num_seqs;              /* >= 0                                         */
@@ -80,6 +89,8 @@ typedef struct {
   const int32_t *cu_kblocks;     /* device [num_seqs+1]                          */
   const int32_t *h_cu_seqlens_q; /* host mirror of cu_seqlens_q                  */
   const int32_t *h_seqlens_k;    /* host mirror of seqlens_k                     */
+  int32_t kv_block;              /* KV block size: 0 (= block), block, or 64 with
+                                    block 128 (decoupled tiles, see above)       */
 } fp2_batch;
 
 /* Queries of the new tokens, packed over the batch: [total_q, Hq, d]. */
@@ -98,7 +109,7 @@ typedef struct {
   fp2_dtype dtype;               /* must equal the query dtype                   */
   int32_t num_kv_heads;          /* Hkv                                          */
   int32_t head_dim;              /* d, equal to the query head_dim               */
-  int32_t page_size;             /* any size >= 1; e4m3 requires page_size == B  */
+  int32_t page_size;             /* any size >= 1; e4m3 requires page_size == KB */
   int32_t num_pages;
   int32_t max_pages_per_seq;     /* >= ceil(seqlens_k[s]/page_size) for every s  */
   const void *k_pages;           /* device [num_pages, page_size, Hkv, d]        */
@@ -111,7 +122,8 @@ typedef struct {
 /* Stage 1a - per-block key/value means (Figure 4's pooled statistics).
  * kbar, vbar: device float32 [Hkv, total_kblocks, d]; entry
  * [g, cu_kblocks[s]+J, :] is the mean of K (V) over the valid tokens of
- * block J of sequence s, head g (e4m3 values times their page scale). */
+ * KV block J (KB tokens) of sequence s, head g (e4m3 values times their
+ * page scale). */
 fp2_status fp2_block_stats(const fp2_batch *batch, const fp2_kv *kv,
                            float *kbar, float *vbar, void *stream);
 
@@ -121,14 +133,15 @@ fp2_status fp2_block_stats(const fp2_batch *batch, const fp2_kv *kv,
  * prefix are kept; this cache is the library's own design: the means of a
  * block whose tokens are all in the cached prefix do not change between
  * calls, so only the blocks holding new tokens are read again.  The cache has one row per KV block a page holds:
- * fp2_block_stats_cache_rows() = num_pages * max(1, page_size / B) rows
- * (0 when page_size and B do not divide one another: unsupported).  Block J
- * of sequence s lives in row page_table[s][J*B/page_size] * max(1,
- * page_size/B) + J % max(1, page_size/B).
+ * fp2_block_stats_cache_rows() = num_pages * max(1, page_size / KB) rows
+ * (0 when page_size and the KV block KB do not divide one another:
+ * unsupported).  Block J of sequence s lives in row
+ * page_table[s][J*KB/page_size] * max(1, page_size/KB) + J % max(1,
+ * page_size/KB).
  *   kbar_cache, vbar_cache  device float32 [cache_rows, Hkv, d], owned by the
  *                   caller alongside its KV pages
  *   refresh_prefix  1: compute every block of the batch; 0: only blocks
- *                   J >= prefix/B (their rows are overwritten), the rows of
+ *                   J >= prefix/KB (their rows are overwritten), the rows of
  *                   prefix blocks are used as an earlier call left them
  * The values are bit for bit those of fp2_block_stats. */
 int64_t fp2_block_stats_cache_rows(const fp2_batch *batch, const fp2_kv *kv);
@@ -160,7 +173,7 @@ int64_t fp2_plan_max_nnz(const fp2_batch *batch, int32_t num_kv_heads);
  *              sequence, ascending within each row
  *   nnz        device int32 [1]: number of entries written
  *   scores     optional device float32 [Hkv*total_qblocks, max_kblocks]
- *              (max_kblocks = largest ceil(seqlens_k/B)): the float32 block
+ *              (max_kblocks = largest ceil(seqlens_k/KB)): the float32 block
  *              scores, -INFINITY above the diagonal; NULL to skip
  *   workspace  device scratch of fp2_plan_workspace_bytes() bytes */
 fp2_status fp2_plan_mask(const fp2_batch *batch, const fp2_q *q, int32_t num_kv_heads,
@@ -170,7 +183,7 @@ fp2_status fp2_plan_mask(const fp2_batch *batch, const fp2_q *q, int32_t num_kv_
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes fp2_prefill_run needs for this batch, head size and KV
- * dtype (0 if the batch is empty or malformed).  For d = 128 and B = 128 it
+ * dtype (0 if the batch is empty or malformed).  For d = 128 and B = KB = 128 it
  * holds V^T tiles of every KV block (one bf16 128 x 128 tile per block and
  * KV head, e4m3 V dequantized: about the size of bf16 V), bf16 kbar rows and
  * vbar^T tiles of the mean tokens, for e4m3 also the K codes of every
@@ -194,10 +207,10 @@ size_t fp2_run_workspace_bytes(const fp2_batch *batch, int32_t num_q_heads, int3
  *   out_dtype         FP2_OUT_BF16 (rounded to nearest even) or FP2_OUT_F32
  *   out               device [total_q, Hq, d] of out_dtype
  *   workspace         device scratch of fp2_run_workspace_bytes() bytes;
- *                     required with d = 128 and B = 128 (bf16 or e4m3),
+ *                     required with d = 128 and B = KB = 128 (bf16 or e4m3),
  *                     else only with mean_correction (FP2_ERR_CAPACITY if
  *                     too small); its contents are overwritten
- * With d = 128 and B = 128 the rows run as work items launched heaviest
+ * With d = 128 and B = KB = 128 the rows run as work items launched heaviest
  * first; the exact tiles of a row heavier than a quarter of a CU's share
  * of the batch are cut into chunks whose float32 partials a second kernel
  * merges (at most 256 extra items).  The environment variable

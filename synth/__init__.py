@@ -117,7 +117,7 @@ class Config:
     hq: int
     hkv: int
     d: int
-    block: int                    # B: query and key block size
+    block: int                    # B: query block size (and KV block size unless kv_block is set)
     page_size: int
     dtype: str                    # "bf16" or "fp8"
     structure: str                # "hot", "band_sinks", "slash" or "plain"
@@ -128,6 +128,7 @@ class Config:
     seq_seeds: Optional[Tuple[int, ...]] = None   # one seed per request (varlen batch)
     shuffle_seed: int = 4999
     description: str = ""
+    kv_block: int = 0             # KV block size; 0: the same as block
 
 
 _QWEN_T = (4096, 8192, 16384, 16384, 32768, 32768, 65536, 8192)
@@ -311,14 +312,15 @@ class Workload:
         return self.q_scale[self.cu_qblocks[s]:self.cu_qblocks[s + 1]]
 
     def causal_pairs(self) -> int:
-        """Number of (q-block, k-block <= diagonal, KV head) triples."""
+        """Number of (q-block, k-block <= last diagonal k-block, KV head) triples."""
         B = self.cfg.block
+        KB = self.cfg.kv_block or B
         tot = 0
         for s in range(self.num_seqs):
-            P = int(self.seqlens_k[s] - self.n_q[s])
-            nqb = -(-int(self.n_q[s]) // B)
-            for i in range(nqb):
-                tot += P // B + i + 1
+            n = int(self.n_q[s])
+            P = int(self.seqlens_k[s]) - n
+            for i in range(-(-n // B)):
+                tot += (P + min((i + 1) * B, n) - 1) // KB + 1
         return tot * self.cfg.hkv
 
 
@@ -339,6 +341,7 @@ def make_custom(cfg: Config, tau: Optional[float] = None, pad_fill: str = "zero"
         seq_seeds = cfg.seq_seeds if cfg.seq_seeds is not None else \
             tuple(cfg.seed + 1000 * r for r in range(S))
     B, ps = cfg.block, cfg.page_size
+    KB = cfg.kv_block or B
     seqlens = np.array(cfg.seqlens, dtype=np.int32)
     n_q = np.array([T - P for T, P in zip(cfg.seqlens, cfg.prefixes)], dtype=np.int32)
     cu_q = np.zeros(S + 1, dtype=np.int32)
@@ -346,12 +349,12 @@ def make_custom(cfg: Config, tau: Optional[float] = None, pad_fill: str = "zero"
     cu_qb = np.zeros(S + 1, dtype=np.int32)
     cu_qb[1:] = np.cumsum([_cdiv(int(n), B) for n in n_q])
     cu_kb = np.zeros(S + 1, dtype=np.int32)
-    cu_kb[1:] = np.cumsum([_cdiv(int(t), B) for t in seqlens])
+    cu_kb[1:] = np.cumsum([_cdiv(int(t), KB) for t in seqlens])
     total_q = int(cu_q[-1])
 
     fp8 = cfg.dtype == "fp8"
-    if fp8 and ps != B:
-        raise ValueError("fp8 KV scales are per page and need page_size == block")
+    if fp8 and ps != KB:
+        raise ValueError("fp8 KV scales are per page and need page_size == the KV block")
     code_t = np.uint8 if fp8 else np.uint16
     q = np.empty((total_q, cfg.hq, cfg.d), dtype=code_t)
     q_scale = np.empty((int(cu_qb[-1]), cfg.hq), dtype=np.float32) if fp8 else None
@@ -366,8 +369,8 @@ def make_custom(cfg: Config, tau: Optional[float] = None, pad_fill: str = "zero"
             qc, qs = quantize_blocks_e4m3(Qn, B)
             q[cu_q[s]:cu_q[s + 1]] = qc
             q_scale[cu_qb[s]:cu_qb[s + 1]] = qs
-            kc, kss = quantize_blocks_e4m3(Kf, B)
-            vc, vss = quantize_blocks_e4m3(Vf, B)
+            kc, kss = quantize_blocks_e4m3(Kf, KB)
+            vc, vss = quantize_blocks_e4m3(Vf, KB)
         else:
             q[cu_q[s]:cu_q[s + 1]] = f32_to_bf16_bits(Qn)
             kc, kss = f32_to_bf16_bits(Kf), None

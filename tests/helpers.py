@@ -8,15 +8,20 @@ import oracle as O
 def decoded_seqs(w):
     cfg = w.cfg
     return [O.decode_sequence(cfg.dtype, cfg.block, w.q_seq(s), w.q_scale_seq(s), w.k_seq[s],
-                              w.k_scale_seq[s], w.v_seq[s], w.v_scale_seq[s])
+                              w.k_scale_seq[s], w.v_seq[s], w.v_scale_seq[s], kv_block=cfg.kv_block or None)
             for s in range(w.num_seqs)]
+
+
+def kv_block(w):
+    """KV block tokens of a workload (its query block unless set apart)."""
+    return w.cfg.kv_block or w.cfg.block
 
 
 def stats_bound(w, seqs):
     """Per-element bound on |float32 block mean - exact mean|: a float32 sum of n
     terms errs by at most (n-1)*2^-24*sum|x| (any order), the scale product and
     the division add 2^-24 each, relative."""
-    B = w.cfg.block
+    B = kv_block(w)
     ks, vs = [], []
     for (_, K, V) in seqs:
         T = K.shape[0]
@@ -64,6 +69,7 @@ def compare_csr(gpu_rp, gpu_ci, plan, w):
 def csr_well_formed(rp, ci, w):
     B = w.cfg.block
     Hkv = w.cfg.hkv
+    KB = kv_block(w)
     total_qb = w.total_qblocks
     assert rp[0] == 0 and np.all(np.diff(rp) > 0)
     for g in range(Hkv):
@@ -72,4 +78,6 @@ def csr_well_formed(rp, ci, w):
             for i in range(int(w.cu_qblocks[s + 1] - w.cu_qblocks[s])):
                 r = g * total_qb + int(w.cu_qblocks[s]) + i
                 row = ci[rp[r]:rp[r + 1]]
-                assert row[0] == 0 and row[-1] == P // B + i and np.all(np.diff(row) > 0), (g, s, i)
+                lo, hi = O.diag_range(P, int(w.n_q[s]), i, B, KB)
+                assert row[0] == 0 and row[-1] == hi and np.all(np.diff(row) > 0), (g, s, i)
+                assert set(range(lo, hi + 1)) <= set(row.tolist()), (g, s, i)

@@ -27,8 +27,8 @@ def test_exports_every_declared_function():
         assert hasattr(so, n), n
 
 
-def _batch(seqlens, nq, block=128):
-    return lib.Batch(block, seqlens, nq, device="cpu")
+def _batch(seqlens, nq, block=128, kv_block=0):
+    return lib.Batch(block, seqlens, nq, device="cpu", kv_block=kv_block)
 
 
 def _kv(hkv=2, d=128, page=128, pages=4, dtype=torch.bfloat16, maxp=4):
@@ -67,6 +67,42 @@ def test_sizes_and_counts():
     # other head sizes: bf16 kbar + fp16 vbar copies only
     assert lib.fp2_run_workspace_bytes(b, 12, 3, 64, lib.FP2_BF16) < tiles
     assert lib.fp2_run_workspace_bytes(b, 12, 3, 64, lib.FP2_FP8_E4M3) >= 2 * 3 * (8 + 2) * 64 * 2
+
+
+def test_decoupled_blocks_sizes_and_counts():
+    """128-token query blocks over 64-token KV blocks: the causal count is that of the blocks
+    holding a visible key (counted here from positions), the register-staged layout is used."""
+    seqlens, nq = [1000, 300, 256], [1000, 172, 128]
+    b = _batch(seqlens, nq, 128, 64)
+    want = 0
+    for T, n in zip(seqlens, nq):
+        P = T - n
+        for i in range(-(-n // 128)):
+            last = P + min(128 * (i + 1), n) - 1          # the query block's last position
+            want += len([J for J in range(-(-T // 64)) if 64 * J <= last])
+    assert lib.fp2_plan_max_nnz(b, 2) == 2 * want
+    # same batch with one block size: the same positions at 128-token granularity
+    assert lib.fp2_plan_max_nnz(_batch(seqlens, nq), 2) < 2 * want
+    assert lib.fp2_plan_max_nnz(_batch(seqlens, nq, 128, 128), 2) == lib.fp2_plan_max_nnz(_batch(seqlens, nq), 2)
+    # no V^T tiles: bf16 kbar and fp16 vbar copies of the 64-token block means only
+    nkb = sum(-(-T // 64) for T in seqlens)
+    assert lib.fp2_run_workspace_bytes(b, 8, 2, 128, lib.FP2_BF16) < 2 * 2 * nkb * 128 * 2 + 1024
+    # one block-stats cache row per 64-token block a page holds
+    assert lib.fp2_block_stats_cache_rows(_batch([256], [256], 128, 64), _kv(page=128)) == 8
+    assert lib.fp2_block_stats_cache_rows(_batch([256], [256], 128, 64), _kv(page=32, pages=8, maxp=8)) == 8
+    f32 = torch.zeros(16)
+    for B, KB in ((128, 32), (64, 128), (64, 32), (128, 96)):
+        _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_block_stats, _batch([256], [256], B, KB), _kv(), f32, f32,
+                match="kv_block")
+    # e4m3 scales are per page: the page must be the 64-token KV block
+    kv8 = lib.KVCache(torch.zeros((4, 128, 2, 128), dtype=torch.uint8),
+                      torch.zeros((4, 128, 2, 128), dtype=torch.uint8),
+                      torch.zeros((1, 4), dtype=torch.int32), f32, f32)
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_block_stats, _batch([256], [256], 128, 64), kv8, f32, f32,
+            match="KV block")
+    # the prefix is still a multiple of the query block
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_block_stats, _batch([320], [256], 128, 64), _kv(), f32, f32,
+            match="prefix")
 
 
 def test_sequence_length_limits():

@@ -13,7 +13,7 @@ import pytest
 
 import oracle as O
 import synth
-from helpers import compare_csr, csr_well_formed, decoded_seqs, stats_bound
+from helpers import compare_csr, csr_well_formed, decoded_seqs, kv_block, stats_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -41,10 +41,10 @@ def check_out(got, ref, tol, out_dtype, extra=0.0):
 
 
 def _cfg(name, seqlens, prefixes, hq, hkv, d, B, page, dtype="bf16", structure="band_sinks",
-         shuffle=True, seed=11):
+         shuffle=True, seed=11, kv_block=0):
     return synth.Config(name=name, seqlens=tuple(seqlens), prefixes=tuple(prefixes), hq=hq, hkv=hkv, d=d,
                         block=B, page_size=page, dtype=dtype, structure=structure, tau=1.0, seed=seed,
-                        shuffle_pages=shuffle)
+                        shuffle_pages=shuffle, kv_block=kv_block)
 
 
 SMALL = {
@@ -65,11 +65,19 @@ SMALL = {
                                    dtype="fp8"),
     # pages that hold two blocks each (B = 64, page 128)
     "d128_b64_p128": _cfg("d128_b64_p128", (700, 300), (256, 0), 8, 2, 128, 64, 128),
+    # 128-token query blocks over 64-token KV blocks: ragged last query blocks whose diagonal is one
+    # KV block (44 and 60 tokens), prefixes, shuffled pages smaller than, equal to and larger than
+    # the KV block, e4m3 (page = KV block), d = 64 and eight query heads per KV head
+    "dec_varlen": _cfg("dec_varlen", (640, 300, 1152), (256, 0, 896), 8, 2, 128, 128, 32, kv_block=64),
+    "dec_fp8": _cfg("dec_fp8", (1024, 512), (0, 256), 8, 2, 128, 128, 64, dtype="fp8", kv_block=64),
+    "dec_d64_p128": _cfg("dec_d64_p128", (512, 384), (128, 256), 8, 4, 64, 128, 128, kv_block=64),
+    "dec_g8": _cfg("dec_g8", (700,), (384,), 16, 2, 128, 128, 64, kv_block=64),
 }
 TAUS = {"tiny": (0.0, 0.005, 0.01, 0.02, 2.0), "varlen_p64": (0.0, 0.5, 3.0),
         "d64_b128_p16": (0.3, 3.0), "d128_b64_g8": (0.2, 2.0), "single_token": (0.0, 1.0),
         "fp8_varlen": (0.0, 0.5, 3.0), "d128_p24_g1": (0.0, 1.0), "d128_p8_g8": (0.0, 1.0),
-        "chunk_after_prefix": (0.5, 1e9), "chunk_after_prefix_fp8": (0.5, 1e9), "d128_b64_p128": (0.0, 1.0)}
+        "chunk_after_prefix": (0.5, 1e9), "chunk_after_prefix_fp8": (0.5, 1e9), "d128_b64_p128": (0.0, 1.0),
+        "dec_varlen": (0.0, 0.5, 3.0), "dec_fp8": (0.0, 0.5, 3.0), "dec_d64_p128": (0.3, 3.0), "dec_g8": (0.0, 1.0)}
 
 _cache = {}
 
@@ -94,7 +102,7 @@ def test_block_stats_parity(name):
     L = layer(w)
     L.stats()
     torch.cuda.synchronize()
-    plan = O.plan_batch(seqs, w.cfg.block, 1.0)
+    plan = O.plan_batch(seqs, w.cfg.block, 1.0, BK=kv_block(w))
     kb_bound, vb_bound = stats_bound(w, seqs)
     kb = L.kbar.cpu().numpy().astype(np.float64)
     vb = L.vbar.cpu().numpy().astype(np.float64)
@@ -111,7 +119,7 @@ def test_plan_parity(name):
         L.plan(tau)
         torch.cuda.synchronize()
         rp, ci = L.csr_host()
-        plan = O.plan_batch(seqs, w.cfg.block, tau)
+        plan = O.plan_batch(seqs, w.cfg.block, tau, BK=kv_block(w))
         csr_well_formed(rp, ci, w)
         rows_bad, flips, ties, hard = compare_csr(rp, ci, plan, w)
         assert hard == 0, f"tau={tau}: {hard} mask flips outside near-ties ({flips} flips, {ties} ties)"
@@ -129,11 +137,12 @@ def test_plan_parity(name):
             off += nqb
         if tau == math.inf:
             assert rp[-1] == w.causal_pairs()
-        if tau == -1.0:
-            assert rp[-1] == sum(min(2, P // w.cfg.block + i + 1)
+        if tau == -1.0:  # only the forced blocks: block 0 and the diagonal run
+            assert rp[-1] == sum(len({0} | set(range(lo, hi + 1)))
                                  for s in range(w.num_seqs)
-                                 for P in [int(w.seqlens_k[s] - w.n_q[s])]
-                                 for i in range(int(w.cu_qblocks[s + 1] - w.cu_qblocks[s]))) * w.cfg.hkv
+                                 for i in range(int(w.cu_qblocks[s + 1] - w.cu_qblocks[s]))
+                                 for lo, hi in [O.diag_range(int(w.seqlens_k[s] - w.n_q[s]), int(w.n_q[s]), i,
+                                                             w.cfg.block, kv_block(w))]) * w.cfg.hkv
 
 
 def _attention_case(name, tau, corr, pad_fill="zero", out_dtype="bf16"):
@@ -143,9 +152,9 @@ def _attention_case(name, tau, corr, pad_fill="zero", out_dtype="bf16"):
     torch.cuda.synchronize()
     rp, ci = L.csr_host()
     nqbs = [int(w.cu_qblocks[s + 1] - w.cu_qblocks[s]) for s in range(w.num_seqs)]
-    nkbs = [-(-int(t) // w.cfg.block) for t in w.seqlens_k]
+    nkbs = [-(-int(t) // kv_block(w)) for t in w.seqlens_k]
     keeps = O.keep_from_csr(rp, ci, w.cfg.hkv, nqbs, nkbs)
-    ref = O.run_batch(seqs, w.cfg.block, tau, corr, keeps=keeps)["out"]
+    ref = O.run_batch(seqs, w.cfg.block, tau, corr, keeps=keeps, BK=kv_block(w))["out"]
     got = out[:w.total_q].float().cpu().numpy().astype(np.float64)
     return got, ref, w, L
 
@@ -159,7 +168,8 @@ def test_attention_parity(name, corr, out_dtype):
         check_out(got, ref, TOL[w.cfg.dtype], out_dtype)
 
 
-@pytest.mark.parametrize("name", ["varlen_p64", "fp8_varlen", "chunk_after_prefix", "d128_b64_p128", "d64_b128_p16"])
+@pytest.mark.parametrize("name", ["varlen_p64", "fp8_varlen", "chunk_after_prefix", "d128_b64_p128", "d64_b128_p16",
+                                  "dec_varlen", "dec_d64_p128"])
 def test_cached_block_stats(name):
     """The block means kept in a cache beside the KV pages: with refresh_prefix the gathered
     kbar / vbar equal fp2_block_stats bit for bit; without it, the rows of blocks holding new
@@ -170,7 +180,7 @@ def test_cached_block_stats(name):
     L = layer(w)
     L.stats()
     rows = lib.fp2_block_stats_cache_rows(L.batch, L.kv)
-    B, ps = w.cfg.block, w.cfg.page_size
+    B, ps = kv_block(w), w.cfg.page_size
     bpp = max(1, ps // B)
     assert rows == w.k_pages.shape[0] * bpp
     kc = torch.full((rows, w.cfg.hkv, w.cfg.d), float("nan"), device="cuda")
