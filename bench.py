@@ -47,6 +47,10 @@ def parse():
                          "extreme_fp8 with and without correction) against their own dense runs")
     ap.add_argument("--configs-out", default="", help="also write the --configs table as markdown to this path")
     ap.add_argument("--sweep-out", default="", help="also write the sweep as a markdown table to this path")
+    ap.add_argument("--tiles", action="store_true",
+                    help="128 x 64 against 128 x 128 tiles at 128K, and the CSR index memory of Table 7's setup")
+    ap.add_argument("--tiles-density", type=float, default=0.05, help="kept fraction for the 128K tile comparison")
+    ap.add_argument("--tiles-out", default="", help="also write the --tiles tables as markdown to this path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -64,23 +68,25 @@ def flop_counts(w, nnz):
     """Dense-equivalent, kept-block and correction FLOPs of one layer.
 
     dense  : 4*d*Hq * sum over queries of visible keys (exact causal count)
-    kept   : nnz * G*B^2 * 4d   (diagonal tiles counted whole, as issued)
-    corr   : skipped (q-block, KV-block < diag, KV head) * G*B * 4d
+    kept   : nnz * G*B*KB * 4d   (diagonal tiles counted whole, as issued)
+    corr   : skipped (q-block, KV-block before the diagonal, KV head) * G*B * 4d
+    (B query block, KB KV block tokens)
     """
     cfg = w.cfg
     d, Hq, B, G = cfg.d, cfg.hq, cfg.block, cfg.hq // cfg.hkv
+    KB = cfg.kv_block or B
     dense = 0
-    skippable = 0  # causal pairs strictly between block 0 and the diagonal
+    skippable = 0  # causal pairs strictly between block 0 and the first diagonal block
     for s in range(w.num_seqs):
         T, n = int(w.seqlens_k[s]), int(w.n_q[s])
         P = T - n
         dense += 4 * d * Hq * (n * P + n * (n + 1) // 2)
         nqb = -(-n // B)
         for i in range(nqb):
-            skippable += max(0, P // B + i - 1)
+            skippable += max(0, (P + i * B) // KB - 1)
     skippable *= cfg.hkv
     causal = w.causal_pairs()
-    kept = nnz * G * B * B * 4 * d
+    kept = nnz * G * B * KB * 4 * d
     forced = causal - skippable               # block 0 + diagonal per row (1 when they coincide)
     skipped = causal - nnz                    # every dropped pair is a skippable one
     corr = skipped * G * B * 4 * d
@@ -439,6 +445,101 @@ def config_runs(args, torch, lib, synth):
     print(json.dumps(out), flush=True)
 
 
+def tile_study(args, torch, lib, synth):
+    """Decoupled tiles (Table 7 pairs 128-token query tiles with a CSR of 64-token KV tiles).
+
+    1. One 128K layer of the bf16 128K workload's data, planned at 128 x 128 and at 128 x 64
+       with tau calibrated to the same kept fraction of each one's causal block pairs (so the
+       kept area is about the same), each against its own dense (tau = +inf) run: ms per
+       layer, MFMA fraction of fp2_prefill_run, and how far the sparse output lies from dense
+       attention on these data (mean |O - O_dense| / mean |O_dense|, and the max).
+    2. The CSR index memory of Table 7's setup: batch 1, 32 query / 4 KV heads, 128 x 64
+       tiles, 64K at 9% and 128K at 5% kept.
+    """
+    import dataclasses
+
+    import numpy as np
+    res = {"metric": "decoupled 128 x 64 tiles against 128 x 128 at 128K; CSR index memory", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "layer": [], "index_memory": []}
+    base = synth.CONFIGS["c128k_bf16"]
+    log("tiles: generating the 128K bf16 data ...")
+    w0 = synth.make_custom(base, tau=0.0)
+    T = int(w0.seqlens_k[0])
+    for KB in (128, 64):
+        cfg = dataclasses.replace(base, kv_block=0 if KB == 128 else KB)
+        cu_kb = np.concatenate([[0], np.cumsum([-(-int(t) // KB) for t in w0.seqlens_k])]).astype(np.int32)
+        w = dataclasses.replace(w0, cfg=cfg, cu_kblocks=cu_kb)
+        batch, q, kv = lib.from_workload(w)
+        L = lib.PrefillLayer(batch, q, kv, out_dtype=torch.float32)
+        L.stats()
+        causal = w.causal_pairs()
+        tau = calibrate_tau(L, causal, args.tiles_density, torch)
+        layer_ms, run_ms = time_layer(L, tau, True, args.steps, args.warmup, torch)
+        nnz = int(L.nnz.item())
+        sparse = L.out.clone()
+        log(f"tiles: 128 x {KB}: tau {tau:.4f}, kept {nnz}/{causal}, {layer_ms:.3f} ms/layer; dense run ...")
+        d_layer, d_run = time_layer(L, math.inf, True, args.dense_steps, 1, torch)
+        dense = L.out
+        diff = (sparse - dense).abs()
+        fl = flop_counts(w, nnz)
+        row = dict(tiles=f"128x{KB}", kernel="attn_d128_kernel" if KB == 128 else "attn_kernel (register-staged)",
+                   tau=round(tau, 5), density=round(nnz / causal, 5), nnz=nnz,
+                   csr_bytes=4 * (batch.total_qblocks * base.hkv + 1 + nnz),
+                   ms_per_layer=round(layer_ms, 4), prefill_run_ms=round(run_ms, 4),
+                   mfma_frac_run=round((fl["kept"] + fl["corr"]) / (run_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+                   dense_ms_per_layer=round(d_layer, 3), speedup_vs_dense=round(d_layer / layer_ms, 2),
+                   dense_equiv_tflops=round(fl["dense"] / (layer_ms * 1e-3) / 1e12, 2),
+                   err_rel_mean=float(diff.mean() / dense.abs().mean()), err_max=float(diff.max()))
+        log("tiles:", json.dumps(row))
+        res["layer"].append(row)
+        del L, batch, q, kv, sparse, dense, diff, w
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    del w0
+    for T, dens in ((65536, 0.09), (131072, 0.05)):
+        cfg = synth.Config(name=f"t7_{T // 1024}k", seqlens=(T,), prefixes=(0,), hq=32, hkv=4, d=128, block=128,
+                           page_size=128, dtype="bf16", structure="band_sinks", tau=0.0, seed=7, kv_block=64,
+                           description=f"L={T}, 32q/4kv, d=128, 128 x 64 tiles, band + 16 sinks")
+        log(f"tiles: index memory at {T // 1024}K, generating ...")
+        w = synth.make_custom(cfg, tau=0.0)
+        batch, q, kv = lib.from_workload(w)
+        L = lib.PrefillLayer(batch, q, kv)
+        L.stats()
+        causal = w.causal_pairs()
+        tau = calibrate_tau(L, causal, dens, torch)
+        L.plan(tau)
+        torch.cuda.synchronize()
+        nnz = int(L.nnz.item())
+        rows = batch.total_qblocks * cfg.hkv
+        nqb = batch.total_qblocks
+        G = cfg.hq // cfg.hkv
+        row = dict(seq=T, target_density=dens, density=round(nnz / causal, 5), nnz=nnz, csr_rows=rows,
+                   csr_bytes=4 * (rows + 1 + nnz), per_query_head_bytes=4 * G * nnz,
+                   dense_mask_bytes=cfg.hq * nqb * nqb)
+        log("tiles:", json.dumps(row))
+        res["index_memory"].append(row)
+        del L, batch, q, kv, w
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    if args.tiles_out:
+        with open(args.tiles_out, "w") as f:
+            f.write("| tiles | kernel | tau | density | kept pairs | CSR bytes | ms/layer | prefill_run ms "
+                    "| MFMA fraction of prefill_run | dense ms/layer | speedup vs dense "
+                    "| mean abs err / mean abs O (vs dense) | max abs err |\n"
+                    "|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+            for r in res["layer"]:
+                f.write(f"| {r['tiles']} | {r['kernel']} | {r['tau']} | {r['density']} | {r['nnz']} | {r['csr_bytes']} "
+                        f"| {r['ms_per_layer']} | {r['prefill_run_ms']} | {r['mfma_frac_run']} "
+                        f"| {r['dense_ms_per_layer']} | {r['speedup_vs_dense']} | {r['err_rel_mean']:.4g} "
+                        f"| {r['err_max']:.4g} |\n")
+            f.write("\n| sequence | target density | density | kept pairs | CSR rows | CSR bytes "
+                    "| same selection per query head | dense byte mask |\n|---|---|---|---|---|---|---|---|\n")
+            for r in res["index_memory"]:
+                f.write(f"| {r['seq']} | {r['target_density']} | {r['density']} | {r['nnz']} | {r['csr_rows']} "
+                        f"| {r['csr_bytes']} | {r['per_query_head_bytes']} | {r['dense_mask_bytes']} |\n")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -453,6 +554,9 @@ def main():
         return
     if args.configs:
         config_runs(args, torch, lib, synth)
+        return
+    if args.tiles:
+        tile_study(args, torch, lib, synth)
         return
     taus = load_taus()
     w, bf = run_workload("c128k_bf16", taus["c128k_bf16"]["tau"], args, torch, lib, synth)
