@@ -482,7 +482,8 @@ def tile_study(args, torch, lib, synth):
         dense = L.out
         diff = (sparse - dense).abs()
         fl = flop_counts(w, nnz)
-        row = dict(tiles=f"128x{KB}", kernel="attn_d128_kernel" if KB == 128 else "attn_kernel (register-staged)",
+        row = dict(tiles=f"128x{KB}",
+                   kernel="attn_d128_kernel" if KB == 128 else "attn_d128_kernel (two 64-token blocks a tile)",
                    tau=round(tau, 5), density=round(nnz / causal, 5), nnz=nnz,
                    csr_bytes=4 * (batch.total_qblocks * base.hkv + 1 + nnz),
                    ms_per_layer=round(layer_ms, 4), prefill_run_ms=round(run_ms, 4),
@@ -583,7 +584,7 @@ def main():
         "config": {"workload": "c128k_bf16: 1 seq L=131072, 32 q / 8 kv heads, d=128, block 128, band + 16 "
                                "sink columns, tau for 5% kept blocks, mean correction on",
                    "tau": bf["tau"], "density": round(bf["density"], 5), "nnz": bf["nnz"]},
-        "roofline": {"bound": "mfma", "kernel": "attn_d128_kernel<false> (fp2_prefill_run: plus its V^T preparation "
+        "roofline": {"bound": "mfma", "kernel": "attn_d128_kernel<false, false> (fp2_prefill_run: plus its V^T preparation "
                                "kernels, ~1% of the call)", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,

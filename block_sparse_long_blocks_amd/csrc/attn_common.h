@@ -45,6 +45,7 @@ struct AttnArgs {
   int num_seqs, hq, hkv, max_pages, page_size, total_qblocks, total_kblocks;
   int correction, slices, rows, out_f32, mt_cap;
   int qblk;                // query block tokens (register-staged kernel; the d128 kernel's is 128)
+  int pair;                // d128 kernel: 64-token KV blocks, two to a 128-key tile
 };
 
 

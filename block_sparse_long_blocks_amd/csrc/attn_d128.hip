@@ -1,11 +1,13 @@
-// Stage 2 for head_dim 128 and block 128, bf16 or e4m3 inputs: block-sparse
-// causal GQA attention over the kept KV blocks plus the mean correction of
-// every skipped block, in one online softmax.
+// Stage 2 for head_dim 128 and query blocks of 128 over KV blocks of 128
+// (bf16 or e4m3 inputs) or of 64 (bf16): block-sparse causal GQA attention
+// over the kept KV blocks plus the mean correction of every skipped block, in
+// one online softmax.
 //
 // FlashPrefill V2 (metallab.ai paper page): Figure 3 (exact path over the
 // CSR-selected blocks, correction path merged in the online softmax),
 // Figure 4 (a pruned block J adds |B_J| * exp(q . kbar_J / sqrt(d)) * (vbar_J, 1)),
-// Table 7 (CSR per KV head, paged KV at any page size).
+// Table 7 (CSR per KV head, paged KV at any page size, 128-token query tiles
+// over a CSR of 64-token KV tiles).
 //
 // CDNA4 layout of the work:
 //  * One workgroup = 8 waves = 256 packed query rows of one CSR row (the G
@@ -39,6 +41,12 @@
 //    would reach 2^64.  The younger wave of each SIMD takes the higher issue
 //    priority for the first half of a tile (the arbiter otherwise serves the
 //    older one first).
+//  * 64-token KV blocks: a tile holds two kept blocks (CSR entries 2i and
+//    2i+1 of the row), waves 0-1 moving the first block's K rows and 2-3 the
+//    second's; V^T is kept as half tiles (128 d x 64 keys) and each lane
+//    takes its 16-byte chunk from the half its key positions belong to.  A
+//    row's last entry may be alone (second half masked); the diagonal mask
+//    is by position, one offset per half.
 //  * The workgroups run work items built on the device (items_kernel):
 //    heaviest first, with the exact tiles of rows much heavier than the rest
 //    cut into chunks whose float32 partials combine_kernel merges.
@@ -126,19 +134,23 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
 // One V^T tile per (KV block, head): thread t moves the 8 keys at positions
 // 8(t/16) .. +7 for the 8 d values of chunk t%16.  Keys past the sequence end
 // are zero.  e4m3 V is dequantized (code times the page's scale, rounded to
-// bf16).
-template <bool FP8>
+// bf16).  HALF (64-token KV blocks): a half tile of 128 d rows x 64 keys per
+// block (rows of 128 bytes), two blocks per workgroup.
+template <bool FP8, bool HALF>
 __global__ __launch_bounds__(256) void vt_exact_kernel(PrepArgs a) {
-  const int kb = blockIdx.x, g = blockIdx.y;
+  constexpr int KB = HALF ? 64 : kBlk;  // keys of a block
+  const int t = threadIdx.x;
+  const int kb = HALF ? 2 * blockIdx.x + (t >> 7) : blockIdx.x, g = blockIdx.y;
+  if (HALF && kb >= a.total_kblocks) return;
   const int s = find_seq(a.cu_kblocks, a.num_seqs, kb);
   const int J = kb - a.cu_kblocks[s];
   const int T = a.seqlens_k[s];
   const int32_t* pt = a.page_table + (int64_t)s * a.max_pages;
-  const int t = threadIdx.x, c = t >> 4, dc = t & 15;
+  const int c = HALF ? (t >> 4) & 7 : t >> 4, dc = t & 15;
   uint4 in[8], out[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int pos = J * kBlk + key_of_pos(8 * c + e);
+    const int pos = J * KB + key_of_pos(8 * c + e);
     uint4 v = make_uint4(0, 0, 0, 0);
     if (pos < T) {
       int pi, slot;
@@ -157,9 +169,9 @@ __global__ __launch_bounds__(256) void vt_exact_kernel(PrepArgs a) {
     in[e] = v;
   }
   transpose8x8(in, out);
-  uint8_t* dst = a.vt + ((int64_t)g * a.total_kblocks + kb) * kTileGlobal + c * 16;
+  uint8_t* dst = a.vt + ((int64_t)g * a.total_kblocks + kb) * (KB * kRowBytes) + c * 16;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dst + (8 * dc + e) * kRowBytes) = out[e];
+  for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dst + (8 * dc + e) * (2 * KB)) = out[e];
 }
 
 // e4m3 K codes of every block that is some query block's diagonal (the
@@ -522,10 +534,14 @@ struct Wave {
         fr[read0<QK8>(n) + e] = *reinterpret_cast<const bf16x8*>(op_addr<QK8>(n, e, Kt, Vt, off0, off1, off8));
   }
 
-  template <bool MASKED, bool QK8, class Dma>
+  // TWO: the tile's keys are two 64-token blocks; on the diagonal tq is the
+  // query's position minus the first block's first key, tq2 the same for the
+  // second block (very negative when the tile holds one block).
+  template <bool MASKED, bool QK8, bool TWO = false, class Dma>
   __device__ __forceinline__ void tile(bf16x8 (&fr)[kRing], bool first, const uint8_t* Kt, const uint8_t* Vt,
                                        int off0, int off1, const int (&off8)[4], float scl, Dma&& dma, int mode,
-                                       int tq, int hf, float lb, float cbs, int J0, int diag, const uint32_t* kept) {
+                                       int tq, int tq2, int hf, float lb, float cbs, int J0, int diag,
+                                       const uint32_t* kept) {
     bf16x8 pp[2] = {qf[0], qf[0]}, pc[2];
     f32x16 s = f32x16{}, sn = f32x16{};
     Soft st;
@@ -536,7 +552,8 @@ struct Wave {
         if (mode == 0) {
           M[j] = ~0u;
         } else if (mode == 1) {
-          const int lim = tq - 32 * j - 4 * hf;  // element i allowed iff 8(i/4) + i%4 <= lim
+          // element i allowed iff 8(i/4) + i%4 <= lim
+          const int lim = (TWO ? (j < NS / 2 ? tq : tq2) - 32 * (j % (NS / 2)) : tq - 32 * j) - 4 * hf;
           M[j] = lim >= 31 ? ~0u : lim < 0 ? 0u : (2u << lim) - 1u;
         } else {
           M[j] = skipped_word(kept, (J0 >> 5) + j, diag) >> (4 * hf);
@@ -573,8 +590,13 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
-template <bool FP8>
+// PAIR: 64-token KV blocks under 128-token query blocks, two blocks (two CSR
+// entries) to a 128-key tile (bf16 only).
+template <bool FP8, bool PAIR>
 __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
+  constexpr int KB = PAIR ? 64 : kBlk;  // tokens of a KV block
+  static_assert(!(PAIR && FP8), "64-token KV blocks: bf16 only");
+  static_assert(!PAIR || (kDmaWaves / 2) * kDmaRows == 64, "a DMA wave's rows lie in one 64-token block");
   // two K and two V^T buffers, as separate objects so that the compiler can
   // tell the DMA target from the buffers being read
   __shared__ __attribute__((aligned(1024))) uint8_t K0[kTileLds];
@@ -609,7 +631,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   const int q0 = a.cu_seqlens_q[s];
   const int n = a.cu_seqlens_q[s + 1] - q0;
   const int T = a.seqlens_k[s];
-  const int diag = (T - n) / kBlk + I;
+  // the diagonal: KV blocks dlo .. diag hold the query block's own positions
+  // (one block of 128 tokens; two of 64, one for a short last query block)
+  const int qpos0 = T - n + I * kBlk;  // position of the block's first query
+  const int diag = PAIR ? (qpos0 + min(kBlk, n - I * kBlk) - 1) / KB : (T - n) / kBlk + I;
+  const int dlo = PAIR ? qpos0 / KB : diag;
   const int G = a.hq / a.hkv;
   const int32_t* pt = a.page_table + (int64_t)s * a.max_pages;
   const int kb0 = a.cu_kblocks[s];
@@ -629,11 +655,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   // do not share the vector-memory counter with the tile DMA
   const int rbeg = ld_uniform(a.row_ptr, row);
   const int rend = ld_uniform(a.row_ptr, row + 1);
-  // this item's exact tiles; the mean tiles go with the row's last item
-  const int kbeg = rbeg + tile0;
-  const int kend = rbeg + tile1;
-  const int nexact = kend - kbeg;
+  // this item's exact tiles (CSR entries kbeg .. kend-1; with 64-token KV
+  // blocks tile i of a row holds its entries 2i and 2i+1, the last perhaps
+  // alone); the mean tiles go with the row's last item
+  const int kbeg = rbeg + (PAIR ? 2 * tile0 : tile0);
+  const int kend = PAIR ? min(rbeg + 2 * tile1, rend) : rbeg + tile1;
+  const int nexact = PAIR ? tile1 - tile0 : kend - kbeg;
   const bool last_item = kend == rend;
+  const int ne = kend - kbeg;
+  // PAIR: the two block indices of tile i packed as ja | jb << 16 (a lone
+  // last entry goes with itself: its second half is masked)
+  auto pack = [&](int ja, int jb, int i) { return ja | ((2 * i + 1 < ne ? jb : ja) << 16); };
+  auto half_of = [](int J, int h) { return h ? J >> 16 : J & 0xFFFF; };
+  // an exact tile on the masked path: some key past some query
+  auto masked_exact = [&](int J, int i) {
+    if constexpr (PAIR) return 2 * i + 1 >= ne || half_of(J, 1) >= dlo;
+    return J == diag;
+  };
 
 
   Wave ws;
@@ -700,12 +738,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   // the LDS counter instead, and every tile's first operand-read wait would
   // then also wait for them.
   const __amdgpu_buffer_rsrc_t rcol =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(a.col_idx + kbeg), (short)0, nexact * 4, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.col_idx + kbeg), (short)0, ne * 4, kBufferFlags);
+  // first token row this DMA wave moves of exact tile J (PAIR: waves 0-1
+  // the first block, 2-3 the second)
+  auto dma_row0 = [&](int J) -> int {
+    if constexpr (PAIR) return half_of(J, wave >= kDmaWaves / 2) * KB + kDmaRows * (wave % (kDmaWaves / 2));
+    return J * kBlk + kDmaRows * wave;
+  };
+  // PAIR: lane chunk c = (l%16) ^ (l/16) of a V^T row holds keys of block
+  // half c/8; a half tile of one 64-token block has 128-byte rows
+  const int vhalf = ((lane & 15) ^ (lane >> 4)) >> 3;
+  const uint32_t voffh = (uint32_t)((lane >> 4) * (2 * KB) + 16 * (((lane & 15) ^ (lane >> 4)) & 7));
   const __amdgpu_buffer_rsrc_t rpt =
       __builtin_amdgcn_make_buffer_rsrc((void*)pt, (short)0, a.max_pages * 4, kBufferFlags);
   auto page_of = [&](int J, int hh) -> int {  // page of rows R w + 16 hh.. of block J (valid after the next barrier)
     int pi, slot;
-    a.pm.split(min(J * kBlk + kDmaRows * wave + 16 * hh, T - 1), pi, slot);
+    a.pm.split(min(dma_row0(J) + 16 * hh, T - 1), pi, slot);
     return __builtin_amdgcn_raw_buffer_load_b32(rpt, pi * 4, 0, 0);
   };
   // a value loaded before the last barrier, read as a wave-uniform scalar there
@@ -720,6 +768,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   struct DmaPlan {
     const uint8_t* kb[kDmaHalves];
     const uint8_t* vb;
+    const uint8_t* vbl;  // PAIR: this lane's V^T source of instruction 0 (+ vstep p)
+    uint32_t vstep;
     uint8_t* kd;
     uint32_t kstep, kvo;
     int kds, nk;
@@ -737,8 +787,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     pl.kds = kGS;
     pl.nk = kDmaRows / 4;
     if (idx < nexact) {
-      pl.vb = a.vt + (((int64_t)g * a.total_kblocks + kb0 + j) * kBlk + kDmaRows * wave) * kRowBytes;
-      const int r0 = j * kBlk + kDmaRows * wave;
+      if constexpr (PAIR) {
+        pl.vbl = a.vt + ((int64_t)g * a.total_kblocks + kb0 + half_of(j, vhalf)) * (KB * kRowBytes) +
+                 kDmaRows * wave * (2 * KB) + voffh;
+        pl.vstep = 4 * (2 * KB);
+      } else {
+        pl.vb = a.vt + (((int64_t)g * a.total_kblocks + kb0 + j) * kBlk + kDmaRows * wave) * kRowBytes;
+      }
+      const int r0 = dma_row0(j);
       pl.fast = pages16 && r0 + kDmaRows - 1 < T;
       if (FP8 && j == diag) {
         // the diagonal block's K codes widened to bf16 rows (zero past the end)
@@ -788,14 +844,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
           a.pm.split(min(r0 + 4 * p + (lane >> 4), T - 1), pi, slot);  // rows past the end repeat the last key
           const uint8_t* ksrc = a.k_pages + (((int64_t)pt[pi] * a.page_size + slot) * a.hkv + g) * kRowBytes + uoff;
           dma16(ksrc, kd + p * kGS);
-          dma16(pl.vb + voff + 1024 * p, vd + p * kGS);
+          if constexpr (PAIR) dma16(pl.vbl + pl.vstep * p, vd + p * kGS);
+          else dma16(pl.vb + voff + 1024 * p, vd + p * kGS);
         }
       }
     } else {
       pl.vb = a.vbt + (((int64_t)g * a.mt_cap + kb0 / kBlk + s + j / kBlk) * kBlk + kDmaRows * wave) * kRowBytes;
+      pl.vbl = pl.vb + voff;
+      pl.vstep = 1024;
       const uint8_t* k16 = reinterpret_cast<const uint8_t*>(a.kbar16);
       const int r0 = j + kDmaRows * wave;
-      pl.fast = r0 + kDmaRows - 1 < diag;
+      pl.fast = r0 + kDmaRows - 1 < dlo;
       if (pl.fast) {
 #pragma unroll
         for (int hh = 0; hh < kDmaHalves; ++hh) pl.kb[hh] = k16 + (mrow0 + r0 + 16 * hh) * kRowBytes;
@@ -804,7 +863,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
       } else {
 #pragma unroll
         for (int p = 0; p < kDmaRows / 4; ++p) {
-          const int jm = min(r0 + 4 * p + (lane >> 4), diag - 1);  // tokens past diag repeat a real one (masked)
+          const int jm = min(r0 + 4 * p + (lane >> 4), dlo - 1);  // tokens past dlo repeat a real one (masked)
           dma16(k16 + (mrow0 + jm) * kRowBytes + uoff, kd + p * kGS);
           dma16(pl.vb + voff + 1024 * p, vd + p * kGS);
         }
@@ -818,6 +877,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     if ((i & 1) == 0) {
       if (p < pl.nk)
         dma16(pl.kb[p >> 2] + (p & 3) * pl.kstep + pl.kvo, pl.kd + p * pl.kds);
+    } else if constexpr (PAIR) {
+      dma16(pl.vbl + pl.vstep * p, Vd + ((kDmaRows / 4) * wave + p) * kGS);
     } else {
       dma16(pl.vb + 1024 * p + voff, Vd + ((kDmaRows / 4) * wave + p) * kGS);
     }
@@ -849,8 +910,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   };
   // Tile 0 is an exact block (the CSR holds block 0): its DMA, the first
   // page and block-index loads go out before the mean-token setup below.
-  int j0 = 0, j1 = 0, j2v = 0, pgv[kDmaHalves] = {};
-  if (0 < nexact) j0 = ld_uniform(a.col_idx, kbeg);
+  int j0 = 0, j1 = 0, j2v = 0, j2vb = 0, pgv[kDmaHalves] = {};
+  if (0 < nexact) {
+    if constexpr (PAIR) j0 = pack(ld_uniform(a.col_idx, kbeg), ld_uniform(a.col_idx, min(kbeg + 1, kend - 1)), 0);
+    else j0 = ld_uniform(a.col_idx, kbeg);
+  }
   // e4m3: the K scale of exact tile i (one page per block) arrives with the
   // barrier before tile i (ksv); the page entry of tile i+1 one tile earlier
   // (pgbv)
@@ -875,7 +939,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
 
   // ---- mean-token tiles that hold at least one skipped block
   int nmean = 0;
-  if (a.correction && diag > 1 && last_item) {
+  if (a.correction && dlo > 1 && last_item) {
     const int nw = (diag + 32) >> 5;
     for (int w = t; w < nw; w += kThreads) kept[w] = 0u;
     lds_barrier();
@@ -885,14 +949,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     }
     lds_barrier();
     if (wave == 0) {
-      const int ncand = (diag + kBlk - 1) / kBlk;
+      const int ncand = (dlo + kBlk - 1) / kBlk;
       int base = 0;
       for (int m0 = 0; m0 < ncand; m0 += 64) {
         const int mt = m0 + lane;
         bool flag = false;
         if (mt < ncand) {
 #pragma unroll
-          for (int w = 0; w < kBlk / 32; ++w) flag |= skipped_word(kept, mt * (kBlk / 32) + w, diag) != 0u;
+          for (int w = 0; w < kBlk / 32; ++w) flag |= skipped_word(kept, mt * (kBlk / 32) + w, dlo) != 0u;
         }
         const uint64_t bal = __ballot(flag);
         if (flag) mtile[base + __popcll(bal & ((1ull << lane) - 1ull))] = mt * kBlk;
@@ -914,9 +978,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
       for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, V0);
     }
   }
-  if (1 < nexact) j1 = ld_uniform(a.col_idx, kbeg + 1);
-  else if (1 < ntiles) j1 = mean_of(1);
-  if (2 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 2 * 4, 0, 0);
+  if (1 < nexact) {
+    if constexpr (PAIR) j1 = pack(ld_uniform(a.col_idx, kbeg + 2), ld_uniform(a.col_idx, min(kbeg + 3, kend - 1)), 1);
+    else j1 = ld_uniform(a.col_idx, kbeg + 1);
+  } else if (1 < ntiles) {
+    j1 = mean_of(1);
+  }
+  if (2 < nexact) {
+    if constexpr (PAIR) {
+      j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 4 * 4, 0, 0);
+      j2vb = __builtin_amdgcn_raw_buffer_load_b32(rcol, 5 * 4, 0, 0);
+    } else {
+      j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 2 * 4, 0, 0);
+    }
+  }
   if constexpr (FP8) {
     if (1 < nexact) pgbv = __builtin_amdgcn_raw_buffer_load_b32(rpt, j1 * 4, 0, 0);
   }
@@ -935,7 +1010,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     bf16x8 fr[Wave::kRing];
     if (wave_active) ws.first_reads<FP8 && !MASKED>(fr, Kc, Vc, off0, off1, off8);
     __builtin_amdgcn_sched_barrier(0);
-    const int j2 = idx + 2 < nexact ? after_barrier(j2v) : mean_of(idx + 2);
+    int j2;
+    if constexpr (PAIR) j2 = idx + 2 < nexact ? pack(after_barrier(j2v), after_barrier(j2vb), idx + 2) : mean_of(idx + 2);
+    else j2 = idx + 2 < nexact ? after_barrier(j2v) : mean_of(idx + 2);
     float sclt = scl;
     if constexpr (FP8) {
       if (idx < nexact) sclt = scl * __uint_as_float((uint32_t)after_barrier(ksv));
@@ -956,8 +1033,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
 #pragma unroll
       for (int hh = 0; hh < kDmaHalves; ++hh) pgv[hh] = page_of(j2, hh);
     }
-    if (idx + 3 < nexact) j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, (idx + 3) * 4, 0, 0);
-    const int mode = idx >= nexact ? 2 : (j0 == diag ? 1 : 0);
+    if (idx + 3 < nexact) {
+      if constexpr (PAIR) {
+        j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 2 * (idx + 3) * 4, 0, 0);
+        j2vb = __builtin_amdgcn_raw_buffer_load_b32(rcol, (2 * (idx + 3) + 1) * 4, 0, 0);
+      } else {
+        j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, (idx + 3) * 4, 0, 0);
+      }
+    }
+    const int mode = idx >= nexact ? 2 : (masked_exact(j0, idx) ? 1 : 0);
     // The issue arbiter serves the older wave of a SIMD first (waves 0-3,
     // which also issue the DMA): the younger waves 4-7 get the higher issue
     // priority until region 3 so that the two finish a tile closer together.
@@ -971,12 +1055,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
         for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, Vn);
       }
     } else if constexpr (!MASKED) {
-      ws.tile<false, FP8>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, 0, tq, hf, 0.f, 0.f, 0, diag, kept);
+      ws.tile<false, FP8>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, 0, tq, 0, hf, 0.f, 0.f, 0, dlo, kept);
     } else {
-      // mean tiles: weight B, log2 B in the exponent (cbs in score units)
+      // mean tiles: weight of a KV block, its log2 in the exponent (cbs in score units)
       const float lbm = mode == 2 ? a.log2_block : 0.f;
-      ws.tile<true, false>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, mode, tq, hf, lbm, lbm / sclt, j0, diag,
-                           kept);
+      if constexpr (PAIR) {
+        // diagonal offsets of the two blocks (a lone block: its second half masked)
+        const int qd = qpos0 + tq;
+        const int tqa = qd - half_of(j0, 0) * KB;
+        const int tqb = 2 * idx + 1 < ne ? qd - half_of(j0, 1) * KB : -(1 << 20);
+        ws.tile<true, false, true>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, mode, tqa, tqb, hf, lbm,
+                                   lbm / sclt, j0, dlo, kept);
+      } else {
+        ws.tile<true, false>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, mode, tq, 0, hf, lbm, lbm / sclt, j0,
+                             dlo, kept);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
     j0 = j1;
@@ -993,10 +1086,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   const std::integral_constant<bool, false> plain_c;
   const std::integral_constant<bool, true> masked_c;
   int idx = 0;
-  while (idx < nexact && j0 != diag) {
+  while (idx < nexact && !masked_exact(j0, idx)) {
     iter(plain_c, idx, K0, V0, K1, V1);
     ++idx;
-    if (!(idx < nexact && j0 != diag)) break;
+    if (!(idx < nexact && !masked_exact(j0, idx))) break;
     iter(plain_c, idx, K1, V1, K0, V0);
     ++idx;
   }
@@ -1088,12 +1181,14 @@ __device__ void rank_tiles(const AttnArgs& a, int r, int& nexact, int& nmean) {
   const int qb = a.total_qblocks - 1 - r / a.hkv;
   const int row = (r % a.hkv) * a.total_qblocks + qb;
   nexact = max(a.row_ptr[row + 1] - a.row_ptr[row], 0);
+  if (a.pair) nexact = (nexact + 1) >> 1;  // 64-token KV blocks, two a tile
   nmean = 0;
   if (a.correction) {
     const int s = find_seq(a.cu_qblocks, a.num_seqs, qb);
     const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
-    const int diag = (a.seqlens_k[s] - n) / kBlk + qb - a.cu_qblocks[s];
-    nmean = (diag + kBlk - 1) / kBlk;
+    // first KV block of the diagonal: its mean tokens come before it
+    const int dlo = (a.seqlens_k[s] - n + (qb - a.cu_qblocks[s]) * kBlk) / (a.pair ? 64 : kBlk);
+    nmean = (dlo + kBlk - 1) / kBlk;
   }
 }
 
@@ -1312,12 +1407,15 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
   if (a.total_kblocks > 0) {
     const dim3 per_block((unsigned)a.total_kblocks, (unsigned)a.hkv);
     if (fp8) {
-      hipLaunchKernelGGL(vt_exact_kernel<true>, per_block, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((vt_exact_kernel<true, false>), per_block, dim3(256), 0, stream, p);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kd_kernel, per_block, dim3(256), 0, stream, p);
+    } else if (a.pair) {
+      hipLaunchKernelGGL((vt_exact_kernel<false, true>), dim3((unsigned)((a.total_kblocks + 1) / 2), (unsigned)a.hkv),
+                         dim3(256), 0, stream, p);
     } else {
-      hipLaunchKernelGGL(vt_exact_kernel<false>, per_block, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((vt_exact_kernel<false, false>), per_block, dim3(256), 0, stream, p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1347,9 +1445,11 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
   const int items_cap = a.rows + a.extra_cap;
   const unsigned grid = (unsigned)(((items_cap + 7) / 8) * 8 * a.slices);
   if (fp8)
-    hipLaunchKernelGGL(attn_d128_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_d128_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (a.pair)
+    hipLaunchKernelGGL((attn_d128_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_d128_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_d128_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.extra_cap <= 0) return e;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)a.extra_cap, (unsigned)a.slices), dim3(kThreads), 0, stream, a);

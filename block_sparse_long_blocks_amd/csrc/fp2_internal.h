@@ -37,18 +37,19 @@ fp2_status check_q(const fp2_q* q, int num_kv_heads, const BatchInfo& info, int 
 fp2_status check_kv(const fp2_kv* kv, const fp2_batch* b, const BatchInfo& info);
 
 size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads);
-// fp2_prefill_run runs the DMA kernel on V^T tiles for d = 128 and query and
-// KV blocks of 128 (bf16 or e4m3), and the register-staged kernel otherwise.
+// fp2_prefill_run runs the DMA kernel on V^T tiles for d = 128 and query
+// blocks of 128 over KV blocks of 128 (bf16 or e4m3) or of 64 (bf16, two to a
+// tile), and the register-staged kernel otherwise.
 inline bool vt_path(int dtype, int head_dim, const BatchInfo& info) {
   return (dtype == FP2_BF16 || dtype == FP2_FP8_E4M3) && head_dim == 128 && info.qblock == 128 &&
-         info.kvblock == 128;
+         (info.kvblock == 128 || (info.kvblock == 64 && dtype == FP2_BF16));
 }
 
 // Byte offsets of the parts of the fp2_prefill_run workspace.
 struct RunLayout {
   size_t k16 = 0;      // bf16 kbar rows [Hkv, total_kblocks, d]
   size_t v16 = 0;      // fp16 vbar rows (register-staged path) or vbar^T tiles (V^T path)
-  size_t vt = 0;       // V^T tiles of every KV block (V^T path)
+  size_t vt = 0;       // V^T tiles of every KV block (V^T path; 64 keys a tile with 64-token blocks)
   size_t kd = 0;       // e4m3 V^T path: K codes as bf16 rows, [Hkv, total_kblocks, B, d]
   size_t items = 0;    // V^T path: work items in launch order, int4 [rows + extra_cap]
   size_t splits = 0;   // V^T path: rows split into chunks, int4 [extra_cap]

@@ -154,10 +154,10 @@ RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int n
   L.k16 = 0;
   L.v16 = rows;
   if (vt_path(dtype, head_dim, info)) {
-    const size_t block = (size_t)info.kvblock;
-    const size_t tile = block * (size_t)head_dim * 2;  // one 128 x 128 bf16 tile
-    L.mt_cap = (int64_t)(tkb / block + (size_t)num_seqs + 1);
-    L.vt = L.v16 + hkv * (size_t)L.mt_cap * tile;
+    const size_t tile = (size_t)info.kvblock * (size_t)head_dim * 2;  // V^T of one KV block, bf16
+    const size_t mtile = 128 * (size_t)head_dim * 2;                   // vbar^T of 128 mean tokens
+    L.mt_cap = (int64_t)(tkb / 128 + (size_t)num_seqs + 1);
+    L.vt = L.v16 + hkv * (size_t)L.mt_cap * mtile;
     L.total = L.vt + hkv * tkb * tile;
     if (dtype == FP2_FP8_E4M3) {
       L.kd = L.total;
@@ -169,7 +169,7 @@ RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int n
     const size_t nrows = hkv * (size_t)info.total_qblocks;
     const int64_t causal_tiles = info.causal_pairs * (int64_t)num_kv_heads;
     L.extra_cap = std::min<int64_t>(kMaxExtraItems, (causal_tiles + 3) / 4);
-    const size_t slices = (size_t)((std::max(num_q_heads / std::max(num_kv_heads, 1), 1) * (int)block + 255) / 256);
+    const size_t slices = (size_t)((std::max(num_q_heads / std::max(num_kv_heads, 1), 1) * info.qblock + 255) / 256);
     L.items = L.total;
     L.splits = L.items + up((nrows + (size_t)L.extra_cap) * 16);
     L.rank_slot = L.splits + up((size_t)L.extra_cap * 16 + 16);

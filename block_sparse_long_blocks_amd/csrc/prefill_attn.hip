@@ -635,6 +635,7 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.total_kblocks = (int)info.total_kblocks;
   a.correction = correction;
   a.qblk = QB;
+  a.pair = vt && BLK == 64;
   const int G = q->num_q_heads / hkv;
   a.slices = (G * QB + kRowsPerWG - 1) / kRowsPerWG;
   a.rows = (int)(info.total_qblocks * hkv);

@@ -72,12 +72,17 @@ SMALL = {
     "dec_fp8": _cfg("dec_fp8", (1024, 512), (0, 256), 8, 2, 128, 128, 64, dtype="fp8", kv_block=64),
     "dec_d64_p128": _cfg("dec_d64_p128", (512, 384), (128, 256), 8, 4, 64, 128, 128, kv_block=64),
     "dec_g8": _cfg("dec_g8", (700,), (384,), 16, 2, 128, 128, 64, kv_block=64),
+    # the same on the DMA kernel's pair tiles (bf16, d = 128): one query block after a long prefix
+    # (rows split into chunks), and pages of 24 tokens (per-lane DMA sources) with G = 1
+    "dec_chunk": _cfg("dec_chunk", (6144,), (6016,), 8, 4, 128, 128, 128, kv_block=64),
+    "dec_p24_g1": _cfg("dec_p24_g1", (900, 260), (128, 0), 2, 2, 128, 128, 24, kv_block=64),
 }
 TAUS = {"tiny": (0.0, 0.005, 0.01, 0.02, 2.0), "varlen_p64": (0.0, 0.5, 3.0),
         "d64_b128_p16": (0.3, 3.0), "d128_b64_g8": (0.2, 2.0), "single_token": (0.0, 1.0),
         "fp8_varlen": (0.0, 0.5, 3.0), "d128_p24_g1": (0.0, 1.0), "d128_p8_g8": (0.0, 1.0),
         "chunk_after_prefix": (0.5, 1e9), "chunk_after_prefix_fp8": (0.5, 1e9), "d128_b64_p128": (0.0, 1.0),
-        "dec_varlen": (0.0, 0.5, 3.0), "dec_fp8": (0.0, 0.5, 3.0), "dec_d64_p128": (0.3, 3.0), "dec_g8": (0.0, 1.0)}
+        "dec_varlen": (0.0, 0.5, 3.0), "dec_fp8": (0.0, 0.5, 3.0), "dec_d64_p128": (0.3, 3.0), "dec_g8": (0.0, 1.0),
+        "dec_chunk": (0.5, 1e9), "dec_p24_g1": (0.0, 1.0)}
 
 _cache = {}
 
@@ -211,7 +216,7 @@ def test_cached_block_stats(name):
 
 
 @pytest.mark.parametrize("corr", [True, False])
-@pytest.mark.parametrize("name", ["varlen_p64", "fp8_varlen"])
+@pytest.mark.parametrize("name", ["varlen_p64", "fp8_varlen", "dec_varlen"])
 def test_split_rows_match_oracle(name, corr, monkeypatch):
     """Rows whose exact tiles are cut into chunks (FP2_MAX_CHUNK_TILES caps the
     chunk; the batch bounds it below by its tiles over its extra-item budget,
@@ -224,8 +229,12 @@ def test_split_rows_match_oracle(name, corr, monkeypatch):
         whole, ref, w, L = _attention_case(name, tau, corr, out_dtype="f32")
         rp, _ = L.csr_host()
         extra_cap = min(256, -(-w.causal_pairs() // 4))
-        chunk = max(2, -(-int(rp[-1]) // extra_cap))
-        assert int(np.max(np.diff(rp))) > chunk  # some row is split
+        # exact tiles per row: one per kept block, or one per two with 64-token KV blocks
+        tiles = np.diff(rp) if kv_block(w) == w.cfg.block else -(-np.diff(rp) // 2)
+        chunk = max(2, -(-int(tiles.sum()) // extra_cap))
+        if tau != math.inf and int(tiles.max()) <= chunk:
+            continue  # no row long enough to split at this threshold
+        assert int(tiles.max()) > chunk  # some row is split
         monkeypatch.setenv("FP2_MAX_CHUNK_TILES", "2")
         split, ref2, _, _ = _attention_case(name, tau, corr, out_dtype="f32")
         assert np.array_equal(ref, ref2)
@@ -234,7 +243,7 @@ def test_split_rows_match_oracle(name, corr, monkeypatch):
         assert not np.array_equal(split, whole)
 
 
-@pytest.mark.parametrize("name", ["tiny", "varlen_p64", "d128_b64_g8"])
+@pytest.mark.parametrize("name", ["tiny", "varlen_p64", "d128_b64_g8", "dec_varlen", "dec_fp8"])
 def test_dense_mode_is_causal_attention(name):
     got, _, w, _ = _attention_case(name, math.inf, True, out_dtype="f32")
     _, seqs = workload(name)
@@ -242,7 +251,7 @@ def test_dense_mode_is_causal_attention(name):
     check_out(got, ref, TOL[w.cfg.dtype], "f32")
 
 
-@pytest.mark.parametrize("name", ["varlen_p64", "d64_b128_p16", "fp8_varlen"])
+@pytest.mark.parametrize("name", ["varlen_p64", "d64_b128_p16", "fp8_varlen", "dec_varlen", "dec_p24_g1"])
 def test_pad_slots_are_never_read(name):
     """Unused slots of each last page hold NaN; results must equal the zero-padded run."""
     got_z, _, w, Lz = _attention_case(name, 0.5, True, "zero")
