@@ -183,9 +183,10 @@ fp2_status fp2_plan_mask(const fp2_batch *batch, const fp2_q *q, int32_t num_kv_
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes fp2_prefill_run needs for this batch, head size and KV
- * dtype (0 if the batch is empty or malformed).  For d = 128 and B = KB = 128 it
- * holds V^T tiles of every KV block (one bf16 128 x 128 tile per block and
- * KV head, e4m3 V dequantized: about the size of bf16 V), bf16 kbar rows and
+ * dtype (0 if the batch is empty or malformed).  For d = 128 and B = KB = 128,
+ * or bf16 with B = 128 over KB = 64, it holds V^T tiles of every KV block
+ * (one bf16 128 x KB tile per block and KV head, e4m3 V dequantized: about
+ * the size of bf16 V), bf16 kbar rows and
  * vbar^T tiles of the mean tokens, for e4m3 also the K codes of every
  * block widened to bf16 rows (another tile per block and head), and the
  * work items in launch order (one per CSR row plus up to 256 chunks of
@@ -207,10 +208,12 @@ size_t fp2_run_workspace_bytes(const fp2_batch *batch, int32_t num_q_heads, int3
  *   out_dtype         FP2_OUT_BF16 (rounded to nearest even) or FP2_OUT_F32
  *   out               device [total_q, Hq, d] of out_dtype
  *   workspace         device scratch of fp2_run_workspace_bytes() bytes;
- *                     required with d = 128 and B = KB = 128 (bf16 or e4m3),
- *                     else only with mean_correction (FP2_ERR_CAPACITY if
+ *                     required with d = 128 and B = KB = 128 (bf16 or e4m3)
+ *                     or bf16 B = 128 over KB = 64, else only with
+ *                     mean_correction (FP2_ERR_CAPACITY if
  *                     too small); its contents are overwritten
- * With d = 128 and B = KB = 128 the rows run as work items launched heaviest
+ * On that path (KB = 64: tiles of two kept 64-token blocks) the rows run as
+ * work items launched heaviest
  * first; the exact tiles of a row heavier than a quarter of a CU's share
  * of the batch are cut into chunks whose float32 partials a second kernel
  * merges (at most 256 extra items).  The environment variable

@@ -8,6 +8,7 @@ threshold, which are counted); attention outputs are compared on sampled
 own mask: the last query block of every KV head (largest causal extent), the
 first, and seeded random ones.
 """
+import dataclasses
 import json
 import os
 
@@ -16,7 +17,7 @@ import pytest
 
 import oracle as O
 import synth
-from helpers import compare_csr, csr_well_formed, decoded_seqs, stats_bound
+from helpers import compare_csr, csr_well_formed, decoded_seqs, kv_block, stats_bound
 from test_gpu_parity import TOL, check_out
 
 pytestmark = pytest.mark.gpu
@@ -43,10 +44,13 @@ def _rows(w, seed, n_random=2):
     return rows
 
 
-def run_full(name, corrections=(True,), out_dtype="bf16"):
+def run_full(name, corrections=(True,), out_dtype="bf16", kv_blk=0, tau=None):
     import block_sparse_long_blocks_amd as lib
-    tau = TAUS[name]["tau"]
-    w = synth.make(name, tau=tau)
+    tau = TAUS[name]["tau"] if tau is None else tau
+    cfg = synth.CONFIGS[name]
+    if kv_blk:
+        cfg = dataclasses.replace(cfg, kv_block=kv_blk)
+    w = synth.make_custom(cfg, tau=tau)
     L = lib.PrefillLayer(*lib.from_workload(w), out_dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16)
     L.stats()
     L.plan(tau)
@@ -62,7 +66,7 @@ def run_full(name, corrections=(True,), out_dtype="bf16"):
     del L
     torch.cuda.empty_cache()
     seqs = decoded_seqs(w)
-    plan = O.plan_batch(seqs, w.cfg.block, tau)
+    plan = O.plan_batch(seqs, w.cfg.block, tau, BK=kv_block(w))
     return w, seqs, plan, tau, (rp, ci, kb, vb), outs
 
 
@@ -81,14 +85,14 @@ def check_stats_and_plan(w, seqs, plan, gpu):
 def check_rows(w, seqs, gpu, out, corr, rows, tol, out_dtype="bf16"):
     rp, ci = gpu[0], gpu[1]
     nqbs = [int(w.cu_qblocks[s + 1] - w.cu_qblocks[s]) for s in range(w.num_seqs)]
-    nkbs = [-(-int(t) // w.cfg.block) for t in w.seqlens_k]
+    nkbs = [-(-int(t) // kv_block(w)) for t in w.seqlens_k]
     keeps = O.keep_from_csr(rp, ci, w.cfg.hkv, nqbs, nkbs)
     B, G = w.cfg.block, w.cfg.hq // w.cfg.hkv
     worst = 0.0
     for s in sorted({r[0] for r in rows}):
         Q, K, V = seqs[s]
         want = [(g, i) for (ss, g, i) in rows if ss == s]
-        ref, _ = O.attend(Q, K, V, keeps[s], B, corr, rows=want)
+        ref, _ = O.attend(Q, K, V, keeps[s], B, corr, rows=want, BK=kv_block(w))
         q0 = int(w.cu_seqlens_q[s])
         for g, i in want:
             t0, t1 = i * B, min(i * B + B, Q.shape[0])
@@ -104,6 +108,18 @@ def test_fullsize_parity(name):
     rows = _rows(w, seed=7)
     worst = check_rows(w, seqs, gpu, outs[True], True, rows, TOL[w.cfg.dtype])
     print(f"{name}: {len(rows)} sampled rows, max abs err {worst:.4f} (bf16 output)")
+
+
+def test_fullsize_decoupled_tiles():
+    """The 128K bf16 data with 128-token query blocks over 64-token KV blocks, on the
+    attention kernel's pair tiles (as `bench.py --tiles` times it); tau 3.9 keeps about
+    5% of the 64-token causal pairs."""
+    print("decoupled 128K: generating and running", flush=True)
+    w, seqs, plan, tau, gpu, outs = run_full("c128k_bf16", kv_blk=64, tau=3.9)
+    check_stats_and_plan(w, seqs, plan, gpu)
+    rows = _rows(w, seed=9)
+    worst = check_rows(w, seqs, gpu, outs[True], True, rows, TOL[w.cfg.dtype])
+    print(f"decoupled 128K: {len(rows)} sampled rows, max abs err {worst:.4f} (bf16 output)")
 
 
 def test_fullsize_extreme_with_and_without_correction():
