@@ -448,7 +448,8 @@ def config_runs(args, torch, lib, synth):
 def tile_study(args, torch, lib, synth):
     """Decoupled tiles (Table 7 pairs 128-token query tiles with a CSR of 64-token KV tiles).
 
-    1. One 128K layer of the bf16 128K workload's data, planned at 128 x 128 and at 128 x 64
+    1. One 128K layer of the 128K workloads' data (bf16, then e4m3 quantized per KV block),
+       planned at 128 x 128 and at 128 x 64
        with tau calibrated to the same kept fraction of each one's causal block pairs (so the
        kept area is about the same), each against its own dense (tau = +inf) run: ms per
        layer, MFMA fraction of fp2_prefill_run, and how far the sparse output lies from dense
@@ -461,14 +462,23 @@ def tile_study(args, torch, lib, synth):
     import numpy as np
     res = {"metric": "decoupled 128 x 64 tiles against 128 x 128 at 128K; CSR index memory", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "layer": [], "index_memory": []}
-    base = synth.CONFIGS["c128k_bf16"]
-    log("tiles: generating the 128K bf16 data ...")
-    w0 = synth.make_custom(base, tau=0.0)
-    T = int(w0.seqlens_k[0])
-    for KB in (128, 64):
-        cfg = dataclasses.replace(base, kv_block=0 if KB == 128 else KB)
-        cu_kb = np.concatenate([[0], np.cumsum([-(-int(t) // KB) for t in w0.seqlens_k])]).astype(np.int32)
-        w = dataclasses.replace(w0, cfg=cfg, cu_kblocks=cu_kb)
+    w0 = None
+    for dt, KB in (("bf16", 128), ("bf16", 64), ("fp8", 128), ("fp8", 64)):
+        base = synth.CONFIGS[f"c128k_{dt}"]
+        if dt == "bf16":
+            # bf16 data do not depend on the block size: one generation serves both tilings
+            if w0 is None:
+                log("tiles: generating the 128K bf16 data ...")
+                w0 = synth.make_custom(base, tau=0.0)
+            cfg = dataclasses.replace(base, kv_block=0 if KB == 128 else KB)
+            cu_kb = np.concatenate([[0], np.cumsum([-(-int(t) // KB) for t in w0.seqlens_k])]).astype(np.int32)
+            w = dataclasses.replace(w0, cfg=cfg, cu_kblocks=cu_kb)
+        else:
+            # e4m3 scales are per page = KV block: the data are quantized per tiling
+            w0 = None
+            cfg = base if KB == 128 else dataclasses.replace(base, kv_block=KB, page_size=KB)
+            log(f"tiles: generating the 128K e4m3 data, {KB}-token KV blocks ...")
+            w = synth.make_custom(cfg, tau=0.0)
         batch, q, kv = lib.from_workload(w)
         L = lib.PrefillLayer(batch, q, kv, out_dtype=torch.float32)
         L.stats()
@@ -477,17 +487,21 @@ def tile_study(args, torch, lib, synth):
         layer_ms, run_ms = time_layer(L, tau, True, args.steps, args.warmup, torch)
         nnz = int(L.nnz.item())
         sparse = L.out.clone()
-        log(f"tiles: 128 x {KB}: tau {tau:.4f}, kept {nnz}/{causal}, {layer_ms:.3f} ms/layer; dense run ...")
+        log(f"tiles: {dt} 128 x {KB}: tau {tau:.4f}, kept {nnz}/{causal}, {layer_ms:.3f} ms/layer; dense run ...")
         d_layer, d_run = time_layer(L, math.inf, True, args.dense_steps, 1, torch)
         dense = L.out
         diff = (sparse - dense).abs()
         fl = flop_counts(w, nnz)
-        row = dict(tiles=f"128x{KB}",
+        if dt == "fp8":  # QK^T of plain tiles on e4m3 MFMA, PV and the masked tiles on bf16 MFMA
+            busy = fl["kept"] / 2 / (PEAK_TFLOPS["fp8"] * 1e12) + (fl["kept"] / 2 + fl["corr"]) / (PEAK_TFLOPS["bf16"] * 1e12)
+        else:
+            busy = (fl["kept"] + fl["corr"]) / (PEAK_TFLOPS["bf16"] * 1e12)
+        row = dict(dtype=dt, tiles=f"128x{KB}",
                    kernel="attn_d128_kernel" if KB == 128 else "attn_d128_kernel (two 64-token blocks a tile)",
                    tau=round(tau, 5), density=round(nnz / causal, 5), nnz=nnz,
                    csr_bytes=4 * (batch.total_qblocks * base.hkv + 1 + nnz),
                    ms_per_layer=round(layer_ms, 4), prefill_run_ms=round(run_ms, 4),
-                   mfma_frac_run=round((fl["kept"] + fl["corr"]) / (run_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+                   mfma_frac_run=round(busy / (run_ms * 1e-3), 4),
                    dense_ms_per_layer=round(d_layer, 3), speedup_vs_dense=round(d_layer / layer_ms, 2),
                    dense_equiv_tflops=round(fl["dense"] / (layer_ms * 1e-3) / 1e12, 2),
                    err_rel_mean=float(diff.mean() / dense.abs().mean()), err_max=float(diff.max()))
@@ -524,12 +538,12 @@ def tile_study(args, torch, lib, synth):
         torch.cuda.empty_cache()
     if args.tiles_out:
         with open(args.tiles_out, "w") as f:
-            f.write("| tiles | kernel | tau | density | kept pairs | CSR bytes | ms/layer | prefill_run ms "
+            f.write("| dtype | tiles | kernel | tau | density | kept pairs | CSR bytes | ms/layer | prefill_run ms "
                     "| MFMA fraction of prefill_run | dense ms/layer | speedup vs dense "
                     "| mean abs err / mean abs O (vs dense) | max abs err |\n"
-                    "|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+                    "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
             for r in res["layer"]:
-                f.write(f"| {r['tiles']} | {r['kernel']} | {r['tau']} | {r['density']} | {r['nnz']} | {r['csr_bytes']} "
+                f.write(f"| {r['dtype']} | {r['tiles']} | {r['kernel']} | {r['tau']} | {r['density']} | {r['nnz']} | {r['csr_bytes']} "
                         f"| {r['ms_per_layer']} | {r['prefill_run_ms']} | {r['mfma_frac_run']} "
                         f"| {r['dense_ms_per_layer']} | {r['speedup_vs_dense']} | {r['err_rel_mean']:.4g} "
                         f"| {r['err_max']:.4g} |\n")

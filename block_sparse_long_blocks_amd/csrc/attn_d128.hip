@@ -1,5 +1,5 @@
-// Stage 2 for head_dim 128 and query blocks of 128 over KV blocks of 128
-// (bf16 or e4m3 inputs) or of 64 (bf16): block-sparse causal GQA attention
+// Stage 2 for head_dim 128 and query blocks of 128 over KV blocks of 128 or
+// of 64, bf16 or e4m3 inputs: block-sparse causal GQA attention
 // over the kept KV blocks plus the mean correction of every skipped block, in
 // one online softmax.
 //
@@ -46,7 +46,9 @@
 //    second's; V^T is kept as half tiles (128 d x 64 keys) and each lane
 //    takes its 16-byte chunk from the half its key positions belong to.  A
 //    row's last entry may be alone (second half masked); the diagonal mask
-//    is by position, one offset per half.
+//    is by position and the logit scale (e4m3: the block's K scale) per
+//    half; e4m3 K codes of every block are widened to bf16 rows, since a
+//    masked tile can hold any kept block beside a diagonal one.
 //  * The workgroups run work items built on the device (items_kernel):
 //    heaviest first, with the exact tiles of rows much heavier than the rest
 //    cut into chunks whose float32 partials combine_kernel merges.
@@ -176,30 +178,34 @@ __global__ __launch_bounds__(256) void vt_exact_kernel(PrepArgs a) {
 
 // e4m3 K codes of every block that is some query block's diagonal (the
 // blocks from the sequence's cached prefix length / B on), widened to bf16
-// rows (exact; the scale stays apart), zero past the sequence end.
+// rows (exact; the scale stays apart), zero past the sequence end.  HALF
+// (64-token KV blocks): every block, since a masked pair tile can hold any
+// kept block beside a diagonal one.
+template <bool HALF>
 __global__ __launch_bounds__(256) void kd_kernel(PrepArgs a) {
+  constexpr int KB = HALF ? 64 : kBlk;
   const int kb = blockIdx.x, g = blockIdx.y;
   const int s = find_seq(a.cu_kblocks, a.num_seqs, kb);
   const int J = kb - a.cu_kblocks[s];
   const int T = a.seqlens_k[s];
   const int P = T - (a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s]);
-  if (J < P / kBlk) return;
+  if (!HALF && J < P / kBlk) return;
   const int32_t* pt = a.page_table + (int64_t)s * a.max_pages;
   const int t = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < KB / 16; ++u) {
     const int id = t + 256 * u;
     const int r = id >> 4, ch = id & 15;  // row, 8-wide d chunk
-    const int pos = J * kBlk + r;
+    const int pos = J * KB + r;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (pos < T) {
       const uint2 c8 = *reinterpret_cast<const uint2*>(
-          a.k_pages + (((int64_t)pt[J] * kBlk + r) * a.hkv + g) * kD + ch * 8);  // one page per block
+          a.k_pages + (((int64_t)pt[J] * KB + r) * a.hkv + g) * kD + ch * 8);  // one page per block
       const f32x4 lo = e4m3x4_to_f32(c8.x), hi = e4m3x4_to_f32(c8.y);
       v = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
                      pack_bf16x2(hi[2], hi[3]));
     }
-    *reinterpret_cast<uint4*>(a.kd + (((int64_t)g * a.total_kblocks + kb) * kBlk + r) * kRowBytes + ch * 16) = v;
+    *reinterpret_cast<uint4*>(a.kd + (((int64_t)g * a.total_kblocks + kb) * KB + r) * kRowBytes + ch * 16) = v;
   }
 }
 
@@ -534,12 +540,15 @@ struct Wave {
         fr[read0<QK8>(n) + e] = *reinterpret_cast<const bf16x8*>(op_addr<QK8>(n, e, Kt, Vt, off0, off1, off8));
   }
 
-  // TWO: the tile's keys are two 64-token blocks; on the diagonal tq is the
-  // query's position minus the first block's first key, tq2 the same for the
-  // second block (very negative when the tile holds one block).
+  // TWO: the tile's keys are two 64-token blocks: scl2 is the logit scale of
+  // the second (steps NS/2 ..; e4m3 K scales differ per block); on the
+  // diagonal tq is the query's position minus the first block's first key,
+  // tq2 the same for the second block (very negative when the tile holds one
+  // block).
   template <bool MASKED, bool QK8, bool TWO = false, class Dma>
   __device__ __forceinline__ void tile(bf16x8 (&fr)[kRing], bool first, const uint8_t* Kt, const uint8_t* Vt,
-                                       int off0, int off1, const int (&off8)[4], float scl, Dma&& dma, int mode,
+                                       int off0, int off1, const int (&off8)[4], float scl, float scl2, Dma&& dma,
+                                       int mode,
                                        int tq, int tq2, int hf, float lb, float cbs, int J0, int diag,
                                        const uint32_t* kept) {
     bf16x8 pp[2] = {qf[0], qf[0]}, pc[2];
@@ -573,9 +582,9 @@ struct Wave {
       // region j+1: QK(j+1) (j < 3), PV(j-1) (j > 0), softmax(j)
       if (j == 0) region<1, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[0], dma);
       if (j == 1) region<2, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[1], dma);
-      if (j == 2) region<3, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[2], dma);
-      if (j == 3) region<4, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[3], dma);
-      soft_close<MASKED>(st, s, scl, first && j == 0, pc, M[j], cbs);
+      if (j == 2) region<3, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, TWO ? scl2 : scl, nb + lb, M[2], dma);
+      if (j == 3) region<4, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, TWO ? scl2 : scl, nb + lb, M[3], dma);
+      soft_close<MASKED>(st, s, (TWO && j >= NS / 2) ? scl2 : scl, first && j == 0, pc, M[j], cbs);
       pp[0] = pc[0];
       pp[1] = pc[1];
     }
@@ -591,11 +600,10 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* dst) {
 }
 
 // PAIR: 64-token KV blocks under 128-token query blocks, two blocks (two CSR
-// entries) to a 128-key tile (bf16 only).
+// entries) to a 128-key tile.
 template <bool FP8, bool PAIR>
 __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   constexpr int KB = PAIR ? 64 : kBlk;  // tokens of a KV block
-  static_assert(!(PAIR && FP8), "64-token KV blocks: bf16 only");
   static_assert(!PAIR || (kDmaWaves / 2) * kDmaRows == 64, "a DMA wave's rows lie in one 64-token block");
   // two K and two V^T buffers, as separate objects so that the compiler can
   // tell the DMA target from the buffers being read
@@ -796,12 +804,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
       }
       const int r0 = dma_row0(j);
       pl.fast = pages16 && r0 + kDmaRows - 1 < T;
-      if (FP8 && j == diag) {
+      if (FP8 && masked_exact(j, idx)) {
         // the diagonal block's K codes widened to bf16 rows (zero past the end)
         pl.fast = true;
+        const int64_t kdr = PAIR ? (mrow0 + half_of(j, wave >= kDmaWaves / 2)) * KB + r0 % KB
+                                 : (mrow0 + j) * kBlk + kDmaRows * wave;
 #pragma unroll
-        for (int hh = 0; hh < kDmaHalves; ++hh)
-          pl.kb[hh] = a.kd + ((mrow0 + j) * kBlk + kDmaRows * wave + 16 * hh) * kRowBytes;
+        for (int hh = 0; hh < kDmaHalves; ++hh) pl.kb[hh] = a.kd + (kdr + 16 * hh) * kRowBytes;
         pl.kstep = 1024;
         pl.kvo = voff;
       } else if (FP8) {
@@ -813,20 +822,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
         if (pl.fast) {
 #pragma unroll
           for (int hh = 0; hh < kDmaHalves; ++hh)
-            pl.kb[hh] = a.k_pages + (((int64_t)pg[0] * kBlk + kDmaRows * wave) * a.hkv + g) * kD;
+            pl.kb[hh] = a.k_pages + (((int64_t)pg[0] * KB + r0 % KB) * a.hkv + g) * kD;
           pl.kstep = 8 * tok8;
           pl.kvo = koff8;
         } else {
 #pragma unroll
           for (int p = 0; p < kDmaRows / 8; ++p) {
             const int r = min(r0 + 8 * p + (lane >> 3), T - 1);  // rows past the end repeat the last key
-            const uint8_t* ksrc = a.k_pages + (((int64_t)pt[r / kBlk] * kBlk + r % kBlk) * a.hkv + g) * kD +
+            const uint8_t* ksrc = a.k_pages + (((int64_t)pt[r / KB] * KB + r % KB) * a.hkv + g) * kD +
                                   16 * ((lane & 7) ^ (lane >> 3));
             dma16(ksrc, pl.kd + p * 1024);
           }
 #pragma unroll
-          for (int p = 0; p < kDmaRows / 4; ++p)
-            dma16(pl.vb + voff + 1024 * p, vd + p * kGS);
+          for (int p = 0; p < kDmaRows / 4; ++p) {
+            if constexpr (PAIR) dma16(pl.vbl + pl.vstep * p, vd + p * kGS);
+            else dma16(pl.vb + voff + 1024 * p, vd + p * kGS);
+          }
         }
       } else if (pl.fast) {
 #pragma unroll
@@ -920,9 +931,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   // (pgbv)
   const __amdgpu_buffer_rsrc_t rks =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.k_scale, (short)0, 0x7fffffff, kBufferFlags);
-  int ksv = 0, pgbv = 0;
+  int ksv = 0, pgbv = 0, ksvb = 0, pgbvb = 0;  // PAIR: the second block's
   if constexpr (FP8) {
-    if (0 < nexact) ksv = __builtin_amdgcn_raw_buffer_load_b32(rks, (ld_uniform(pt, j0) * a.hkv + g) * 4, 0, 0);
+    if (0 < nexact) {
+      ksv = __builtin_amdgcn_raw_buffer_load_b32(rks, (ld_uniform(pt, half_of(j0, 0)) * a.hkv + g) * 4, 0, 0);
+      if constexpr (PAIR)
+        ksvb = __builtin_amdgcn_raw_buffer_load_b32(rks, (ld_uniform(pt, half_of(j0, 1)) * a.hkv + g) * 4, 0, 0);
+    }
   }
   if (0 < nexact) {
     int pg0[kDmaHalves] = {};
@@ -993,7 +1008,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     }
   }
   if constexpr (FP8) {
-    if (1 < nexact) pgbv = __builtin_amdgcn_raw_buffer_load_b32(rpt, j1 * 4, 0, 0);
+    if (1 < nexact) {
+      pgbv = __builtin_amdgcn_raw_buffer_load_b32(rpt, half_of(j1, 0) * 4, 0, 0);
+      if constexpr (PAIR) pgbvb = __builtin_amdgcn_raw_buffer_load_b32(rpt, half_of(j1, 1) * 4, 0, 0);
+    }
   }
   if (1 < nexact && dma_wave) {
 #pragma unroll
@@ -1013,11 +1031,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     int j2;
     if constexpr (PAIR) j2 = idx + 2 < nexact ? pack(after_barrier(j2v), after_barrier(j2vb), idx + 2) : mean_of(idx + 2);
     else j2 = idx + 2 < nexact ? after_barrier(j2v) : mean_of(idx + 2);
-    float sclt = scl;
+    float sclt = scl, sclt2 = scl;
     if constexpr (FP8) {
-      if (idx < nexact) sclt = scl * __uint_as_float((uint32_t)after_barrier(ksv));
-      if (idx + 1 < nexact) ksv = __builtin_amdgcn_raw_buffer_load_b32(rks, (after_barrier(pgbv) * a.hkv + g) * 4, 0, 0);
-      if (idx + 2 < nexact) pgbv = __builtin_amdgcn_raw_buffer_load_b32(rpt, j2 * 4, 0, 0);
+      if (idx < nexact) {
+        sclt = scl * __uint_as_float((uint32_t)after_barrier(ksv));
+        if constexpr (PAIR) sclt2 = scl * __uint_as_float((uint32_t)after_barrier(ksvb));
+      }
+      if (idx + 1 < nexact) {
+        ksv = __builtin_amdgcn_raw_buffer_load_b32(rks, (after_barrier(pgbv) * a.hkv + g) * 4, 0, 0);
+        if constexpr (PAIR)
+          ksvb = __builtin_amdgcn_raw_buffer_load_b32(rks, (after_barrier(pgbvb) * a.hkv + g) * 4, 0, 0);
+      }
+      if (idx + 2 < nexact) {
+        pgbv = __builtin_amdgcn_raw_buffer_load_b32(rpt, half_of(j2, 0) * 4, 0, 0);
+        if constexpr (PAIR) pgbvb = __builtin_amdgcn_raw_buffer_load_b32(rpt, half_of(j2, 1) * 4, 0, 0);
+      }
     }
     DmaPlan pl;
     pl.fast = false;
@@ -1055,7 +1083,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
         for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, Vn);
       }
     } else if constexpr (!MASKED) {
-      ws.tile<false, FP8>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, 0, tq, 0, hf, 0.f, 0.f, 0, dlo, kept);
+      ws.tile<false, FP8, PAIR>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, 0, tq, 0, hf, 0.f, 0.f, 0,
+                                dlo, kept);
     } else {
       // mean tiles: weight of a KV block, its log2 in the exponent (cbs in score units)
       const float lbm = mode == 2 ? a.log2_block : 0.f;
@@ -1064,11 +1093,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
         const int qd = qpos0 + tq;
         const int tqa = qd - half_of(j0, 0) * KB;
         const int tqb = 2 * idx + 1 < ne ? qd - half_of(j0, 1) * KB : -(1 << 20);
-        ws.tile<true, false, true>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, mode, tqa, tqb, hf, lbm,
+        ws.tile<true, false, true>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, mode, tqa, tqb, hf, lbm,
                                    lbm / sclt, j0, dlo, kept);
       } else {
-        ws.tile<true, false>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, dma, mode, tq, 0, hf, lbm, lbm / sclt, j0,
-                             dlo, kept);
+        ws.tile<true, false>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt, dma, mode, tq, 0, hf, lbm, lbm / sclt,
+                             j0, dlo, kept);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -1406,11 +1435,17 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
   p.mt_cap = a.mt_cap;
   if (a.total_kblocks > 0) {
     const dim3 per_block((unsigned)a.total_kblocks, (unsigned)a.hkv);
-    if (fp8) {
+    const dim3 per_pair((unsigned)((a.total_kblocks + 1) / 2), (unsigned)a.hkv);
+    if (fp8 && a.pair) {
+      hipLaunchKernelGGL((vt_exact_kernel<true, true>), per_pair, dim3(256), 0, stream, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kd_kernel<true>, per_block, dim3(256), 0, stream, p);
+    } else if (fp8) {
       hipLaunchKernelGGL((vt_exact_kernel<true, false>), per_block, dim3(256), 0, stream, p);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kd_kernel, per_block, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(kd_kernel<false>, per_block, dim3(256), 0, stream, p);
     } else if (a.pair) {
       hipLaunchKernelGGL((vt_exact_kernel<false, true>), dim3((unsigned)((a.total_kblocks + 1) / 2), (unsigned)a.hkv),
                          dim3(256), 0, stream, p);
@@ -1444,7 +1479,9 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
   if (e != hipSuccess) return e;
   const int items_cap = a.rows + a.extra_cap;
   const unsigned grid = (unsigned)(((items_cap + 7) / 8) * 8 * a.slices);
-  if (fp8)
+  if (fp8 && a.pair)
+    hipLaunchKernelGGL((attn_d128_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (fp8)
     hipLaunchKernelGGL((attn_d128_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   else if (a.pair)
     hipLaunchKernelGGL((attn_d128_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, a);

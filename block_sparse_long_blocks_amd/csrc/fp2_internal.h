@@ -38,11 +38,11 @@ fp2_status check_kv(const fp2_kv* kv, const fp2_batch* b, const BatchInfo& info)
 
 size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads);
 // fp2_prefill_run runs the DMA kernel on V^T tiles for d = 128 and query
-// blocks of 128 over KV blocks of 128 (bf16 or e4m3) or of 64 (bf16, two to a
-// tile), and the register-staged kernel otherwise.
+// blocks of 128 over KV blocks of 128 or of 64 (two to a tile), bf16 or e4m3,
+// and the register-staged kernel otherwise.
 inline bool vt_path(int dtype, int head_dim, const BatchInfo& info) {
   return (dtype == FP2_BF16 || dtype == FP2_FP8_E4M3) && head_dim == 128 && info.qblock == 128 &&
-         (info.kvblock == 128 || (info.kvblock == 64 && dtype == FP2_BF16));
+         (info.kvblock == 128 || info.kvblock == 64);
 }
 
 // Byte offsets of the parts of the fp2_prefill_run workspace.

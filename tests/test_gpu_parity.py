@@ -72,17 +72,19 @@ SMALL = {
     "dec_fp8": _cfg("dec_fp8", (1024, 512), (0, 256), 8, 2, 128, 128, 64, dtype="fp8", kv_block=64),
     "dec_d64_p128": _cfg("dec_d64_p128", (512, 384), (128, 256), 8, 4, 64, 128, 128, kv_block=64),
     "dec_g8": _cfg("dec_g8", (700,), (384,), 16, 2, 128, 128, 64, kv_block=64),
-    # the same on the DMA kernel's pair tiles (bf16, d = 128): one query block after a long prefix
-    # (rows split into chunks), and pages of 24 tokens (per-lane DMA sources) with G = 1
+    # the same on the DMA kernel's pair tiles (d = 128): one query block after a long prefix (rows
+    # split into chunks; e4m3: masked pair tiles that hold prefix blocks), and pages of 24 tokens
+    # (per-lane DMA sources) with G = 1
     "dec_chunk": _cfg("dec_chunk", (6144,), (6016,), 8, 4, 128, 128, 128, kv_block=64),
     "dec_p24_g1": _cfg("dec_p24_g1", (900, 260), (128, 0), 2, 2, 128, 128, 24, kv_block=64),
+    "dec_chunk_fp8": _cfg("dec_chunk_fp8", (6144,), (6016,), 8, 4, 128, 128, 64, dtype="fp8", kv_block=64),
 }
 TAUS = {"tiny": (0.0, 0.005, 0.01, 0.02, 2.0), "varlen_p64": (0.0, 0.5, 3.0),
         "d64_b128_p16": (0.3, 3.0), "d128_b64_g8": (0.2, 2.0), "single_token": (0.0, 1.0),
         "fp8_varlen": (0.0, 0.5, 3.0), "d128_p24_g1": (0.0, 1.0), "d128_p8_g8": (0.0, 1.0),
         "chunk_after_prefix": (0.5, 1e9), "chunk_after_prefix_fp8": (0.5, 1e9), "d128_b64_p128": (0.0, 1.0),
         "dec_varlen": (0.0, 0.5, 3.0), "dec_fp8": (0.0, 0.5, 3.0), "dec_d64_p128": (0.3, 3.0), "dec_g8": (0.0, 1.0),
-        "dec_chunk": (0.5, 1e9), "dec_p24_g1": (0.0, 1.0)}
+        "dec_chunk": (0.5, 1e9), "dec_p24_g1": (0.0, 1.0), "dec_chunk_fp8": (0.5, 1e9)}
 
 _cache = {}
 
@@ -216,7 +218,7 @@ def test_cached_block_stats(name):
 
 
 @pytest.mark.parametrize("corr", [True, False])
-@pytest.mark.parametrize("name", ["varlen_p64", "fp8_varlen", "dec_varlen"])
+@pytest.mark.parametrize("name", ["varlen_p64", "fp8_varlen", "dec_varlen", "dec_fp8"])
 def test_split_rows_match_oracle(name, corr, monkeypatch):
     """Rows whose exact tiles are cut into chunks (FP2_MAX_CHUNK_TILES caps the
     chunk; the batch bounds it below by its tiles over its extra-item budget,
