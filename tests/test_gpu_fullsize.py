@@ -48,8 +48,8 @@ def run_full(name, corrections=(True,), out_dtype="bf16", kv_blk=0, tau=None):
     import block_sparse_long_blocks_amd as lib
     tau = TAUS[name]["tau"] if tau is None else tau
     cfg = synth.CONFIGS[name]
-    if kv_blk:
-        cfg = dataclasses.replace(cfg, kv_block=kv_blk)
+    if kv_blk:  # e4m3 scales are per page: pages of one KV block
+        cfg = dataclasses.replace(cfg, kv_block=kv_blk, page_size=kv_blk if cfg.dtype == "fp8" else cfg.page_size)
     w = synth.make_custom(cfg, tau=tau)
     L = lib.PrefillLayer(*lib.from_workload(w), out_dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16)
     L.stats()
@@ -110,16 +110,17 @@ def test_fullsize_parity(name):
     print(f"{name}: {len(rows)} sampled rows, max abs err {worst:.4f} (bf16 output)")
 
 
-def test_fullsize_decoupled_tiles():
-    """The 128K bf16 data with 128-token query blocks over 64-token KV blocks, on the
-    attention kernel's pair tiles (as `bench.py --tiles` times it); tau 3.9 keeps about
-    5% of the 64-token causal pairs."""
-    print("decoupled 128K: generating and running", flush=True)
-    w, seqs, plan, tau, gpu, outs = run_full("c128k_bf16", kv_blk=64, tau=3.9)
+@pytest.mark.parametrize("name", ["c128k_bf16", "c128k_fp8"])
+def test_fullsize_decoupled_tiles(name):
+    """The 128K data with 128-token query blocks over 64-token KV blocks, on the attention
+    kernel's pair tiles (as `bench.py --tiles` times it); tau 3.9 keeps about 5% of the
+    64-token causal pairs."""
+    print(f"decoupled {name}: generating and running", flush=True)
+    w, seqs, plan, tau, gpu, outs = run_full(name, kv_blk=64, tau=3.9)
     check_stats_and_plan(w, seqs, plan, gpu)
     rows = _rows(w, seed=9)
     worst = check_rows(w, seqs, gpu, outs[True], True, rows, TOL[w.cfg.dtype])
-    print(f"decoupled 128K: {len(rows)} sampled rows, max abs err {worst:.4f} (bf16 output)")
+    print(f"decoupled {name}: {len(rows)} sampled rows, max abs err {worst:.4f} (bf16 output)")
 
 
 def test_fullsize_extreme_with_and_without_correction():
