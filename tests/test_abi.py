@@ -114,6 +114,9 @@ def test_sequence_length_limits():
     rejected on the host (the kept-block bitmask and the plan's score row live in LDS)."""
     assert lib.fp2_plan_max_nnz(_batch([1 << 21], [256]), 1) == 16383 + 16384  # diagonals 16382, 16383
     assert lib.fp2_plan_max_nnz(_batch([(1 << 21) + 128], [256]), 1) == -1
+    # 64-token KV blocks under 128-token query blocks: 16,384 of them is 2^20 keys
+    assert lib.fp2_plan_max_nnz(_batch([1 << 20], [256], 128, 64), 1) == 16382 + 16384  # runs 16380-1, 16382-3
+    assert lib.fp2_plan_max_nnz(_batch([(1 << 20) + 64], [320], 128, 64), 1) == -1
 
 
 def test_block_stats_cache_rows_and_checks():

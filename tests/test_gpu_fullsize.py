@@ -144,16 +144,19 @@ def test_fullsize_extreme_with_and_without_correction():
     assert err[True] < err[False]
 
 
-def test_max_kv_blocks():
-    """The largest sequence the library accepts: 2^21 keys = 16,384 KV blocks of 128 (the kept-block
-    bitmask, the score row of the plan and the mean-token list at their limits), two query blocks at
-    the end of a 2,096,896-token cached prefix, 4 query / 1 KV head, d 128, bf16, unstructured
-    N(0,1) data with tau for a few percent: block means, kept lists and attention (with and without
-    the correction, whose mean-token tiles then span all 16,383 skippable blocks) against the oracle."""
+@pytest.mark.parametrize("kvb", [128, 64])
+def test_max_kv_blocks(kvb):
+    """The largest sequence the library accepts: 16,384 KV blocks (2^21 keys in blocks of 128, 2^20
+    in blocks of 64 under 128-token query blocks: the kept-block bitmask, the score row of the plan
+    and the mean-token list at their limits), two query blocks at the end of the cached prefix,
+    4 query / 1 KV head, d 128, bf16, unstructured N(0,1) data with tau for a few percent: block
+    means, kept lists and attention (with and without the correction, whose mean-token tiles then
+    span all skippable blocks) against the oracle."""
     import block_sparse_long_blocks_amd as lib
-    T = 1 << 21
+    T = 16384 * kvb
     cfg = synth.Config(name="max_kv_blocks", seqlens=(T,), prefixes=(T - 256,), hq=4, hkv=1, d=128, block=128,
-                       page_size=128, dtype="bf16", structure="plain", tau=0.008, seed=13)
+                       page_size=128, dtype="bf16", structure="plain", tau=0.008, seed=13,
+                       kv_block=0 if kvb == 128 else kvb)
     w = synth.make_custom(cfg)
     assert w.total_kblocks == 16384
     print("\nmax_kv_blocks: inputs generated", flush=True)
@@ -173,7 +176,7 @@ def test_max_kv_blocks():
     torch.cuda.empty_cache()
     print("max_kv_blocks: GPU calls done", flush=True)
     seqs = decoded_seqs(w)
-    plan = O.plan_batch(seqs, cfg.block, cfg.tau)
+    plan = O.plan_batch(seqs, cfg.block, cfg.tau, BK=kvb)
     print("max_kv_blocks: oracle plan done", flush=True)
     check_stats_and_plan(w, seqs, plan, (rp, ci, kb, vb))
     assert 0 < rp[-1] < w.causal_pairs()  # sparse: the correction has skipped blocks to cover
