@@ -325,46 +325,53 @@ def test_empty_batch_and_empty_sequence():
     assert int(Le.nnz.item()) == 0 and int(Le.row_ptr[0].item()) == 0
 
 
+@pytest.mark.parametrize("kvb", [128, 64])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_reference_max_refresh_in_every_tile_kind(dtype):
+def test_reference_max_refresh_in_every_tile_kind(dtype, kvb):
     """Scores that climb by far more than 64 log2 units along the keys (about 2 per
-    key), and one block (2) lying far above every other, under a hand-made mask
-    (block 0, block I//2 and the diagonal per query block I): the running
-    reference max must be raised after the first step inside exact tiles,
-    diagonal tiles and mean-token tiles (block 2 skipped, its mean token on top),
-    and the result must still match the oracle on the same mask.  Here one or two
-    keys carry each row, so the kernel's one systematic error shows whole: PV
-    takes the probabilities rounded to bf16 while the row sum adds them in
-    float32, which moves O by at most 2^-9 max|v|; the bound adds that term.
-    e4m3: one scale per 128-token block and head (query block and head for Q)."""
+    key), and one 128-token span (keys 256-383) lying far above every other, under a
+    hand-made mask (block 0, the block at query block I//2's start and the diagonal
+    run per query block I): the running reference max must be raised after the first
+    step inside exact tiles, diagonal tiles and mean-token tiles (the high span
+    skipped, its mean tokens on top), and the result must still match the oracle on
+    the same mask.  Here one or two keys carry each row, so the kernel's one
+    systematic error shows whole: PV takes the probabilities rounded to bf16 while
+    the row sum adds them in float32, which moves O by at most 2^-9 max|v|; the
+    bound adds that term.  e4m3: one scale per KV block and head (query block and
+    head for Q).  kvb = 64: 64-token KV blocks under 128-token query blocks, two to a
+    tile, each half with its own K scale; rows of three or four entries give full and
+    lone-entry pair tiles."""
     import block_sparse_long_blocks_amd as lib
     rng = np.random.default_rng(5)
     B, d, hq, hkv, T = 128, 128, 8, 2, 1024
+    r = B // kvb
     pos = np.arange(T, dtype=np.float64)
     q = 1.0 + 0.25 * rng.standard_normal((T, hq, d))
     k = (0.125 * pos)[:, None, None] + 0.25 * rng.standard_normal((T, hkv, d))
     k[2 * B:3 * B] += 200.0
     v = rng.standard_normal((T, hkv, d))
-    nb = T // B
+    nq, nb = T // B, T // kvb
     page_table = np.arange(nb, dtype=np.int32)[None, :]
     if dtype == "bf16":
         qc, kc, vc = (synth.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
         qs = ks = vs = None
     else:
-        (qc, qs), (kc, ks), (vc, vs) = (synth.quantize_blocks_e4m3(x.astype(np.float32), B) for x in (q, k, v))
-    batch, queries, kv = lib.from_arrays(B, [T], [T], qc, qs, kc.reshape(nb, B, hkv, d),
-                                         vc.reshape(nb, B, hkv, d), page_table, k_scale=ks, v_scale=vs)
-    keep = np.zeros((hkv, nb, nb), dtype=bool)
-    for i in range(nb):
-        keep[:, i, [0, i // 2, i]] = True
+        qc, qs = synth.quantize_blocks_e4m3(q.astype(np.float32), B)
+        (kc, ks), (vc, vs) = (synth.quantize_blocks_e4m3(x.astype(np.float32), kvb) for x in (k, v))
+    batch, queries, kv = lib.from_arrays(B, [T], [T], qc, qs, kc.reshape(nb, kvb, hkv, d),
+                                         vc.reshape(nb, kvb, hkv, d), page_table, k_scale=ks, v_scale=vs,
+                                         kv_block=0 if kvb == B else kvb)
+    keep = np.zeros((hkv, nq, nb), dtype=bool)
+    for i in range(nq):
+        keep[:, i, [0, r * (i // 2)] + list(range(r * i, r * i + r))] = True
     rp = [0]
     ci = []
     for g in range(hkv):
-        for i in range(nb):
+        for i in range(nq):
             cols = np.nonzero(keep[g, i])[0]
             ci.extend(cols.tolist())
             rp.append(len(ci))
-    dec = O.decode_sequence(dtype, B, qc, qs, kc, ks, vc, vs)
+    dec = O.decode_sequence(dtype, B, qc, qs, kc, ks, vc, vs, kv_block=kvb)
     for corr in (True, False):
         L = lib.PrefillLayer(batch, queries, kv, out_dtype=torch.float32)
         L.stats()
@@ -373,5 +380,5 @@ def test_reference_max_refresh_in_every_tile_kind(dtype):
         L.attend(corr)
         torch.cuda.synchronize()
         got = L.out[:T].cpu().numpy().astype(np.float64)
-        ref = O.run_batch([tuple(dec)], B, 0.0, corr, keeps=[keep])["out"]
+        ref = O.run_batch([tuple(dec)], B, 0.0, corr, keeps=[keep], BK=kvb)["out"]
         check_out(got, ref, TOL[dtype], "f32", extra=2.0 ** -9 * float(np.abs(dec[2]).max()))
