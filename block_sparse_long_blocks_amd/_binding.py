@@ -19,7 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp2.so"
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
-        f"{_LIB_PATH} is not built; run `python -m block_sparse_long_blocks_amd.build` "
+        f"{_LIB_PATH} is not built; run `python block_sparse_long_blocks_amd/build.py` from the repository root "
         "(hipcc --offload-arch=gfx950).  There is no fallback implementation.")
 _lib = ctypes.CDLL(_LIB_PATH)
 

@@ -1,6 +1,7 @@
 """Build libfp2.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-Usage: python -m block_sparse_long_blocks_amd.build [--debug]
+Usage: python block_sparse_long_blocks_amd/build.py [--debug]   (from the repository root; running it as a
+module would import the package, which needs the library first)
 """
 import os
 import subprocess
