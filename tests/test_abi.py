@@ -194,3 +194,28 @@ def test_no_fallback_without_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError, match="not built"):
         spec.loader.exec_module(mod)
+
+
+def test_build_entry_builds_before_importing_the_package(tmp_path):
+    """__graft_entry__.build() must work where libfp2.so is not built yet: it may not import the
+    package (whose import loads the library) before the build step has run.  The build step is a
+    stand-in here that copies the library built in this tree into the copy."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "block_sparse_long_blocks_amd"
+    shutil.copytree(os.path.join(ROOT, "block_sparse_long_blocks_amd"), pkg,
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    shutil.copy(os.path.join(ROOT, "__graft_entry__.py"), tmp_path)
+    (pkg / "build.py").write_text(
+        "import os, shutil\n"
+        f"SRC = {lib.library_path()!r}\n"
+        "def build(debug=False):\n"
+        "    dst = os.path.join(os.path.dirname(os.path.abspath(__file__)), 'libfp2.so')\n"
+        "    shutil.copy(SRC, dst)\n"
+        "    return dst\n")
+    assert not (pkg / "libfp2.so").exists()
+    r = subprocess.run([sys.executable, "-c", "import __graft_entry__ as g; g.build()"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "built" in r.stdout
