@@ -8,6 +8,7 @@ import pytest
 
 import oracle.fp2_oracle as ref_mod
 from test_oracle import brute_force, _rand_seq, _torch_sdpa
+from test_oracle_decode import _codes, _expect, _scales
 
 
 def _mutant(old: str, new: str):
@@ -108,8 +109,34 @@ def pin_threshold_decoupled(mod):
         assert list(np.nonzero(res["keep"][0][g, i])[0]) == js
 
 
+def pin_decode_e4m3(mod):
+    # 128-token query blocks over 64-token KV blocks after a cached prefix
+    rng = np.random.default_rng(23)
+    block, kv_block, P, n, Hq, Hkv, d = 128, 64, 128, 200, 4, 2, 4
+    T = P + n
+    q, k, v = _codes(rng, (n, Hq, d)), _codes(rng, (T, Hkv, d)), _codes(rng, (T, Hkv, d))
+    qs = _scales(-(-n // block), Hq, 0.0)
+    ks = _scales(-(-T // kv_block), Hkv, 100.0)
+    vs = _scales(-(-T // kv_block), Hkv, 1000.0)
+    Q, K, V = mod.decode_sequence("fp8", block, q, qs, k, ks, v, vs, kv_block=kv_block)
+    np.testing.assert_array_equal(Q, _expect(q, qs, block))
+    np.testing.assert_array_equal(K, _expect(k, ks, kv_block))
+    np.testing.assert_array_equal(V, _expect(v, vs, kv_block))
+
+
+def pin_keep_from_csr(mod):
+    # two sequences (2 and 1 query blocks, 3 and 2 KV blocks), two KV heads
+    rows = [[0], [0, 2], [0, 1], [0, 1], [1, 2], [1]]
+    row_ptr = np.cumsum([0] + [len(r) for r in rows])
+    col_idx = np.array([j for r in rows for j in r])
+    keeps = mod.keep_from_csr(row_ptr, col_idx, 2, [2, 1], [3, 2])
+    got = [sorted(np.nonzero(keeps[s][g, i])[0].tolist())
+           for g in range(2) for s, nqb in enumerate([2, 1]) for i in range(nqb)]
+    assert got == rows
+
+
 PINS = [pin_brute, pin_dense, pin_identical_keys, pin_tau_zero, pin_prefix, pin_brute_decoupled,
-        pin_threshold_decoupled]
+        pin_threshold_decoupled, pin_decode_e4m3, pin_keep_from_csr]
 
 MUTATIONS = [
     ("surrogate weight 1 instead of B", "* c + logB", "* c"),
@@ -128,6 +155,14 @@ MUTATIONS = [
     ("scores stop at the first diagonal block", "s[g, i, :hi + 1] = full[i, :hi + 1]",
      "s[g, i, :hi] = full[i, :hi]"),
     ("exp base 2", "w = np.exp(L - m)", "w = np.exp2(L - m)"),
+    ("threshold above the row max", "thr = (rowmax - t32)", "thr = (rowmax + t32)"),
+    ("K/V scales indexed by the query block", "kb = kv_block or block", "kb = block"),
+    ("scales taken per token", "tok_block = np.arange(T) // block",
+     "tok_block = np.minimum(np.arange(T), scales.shape[0] - 1)"),
+    ("CSR row base off by one sequence", "r = g * total_qb + base + i\n                keep[g, i",
+     "r = g * total_qb + i\n                keep[g, i"),
+    ("CSR rows read head-minor", "r = g * total_qb + base + i\n                keep[g, i",
+     "r = (base + i) * Hkv + g\n                keep[g, i"),
 ]
 
 
