@@ -102,6 +102,7 @@ fp2_status fp2_plan_mask(const fp2_batch* batch, const fp2_q* q, int32_t num_kv_
   fp2_status st = check_batch(batch, &info);
   if (st != FP2_OK) return st;
   if ((st = check_q(q, num_kv_heads, info, batch->block)) != FP2_OK) return st;
+  if ((st = check_index_range(info, num_kv_heads)) != FP2_OK) return st;
   if (std::isnan(tau)) return fail(FP2_ERR_INVALID, "tau is NaN");
   if (!nnz) return fail(FP2_ERR_INVALID, "nnz is NULL");
   if (info.total_qblocks > 0) {
@@ -147,6 +148,7 @@ fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv*
   if (st != FP2_OK) return st;
   if ((st = check_kv(kv, batch, info)) != FP2_OK) return st;
   if ((st = check_q(q, kv->num_kv_heads, info, batch->block)) != FP2_OK) return st;
+  if ((st = check_index_range(info, kv->num_kv_heads)) != FP2_OK) return st;
   if (q->dtype != kv->dtype) return fail(FP2_ERR_UNSUPPORTED, "q and kv dtypes differ");
   if (q->head_dim != kv->head_dim) return fail(FP2_ERR_INVALID, "q and kv head_dim differ");
   if (mean_correction != 0 && mean_correction != 1)

@@ -35,6 +35,9 @@ const char* last_error();
 fp2_status check_batch(const fp2_batch* b, BatchInfo* info);
 fp2_status check_q(const fp2_q* q, int num_kv_heads, const BatchInfo& info, int block);
 fp2_status check_kv(const fp2_kv* kv, const fp2_batch* b, const BatchInfo& info);
+// The CSR's row_ptr, col_idx and nnz are int32: rows and entries (the causal
+// pair count, reached at tau = +inf) must stay below 2^31.
+fp2_status check_index_range(const BatchInfo& info, int num_kv_heads);
 
 size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads);
 // fp2_prefill_run runs the DMA kernel on V^T tiles for d = 128 and query

@@ -74,6 +74,18 @@ fp2_status check_batch(const fp2_batch* b, BatchInfo* info) {
   return FP2_OK;
 }
 
+fp2_status check_index_range(const BatchInfo& info, int num_kv_heads) {
+  const long long kMax = (1LL << 31) - 1;
+  if (info.total_qblocks * num_kv_heads + 1 > kMax)
+    return fail(FP2_ERR_UNSUPPORTED, "total_qblocks * num_kv_heads = " + S(info.total_qblocks * num_kv_heads) +
+                                         " CSR rows do not fit 32-bit row indices");
+  if (info.causal_pairs * num_kv_heads > kMax)
+    return fail(FP2_ERR_UNSUPPORTED, "the batch has " + S(info.causal_pairs * num_kv_heads) +
+                                         " causal (query block, KV block, KV head) pairs; the CSR holds at most "
+                                         "2^31 - 1 entries");
+  return FP2_OK;
+}
+
 fp2_status check_q(const fp2_q* q, int num_kv_heads, const BatchInfo& info, int block) {
   if (!q) return fail(FP2_ERR_INVALID, "q is NULL");
   if (q->dtype != FP2_BF16 && q->dtype != FP2_FP8_E4M3)

@@ -159,7 +159,10 @@ fp2_status fp2_gather_block_stats(const fp2_batch *batch, const fp2_kv *kv,
 size_t fp2_plan_workspace_bytes(const fp2_batch *batch, int32_t num_kv_heads);
 
 /* Largest possible number of kept entries: the causal (query block, KV
- * block, KV head) count.  col_capacity must be at least this. */
+ * block, KV head) count.  col_capacity must be at least this.  row_ptr,
+ * col_idx and nnz are int32: fp2_plan_mask and fp2_prefill_run return
+ * FP2_ERR_UNSUPPORTED when this count, or the row count
+ * num_kv_heads * total_qblocks + 1, exceeds 2^31 - 1. */
 int64_t fp2_plan_max_nnz(const fp2_batch *batch, int32_t num_kv_heads);
 
 /* Stage 1b - pattern discovery and max-based thresholding (Figure 3,

@@ -119,6 +119,27 @@ def test_sequence_length_limits():
     assert lib.fp2_plan_max_nnz(_batch([(1 << 20) + 64], [320], 128, 64), 1) == -1
 
 
+def test_int32_csr_limit():
+    """row_ptr, col_idx and nnz are int32: two 2^21-token sequences with 8 KV heads have
+    2 * 16384 * 16385 / 2 * 8 = 2,147,614,720 causal pairs > 2^31 - 1, so a dense plan
+    would wrap; the host rejects the batch before any launch.  One sequence fits."""
+    f32 = torch.zeros(16)
+    i32 = torch.zeros(16, dtype=torch.int32)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    big = _batch([1 << 21, 1 << 21], [1 << 21, 1 << 21])
+    assert lib.fp2_plan_max_nnz(big, 8) == 2 * 16384 * 16385 // 2 * 8 > (1 << 31) - 1
+    q = lib.Queries(torch.zeros((1, 32, 128), dtype=torch.bfloat16))  # pointers only: nothing is launched
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_plan_mask, big, q, 8, f32, math.inf, i32, i32, i32, ws,
+            match="2\\^31")
+    kv = _kv(hkv=8, maxp=16384)
+    out = torch.zeros(8)
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_prefill_run, big, q, kv, i32, i32, f32, f32, False, out, ws,
+            match="2\\^31")
+    # one such sequence is 1,073,807,360 pairs: past the index check, stopped by the capacity check
+    one = _batch([1 << 21], [1 << 21])
+    _expect(lib.FP2_ERR_CAPACITY, lib.fp2_plan_mask, one, q, 8, f32, math.inf, i32, i32, i32, ws)
+
+
 def test_block_stats_cache_rows_and_checks():
     """The paged block-stats cache: one row per KV block a page holds; page sizes that do not
     divide B (or the reverse) are unsupported; bad arguments are rejected before any launch."""
