@@ -285,7 +285,7 @@ def stats_cache_timing(L, args, torch, lib):
 def chunked_prefill_case(args, torch, lib, synth):
     """One 128-token query chunk after a 130944-token cached prefix (1 query
     block, so 8 CSR rows of up to 1024 blocks): fp2_prefill_run with the heavy
-    rows split into chunks (the default) and with FP2_MAX_CHUNK_TILES=-1."""
+    rows split into chunks (the default) and with splitting turned off (max_chunk_tiles = -1)."""
     rows = []
     for dtype in ("bf16", "fp8"):
         log(f"chunked prefill case: generating the {dtype} layer ...")
@@ -299,11 +299,8 @@ def chunked_prefill_case(args, torch, lib, synth):
             L.plan(tau)
             torch.cuda.synchronize()
             res = {}
-            for key, env in (("ms_split", None), ("ms_nosplit", "-1")):
-                if env is None:
-                    os.environ.pop("FP2_MAX_CHUNK_TILES", None)
-                else:
-                    os.environ["FP2_MAX_CHUNK_TILES"] = env
+            for key, cap in (("ms_split", 0), ("ms_nosplit", -1)):
+                L.max_chunk_tiles = cap
                 for _ in range(args.warmup):
                     L.attend(True)
                 torch.cuda.synchronize()
@@ -314,7 +311,7 @@ def chunked_prefill_case(args, torch, lib, synth):
                 e1.record()
                 torch.cuda.synchronize()
                 res[key] = round(e0.elapsed_time(e1) / args.steps, 4)
-            os.environ.pop("FP2_MAX_CHUNK_TILES", None)
+            L.max_chunk_tiles = 0
             rows.append(dict(dtype=dtype, tau=tau if math.isfinite(tau) else "inf", nnz=int(L.nnz.item()), **res,
                              ratio=round(res["ms_nosplit"] / res["ms_split"], 2), **stats_cache_timing(L, args, torch, lib)))
             log("chunked prefill:", json.dumps(rows[-1]))

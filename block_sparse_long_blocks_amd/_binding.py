@@ -74,8 +74,8 @@ _lib.fp2_run_workspace_bytes.argtypes = [ctypes.POINTER(CBatch), ctypes.c_int32,
                                          ctypes.c_int]
 _lib.fp2_run_workspace_bytes.restype = ctypes.c_size_t
 _lib.fp2_prefill_run.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CQ), ctypes.POINTER(CKV), _p, _p,
-                                 _p, _p, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _p, _p, ctypes.c_size_t,
-                                 _p]
+                                 _p, _p, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _p, ctypes.c_int32, _p,
+                                 ctypes.c_size_t, _p]
 _lib.fp2_prefill_run.restype = ctypes.c_int
 _lib.fp2_last_error.argtypes = []
 _lib.fp2_last_error.restype = ctypes.c_char_p
@@ -250,15 +250,17 @@ def fp2_run_workspace_bytes(batch: Batch, num_q_heads: int, num_kv_heads: int, h
 
 def fp2_prefill_run(batch: Batch, q: Queries, kv: KVCache, row_ptr: torch.Tensor, col_idx: torch.Tensor,
                     kbar: torch.Tensor, vbar: torch.Tensor, mean_correction: bool, out: torch.Tensor,
-                    workspace: torch.Tensor, softmax_scale: Optional[float] = None, stream=None):
+                    workspace: torch.Tensor, softmax_scale: Optional[float] = None, stream=None,
+                    max_chunk_tiles: int = 0):
+    """max_chunk_tiles: 0 = the library's choice, > 0 caps a work item's exact tiles, < 0 never splits rows."""
     b, qc, k = batch.c, q.c, kv.c
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(q.q.shape[2])
     out_dtype = FP2_OUT_F32 if out.dtype == torch.float32 else FP2_OUT_BF16
     _check(_lib.fp2_prefill_run(ctypes.byref(b), ctypes.byref(qc), ctypes.byref(k), _ptr(row_ptr),
                                 _ptr(col_idx), _ptr(kbar), _ptr(vbar), int(bool(mean_correction)),
-                                ctypes.c_float(softmax_scale), out_dtype, _ptr(out), _ptr(workspace),
-                                workspace.numel(), _stream(stream)))
+                                ctypes.c_float(softmax_scale), out_dtype, _ptr(out), int(max_chunk_tiles),
+                                _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def library_path() -> str:

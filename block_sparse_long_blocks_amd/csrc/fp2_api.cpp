@@ -21,7 +21,7 @@ hipError_t launch_plan(const fp2_batch* b, const fp2_q* q, int hkv, const BatchI
 hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, const BatchInfo& info,
                           const int32_t* row_ptr, const int32_t* col_idx, const float* kbar,
                           const float* vbar, int correction, float softmax_scale, int out_f32,
-                          void* out, void* workspace, hipStream_t stream);
+                          void* out, int max_chunk_tiles, void* workspace, hipStream_t stream);
 
 static fp2_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return FP2_OK;
@@ -141,8 +141,8 @@ size_t fp2_run_workspace_bytes(const fp2_batch* batch, int32_t num_q_heads, int3
 fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv* kv,
                            const int32_t* row_ptr, const int32_t* col_idx, const float* kbar,
                            const float* vbar, int32_t mean_correction, float softmax_scale,
-                           fp2_out_dtype out_dtype, void* out, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           fp2_out_dtype out_dtype, void* out, int32_t max_chunk_tiles, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   BatchInfo info;
   fp2_status st = check_batch(batch, &info);
   if (st != FP2_OK) return st;
@@ -168,8 +168,8 @@ fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv*
                                         std::to_string(wneed) + " bytes");
   }
   return hip_status(launch_prefill(batch, q, kv, info, row_ptr, col_idx, kbar, vbar,
-                                   mean_correction, softmax_scale, out_dtype == FP2_OUT_F32, out, workspace,
-                                   (hipStream_t)stream),
+                                   mean_correction, softmax_scale, out_dtype == FP2_OUT_F32, out, max_chunk_tiles,
+                                   workspace, (hipStream_t)stream),
                     "fp2_prefill_run launch");
 }
 

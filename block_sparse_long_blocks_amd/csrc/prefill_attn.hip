@@ -572,7 +572,7 @@ hipError_t launch_attn_dt(int D, int BLK, const AttnArgs& a, unsigned grid, hipS
 hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, const BatchInfo& info,
                           const int32_t* row_ptr, const int32_t* col_idx, const float* kbar,
                           const float* vbar, int correction, float softmax_scale, int out_f32,
-                          void* out, void* workspace, hipStream_t stream) {
+                          void* out, int max_chunk_tiles, void* workspace, hipStream_t stream) {
   if (info.total_qblocks == 0) return hipSuccess;
   const int D = q->head_dim, BLK = info.kvblock, QB = info.qblock, hkv = kv->num_kv_heads;
   const bool vt = vt_path(q->dtype, D, info);
@@ -612,14 +612,10 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.counters = reinterpret_cast<int32_t*>(wsb + L.counters);
   a.part = reinterpret_cast<float*>(wsb + L.part);
   a.extra_cap = (int)L.extra_cap;
-  // FP2_MAX_CHUNK_TILES (optional): > 0 caps the exact tiles of one work item
-  // below the batch's own choice, < 0 turns the splitting of rows off
-  a.chunk_cap = 0;
-  if (const char* env = std::getenv("FP2_MAX_CHUNK_TILES")) {
-    const int v = std::atoi(env);
-    if (v < 0) a.extra_cap = 0;
-    a.chunk_cap = std::max(0, v);
-  }
+  // max_chunk_tiles > 0 caps the exact tiles of one work item below the
+  // batch's own choice, < 0 turns the splitting of rows off
+  if (max_chunk_tiles < 0) a.extra_cap = 0;
+  a.chunk_cap = std::max(0, max_chunk_tiles);
   a.mt_cap = (int)L.mt_cap;
   a.out = out;
   a.out_f32 = out_f32;

@@ -32,6 +32,7 @@ class PrefillLayer:
         self.run_ws = torch.empty(max(1, fp2_run_workspace_bytes(batch, q.q.shape[1], hkv, d, kv.dtype)), dtype=torch.uint8, device=dev)
         self.out = torch.empty((max(1, batch.total_q), q.q.shape[1], d), dtype=out_dtype, device=dev)
         self.scores = torch.empty((rows, max(1, batch.max_kblocks)), **f32) if with_scores else None
+        self.max_chunk_tiles = 0  # fp2_prefill_run's chunk cap: 0 library's choice, > 0 cap, < 0 no split
 
     def stats(self, stream=None):
         fp2_block_stats(self.batch, self.kv, self.kbar, self.vbar, stream)
@@ -42,7 +43,7 @@ class PrefillLayer:
 
     def attend(self, correction: bool, stream=None, softmax_scale: Optional[float] = None):
         fp2_prefill_run(self.batch, self.q, self.kv, self.row_ptr, self.col_idx, self.kbar, self.vbar,
-                        correction, self.out, self.run_ws, softmax_scale, stream)
+                        correction, self.out, self.run_ws, softmax_scale, stream, self.max_chunk_tiles)
 
     def __call__(self, tau: float, correction: bool, stream=None):
         self.stats(stream)

@@ -152,9 +152,10 @@ def test_plan_parity(name):
                                                              w.cfg.block, kv_block(w))]) * w.cfg.hkv
 
 
-def _attention_case(name, tau, corr, pad_fill="zero", out_dtype="bf16"):
+def _attention_case(name, tau, corr, pad_fill="zero", out_dtype="bf16", max_chunk_tiles=0):
     w, seqs = workload(name, pad_fill)
     L = layer(w, out_dtype=out_dtype)
+    L.max_chunk_tiles = max_chunk_tiles
     out = L(tau, corr)
     torch.cuda.synchronize()
     rp, ci = L.csr_host()
@@ -219,15 +220,14 @@ def test_cached_block_stats(name):
 
 @pytest.mark.parametrize("corr", [True, False])
 @pytest.mark.parametrize("name", ["varlen_p64", "fp8_varlen", "dec_varlen", "dec_fp8"])
-def test_split_rows_match_oracle(name, corr, monkeypatch):
-    """Rows whose exact tiles are cut into chunks (FP2_MAX_CHUNK_TILES caps the
-    chunk; the batch bounds it below by its tiles over its extra-item budget,
+def test_split_rows_match_oracle(name, corr):
+    """Rows whose exact tiles are cut into chunks (fp2_prefill_run's
+    max_chunk_tiles caps the chunk; the batch bounds it below by its tiles over its extra-item budget,
     4 tiles here) run as separate work items whose float32 partials (O, the
     reference max, the row sum) a combine kernel merges: the result stays
     within the bar of the oracle, and differs in its last bits from the
     unsplit run (so the split path really ran)."""
     for tau in (math.inf, 0.5):
-        monkeypatch.delenv("FP2_MAX_CHUNK_TILES", raising=False)
         whole, ref, w, L = _attention_case(name, tau, corr, out_dtype="f32")
         rp, _ = L.csr_host()
         extra_cap = min(256, -(-w.causal_pairs() // 4))
@@ -237,8 +237,7 @@ def test_split_rows_match_oracle(name, corr, monkeypatch):
         if tau != math.inf and int(tiles.max()) <= chunk:
             continue  # no row long enough to split at this threshold
         assert int(tiles.max()) > chunk  # some row is split
-        monkeypatch.setenv("FP2_MAX_CHUNK_TILES", "2")
-        split, ref2, _, _ = _attention_case(name, tau, corr, out_dtype="f32")
+        split, ref2, _, _ = _attention_case(name, tau, corr, out_dtype="f32", max_chunk_tiles=2)
         assert np.array_equal(ref, ref2)
         check_out(split, ref, TOL[w.cfg.dtype], "f32")
         check_out(whole, ref, TOL[w.cfg.dtype], "f32")
