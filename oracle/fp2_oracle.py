@@ -247,7 +247,7 @@ def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, keep: np.ndarray, B: int
         keys = np.concatenate([np.arange(j * BK, min((j + 1) * BK, T)) for j in kept])
         qpos = P + np.arange(t0, t1)                       # absolute query positions
         Qb = Q[t0:t1, g * G:(g + 1) * G, :]               # [nt, G, d]
-        logit = np.einsum("tgd,kd->tgk", Qb, K[keys, g, :]) * c
+        logit = (Qb @ K[keys, g, :].T) * c                # [nt, G, nk]
         visible = keys[None, :] <= qpos[:, None]          # [nt, nk]
         logit = np.where(visible[:, None, :], logit, -np.inf)
         parts_l = [logit]
@@ -255,7 +255,7 @@ def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, keep: np.ndarray, B: int
         if correction:
             skipped = np.array([j for j in range(1, dlo) if not keep[g, i, j]], dtype=np.int64)
             if skipped.size:
-                lbar = np.einsum("tgd,kd->tgk", Qb, kbar[skipped, g, :]) * c + logB
+                lbar = (Qb @ kbar[skipped, g, :].T) * c + logB
                 parts_l.append(lbar)
                 parts_v.append(vbar[skipped, g, :])
         L = np.concatenate(parts_l, axis=2)               # [nt, G, nk_total]
@@ -263,7 +263,7 @@ def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, keep: np.ndarray, B: int
         m = L.max(axis=2, keepdims=True)
         w = np.exp(L - m)
         den = w.sum(axis=2)
-        O[t0:t1, g * G:(g + 1) * G, :] = np.einsum("tgk,kd->tgd", w, Vv) / den[..., None]
+        O[t0:t1, g * G:(g + 1) * G, :] = (w @ Vv) / den[..., None]
         lse[t0:t1, g * G:(g + 1) * G] = m[..., 0] + np.log(den)
     return O, lse
 
