@@ -336,7 +336,8 @@ def test_reference_max_refresh_in_every_tile_kind(dtype, kvb):
     the same mask.  Here one or two keys carry each row, so the kernel's one
     systematic error shows whole: PV takes the probabilities rounded to bf16 while
     the row sum adds them in float32, which moves O by at most 2^-9 max|v|; the
-    bound adds that term.  e4m3: one scale per KV block and head (query block and
+    bound adds that term, and the measured worst error is printed beside the 1e-2
+    bar.  e4m3: one scale per KV block and head (query block and
     head for Q).  kvb = 64: 64-token KV blocks under 128-token query blocks, two to a
     tile, each half with its own K scale; rows of three or four entries give full and
     lone-entry pair tiles."""
@@ -380,4 +381,6 @@ def test_reference_max_refresh_in_every_tile_kind(dtype, kvb):
         torch.cuda.synchronize()
         got = L.out[:T].cpu().numpy().astype(np.float64)
         ref = O.run_batch([tuple(dec)], B, 0.0, corr, keeps=[keep], BK=kvb)["out"]
-        check_out(got, ref, TOL[dtype], "f32", extra=2.0 ** -9 * float(np.abs(dec[2]).max()))
+        worst = check_out(got, ref, TOL[dtype], "f32", extra=2.0 ** -9 * float(np.abs(dec[2]).max()))
+        print(f"\nrefresh stress {dtype} kvb={kvb} correction={corr}: max abs err {worst:.4f} "
+              f"(bar {TOL[dtype]}, bound {TOL[dtype] + 2.0 ** -9 * float(np.abs(dec[2]).max()):.4f})")
