@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "FP2_OK", 1: "FP2_ERR_INVALID", 2: "FP2_ERR_UNSUPPORTED", 3: 
                 4: "FP2_ERR_HIP"}
 
 SYMBOLS = ("fp2_block_stats", "fp2_block_stats_cache_rows", "fp2_block_stats_cached", "fp2_gather_block_stats",
-           "fp2_plan_workspace_bytes", "fp2_plan_max_nnz", "fp2_plan_mask",
+           "fp2_plan_workspace_bytes", "fp2_plan_max_nnz", "fp2_plan_mask", "fp2_plan_mask_noalloc",
            "fp2_run_workspace_bytes", "fp2_prefill_run", "fp2_last_error")
 
 _p = ctypes.c_void_p
@@ -70,6 +70,9 @@ _lib.fp2_plan_max_nnz.restype = ctypes.c_int64
 _lib.fp2_plan_mask.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CQ), ctypes.c_int32, _p,
                                ctypes.c_float, _p, _p, ctypes.c_int64, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.fp2_plan_mask.restype = ctypes.c_int
+_lib.fp2_plan_mask_noalloc.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CQ), ctypes.c_int32, _p,
+                                       ctypes.c_float, _p, _p, ctypes.c_int64, _p, _p, _p]
+_lib.fp2_plan_mask_noalloc.restype = ctypes.c_int
 _lib.fp2_run_workspace_bytes.argtypes = [ctypes.POINTER(CBatch), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int]
 _lib.fp2_run_workspace_bytes.restype = ctypes.c_size_t
@@ -240,6 +243,16 @@ def fp2_plan_mask(batch: Batch, q: Queries, num_kv_heads: int, kbar: torch.Tenso
                               ctypes.c_float(tau), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
                               _ptr(nnz), _ptr(scores), _ptr(workspace), workspace.numel(),
                               _stream(stream)))
+
+
+def fp2_plan_mask_noalloc(batch: Batch, q: Queries, num_kv_heads: int, kbar: torch.Tensor, tau: float,
+                          row_ptr: torch.Tensor, col_idx: torch.Tensor, nnz: torch.Tensor,
+                          scores: Optional[torch.Tensor] = None, stream=None):
+    """fp2_plan_mask with the library's own device scratch as its workspace (no allocation)."""
+    b, qc = batch.c, q.c
+    _check(_lib.fp2_plan_mask_noalloc(ctypes.byref(b), ctypes.byref(qc), num_kv_heads, _ptr(kbar),
+                                      ctypes.c_float(tau), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                      _ptr(nnz), _ptr(scores), _stream(stream)))
 
 
 def fp2_run_workspace_bytes(batch: Batch, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int) -> int:

@@ -18,6 +18,8 @@ hipError_t launch_gather_stats(const fp2_batch* b, const fp2_kv* kv, const Batch
 hipError_t launch_plan(const fp2_batch* b, const fp2_q* q, int hkv, const BatchInfo& info,
                        const float* kbar, float tau, int32_t* row_ptr, int32_t* col_idx,
                        int32_t* nnz, float* scores, void* workspace, hipStream_t stream);
+hipError_t launch_zero_plan(int32_t* row_ptr, int32_t* nnz, hipStream_t stream);
+hipError_t scratch_address(void** out);
 hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, const BatchInfo& info,
                           const int32_t* row_ptr, const int32_t* col_idx, const float* kbar,
                           const float* vbar, int correction, float softmax_scale, int out_f32,
@@ -94,40 +96,67 @@ int64_t fp2_plan_max_nnz(const fp2_batch* batch, int32_t num_kv_heads) {
   return info.causal_pairs * num_kv_heads;
 }
 
+// Checks shared by fp2_plan_mask and fp2_plan_mask_noalloc (everything but
+// the workspace).
+static fp2_status check_plan(const fp2_batch* batch, const fp2_q* q, int32_t num_kv_heads, const float* kbar,
+                             float tau, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* nnz,
+                             BatchInfo* info) {
+  fp2_status st = check_batch(batch, info);
+  if (st != FP2_OK) return st;
+  if ((st = check_q(q, num_kv_heads, *info, batch->block)) != FP2_OK) return st;
+  if ((st = check_index_range(*info, num_kv_heads)) != FP2_OK) return st;
+  if (std::isnan(tau)) return fail(FP2_ERR_INVALID, "tau is NaN");
+  if (!nnz) return fail(FP2_ERR_INVALID, "nnz is NULL");
+  if (info->total_qblocks > 0) {
+    if (!kbar || !row_ptr || !col_idx) return fail(FP2_ERR_INVALID, "kbar/row_ptr/col_idx is NULL");
+  } else if (!row_ptr) {
+    return fail(FP2_ERR_INVALID, "row_ptr is NULL");
+  }
+  const int64_t need = info->causal_pairs * num_kv_heads;
+  if (col_capacity < need)
+    return fail(FP2_ERR_CAPACITY, "col_capacity " + std::to_string(col_capacity) + " < " +
+                                      std::to_string(need) + " (fp2_plan_max_nnz)");
+  return FP2_OK;
+}
+
 fp2_status fp2_plan_mask(const fp2_batch* batch, const fp2_q* q, int32_t num_kv_heads,
                          const float* kbar, float tau, int32_t* row_ptr, int32_t* col_idx,
                          int64_t col_capacity, int32_t* nnz, float* scores, void* workspace,
                          size_t workspace_bytes, void* stream) {
   BatchInfo info;
-  fp2_status st = check_batch(batch, &info);
+  fp2_status st = check_plan(batch, q, num_kv_heads, kbar, tau, row_ptr, col_idx, col_capacity, nnz, &info);
   if (st != FP2_OK) return st;
-  if ((st = check_q(q, num_kv_heads, info, batch->block)) != FP2_OK) return st;
-  if ((st = check_index_range(info, num_kv_heads)) != FP2_OK) return st;
-  if (std::isnan(tau)) return fail(FP2_ERR_INVALID, "tau is NaN");
-  if (!nnz) return fail(FP2_ERR_INVALID, "nnz is NULL");
-  if (info.total_qblocks > 0) {
-    if (!kbar || !row_ptr || !col_idx) return fail(FP2_ERR_INVALID, "kbar/row_ptr/col_idx is NULL");
-    if (!workspace) return fail(FP2_ERR_INVALID, "workspace is NULL");
-  } else if (!row_ptr) {
-    return fail(FP2_ERR_INVALID, "row_ptr is NULL");
-  }
-  const int64_t need = info.causal_pairs * num_kv_heads;
-  if (col_capacity < need)
-    return fail(FP2_ERR_CAPACITY, "col_capacity " + std::to_string(col_capacity) + " < " +
-                                      std::to_string(need) + " (fp2_plan_max_nnz)");
+  if (info.total_qblocks > 0 && !workspace) return fail(FP2_ERR_INVALID, "workspace is NULL");
   const size_t wneed = plan_workspace_bytes(info, num_kv_heads);
   if (workspace_bytes < wneed)
     return fail(FP2_ERR_CAPACITY, "plan workspace " + std::to_string(workspace_bytes) + " < " +
                                       std::to_string(wneed) + " bytes");
   hipStream_t s = (hipStream_t)stream;
-  if (info.total_qblocks == 0) {  // empty plan: row_ptr = {0}, nnz = 0
-    hipError_t e = hipMemsetAsync(row_ptr, 0, sizeof(int32_t), s);
-    if (e == hipSuccess) e = hipMemsetAsync(nnz, 0, sizeof(int32_t), s);
-    return hip_status(e, "fp2_plan_mask");
-  }
+  if (info.total_qblocks == 0) return hip_status(launch_zero_plan(row_ptr, nnz, s), "fp2_plan_mask");
   return hip_status(launch_plan(batch, q, num_kv_heads, info, kbar, tau, row_ptr, col_idx, nnz,
                                 scores, workspace, s),
                     "fp2_plan_mask launch");
+}
+
+fp2_status fp2_plan_mask_noalloc(const fp2_batch* batch, const fp2_q* q, int32_t num_kv_heads,
+                                 const float* kbar, float tau, int32_t* row_ptr, int32_t* col_idx,
+                                 int64_t col_capacity, int32_t* nnz, float* scores, void* stream) {
+  BatchInfo info;
+  fp2_status st = check_plan(batch, q, num_kv_heads, kbar, tau, row_ptr, col_idx, col_capacity, nnz, &info);
+  if (st != FP2_OK) return st;
+  const size_t wneed = plan_workspace_bytes(info, num_kv_heads);
+  if (wneed > kPlanScratchBytes)
+    return fail(FP2_ERR_CAPACITY, "this batch needs " + std::to_string(wneed) +
+                                      " bytes of plan workspace; the allocation-free call holds at most " +
+                                      std::to_string(kPlanScratchBytes) + " (use fp2_plan_mask)");
+  hipStream_t s = (hipStream_t)stream;
+  if (info.total_qblocks == 0) return hip_status(launch_zero_plan(row_ptr, nnz, s), "fp2_plan_mask_noalloc");
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_status(e, "fp2_plan_mask_noalloc: scratch address");
+  return hip_status(launch_plan(batch, q, num_kv_heads, info, kbar, tau, row_ptr, col_idx, nnz,
+                                scores, ws, s),
+                    "fp2_plan_mask_noalloc launch");
 }
 
 size_t fp2_run_workspace_bytes(const fp2_batch* batch, int32_t num_q_heads, int32_t num_kv_heads,

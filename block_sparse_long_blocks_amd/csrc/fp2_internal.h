@@ -70,6 +70,8 @@ RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int n
 // batches), and the floats of one partial result (per slot, slice and wave:
 // O as 16 float4 per lane, then the reference max and row sum per lane).
 constexpr int64_t kMaxExtraItems = 256;
+// Size of the device array that serves as fp2_plan_mask_noalloc's workspace.
+constexpr size_t kPlanScratchBytes = FP2_PLAN_NOALLOC_MAX_BYTES;
 constexpr int64_t kPartFloatsPerWave = 64 * 64 + 2 * 64;
 inline int plan_words(const BatchInfo& info) { return int((info.max_kblocks + 31) / 32); }
 

@@ -20,14 +20,25 @@
 //   scan_counts  : one workgroup; exclusive scan of the counts -> row_ptr, nnz.
 //   fill_cols    : one workgroup per row; expands the bitmask into ascending
 //                  KV-block indices at row_ptr[row].
+#include <mutex>
+
 #include "fp2_device.h"
 #include "fp2_internal.h"
 
 namespace fp2 {
 
+// Workspace of fp2_plan_mask_noalloc (callers that cannot allocate): the
+// keep bitmask and kept counts live in this array, one copy per GPU, held
+// until the process ends.  Host code never uses its name as an address:
+// scratch_address() looks the device address up once per device.
+static __device__ __align__(256) uint8_t scratch[kPlanScratchBytes];
+
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 struct PlanArgs {
   const int32_t* cu_seqlens_q;
@@ -277,7 +288,38 @@ __global__ __launch_bounds__(kThreads) void fill_cols_kernel(const uint32_t* __r
   }
 }
 
+// An empty plan: row_ptr = {0}, nnz = 0 (a kernel, not a memset, so that the
+// call can be captured into a HIP graph).
+__global__ void zero_plan_kernel(int32_t* row_ptr, int32_t* nnz) {
+  if (threadIdx.x == 0) {
+    row_ptr[0] = 0;
+    nnz[0] = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_zero_plan(int32_t* row_ptr, int32_t* nnz, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_plan_kernel, dim3(1), dim3(64), 0, stream, row_ptr, nnz);
+  return hipGetLastError();
+}
+
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with this device current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_plan(const fp2_batch* b, const fp2_q* q, int hkv, const BatchInfo& info,
                        const float* kbar, float tau, int32_t* row_ptr, int32_t* col_idx,

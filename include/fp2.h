@@ -185,6 +185,25 @@ fp2_status fp2_plan_mask(const fp2_batch *batch, const fp2_q *q, int32_t num_kv_
                          int32_t *nnz, float *scores,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* fp2_plan_mask for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and outputs, bit for bit, with the workspace taken
+ * from a device array the library holds, FP2_PLAN_NOALLOC_MAX_BYTES on each
+ * GPU it runs on, kept until the process ends.  The call itself allocates
+ * nothing and records no memset.
+ *   Returns FP2_ERR_CAPACITY when fp2_plan_workspace_bytes() of the batch
+ *   exceeds FP2_PLAN_NOALLOC_MAX_BYTES (8 MiB: about 2 million bitmask words
+ *   and counts, e.g. 128K tokens with 8 KV heads needs 1.1 MB).
+ *   The array is shared by every call on one GPU and keeps the last call's
+ *   contents (each call overwrites what it reads): calls that overlap on one
+ *   GPU (two streams, or two threads) race and must be serialised by the
+ *   caller.  Other arguments and errors as fp2_plan_mask. */
+#define FP2_PLAN_NOALLOC_MAX_BYTES ((size_t)8 << 20)
+fp2_status fp2_plan_mask_noalloc(const fp2_batch *batch, const fp2_q *q, int32_t num_kv_heads,
+                                 const float *kbar, float tau,
+                                 int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
+                                 int32_t *nnz, float *scores, void *stream);
+
 /* Workspace bytes fp2_prefill_run needs for this batch, head size and KV
  * dtype (0 if the batch is empty or malformed).  For d = 128 with B = 128
  * over KB = 128 or KB = 64 (bf16 or e4m3), it holds V^T tiles of every KV block

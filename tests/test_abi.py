@@ -140,6 +140,27 @@ def test_int32_csr_limit():
     _expect(lib.FP2_ERR_CAPACITY, lib.fp2_plan_mask, one, q, 8, f32, math.inf, i32, i32, i32, ws)
 
 
+def test_noalloc_plan_rejects_batches_beyond_its_scratch():
+    """fp2_plan_mask_noalloc's workspace is a fixed 8 MiB device array: a batch whose plan
+    workspace is larger (one sequence with 16,384 KV blocks, so 512 bitmask words a row, plus
+    4,096 one-block sequences: 4,097 query blocks x 8 KV heads = 32,776 rows, 67 MB) is refused
+    on the host before anything is launched; the same batch passes the other checks."""
+    seqlens = [1 << 21] + [128] * 4096
+    nq = [128] + [128] * 4096
+    b = _batch(seqlens, nq)
+    need = lib.fp2_plan_workspace_bytes(b, 8)
+    assert need > 8 << 20
+    f32 = torch.zeros(16)
+    i32 = torch.zeros(16, dtype=torch.int32)
+    q = lib.Queries(torch.zeros((1, 32, 128), dtype=torch.bfloat16))  # pointers only: nothing is launched
+    cols = torch.zeros(lib.fp2_plan_max_nnz(b, 8), dtype=torch.int32)
+    _expect(lib.FP2_ERR_CAPACITY, lib.fp2_plan_mask_noalloc, b, q, 8, f32, 1.0, i32, cols, i32,
+            match="allocation-free")
+    # a too-small col_capacity is still reported first, as fp2_plan_mask does
+    _expect(lib.FP2_ERR_CAPACITY, lib.fp2_plan_mask_noalloc, b, q, 8, f32, 1.0, i32, i32, i32,
+            match="col_capacity")
+
+
 def test_block_stats_cache_rows_and_checks():
     """The paged block-stats cache: one row per KV block a page holds; page sizes that do not
     divide B (or the reverse) are unsupported; bad arguments are rejected before any launch."""
