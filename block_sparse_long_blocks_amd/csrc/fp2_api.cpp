@@ -1,7 +1,7 @@
 // C ABI of the library: host-side checks, then kernel launches on the
 // caller's stream.  No allocation, no synchronisation, no state besides the
 // per-thread error text.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cmath>
 

@@ -18,6 +18,12 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(fp2_[a-z_]+)\s*\(", src)))
 
 
+def test_library_is_the_one_requested():
+    """The in-tree libfp2.so, or the build a test run asked for (the sanitized host build)."""
+    want = os.environ.get("FP2_TEST_LIBRARY") or os.path.join(ROOT, "block_sparse_long_blocks_amd", "libfp2.so")
+    assert os.path.realpath(lib.library_path()) == os.path.realpath(want)
+
+
 def test_exports_every_declared_function():
     import ctypes
     names = declared_functions()
