@@ -137,13 +137,39 @@ def run_workload(name, tau, args, torch, lib, synth, corr=True, stats_cache=Fals
         L.attend(corr)
         e[3].record(stream)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    wall_sep = (time.perf_counter() - t_wall) * 1e3 / args.steps
     st = [sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps for i in range(3)]
-    step_ms = sum(ev[k][0].elapsed_time(ev[k][3]) for k in range(args.steps)) / args.steps
+    sep_ms = sum(ev[k][0].elapsed_time(ev[k][3]) for k in range(args.steps)) / args.steps
+    # the same layer with stage 1 as one fused call (fp2_stage1)
+    for _ in range(args.warmup):
+        L.stage1(tau)
+        L.attend(corr)
+    torch.cuda.synchronize()
+    ef = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        e = ef[k]
+        e[0].record(stream)
+        L.stage1(tau)
+        e[1].record(stream)
+        L.attend(corr)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall_fused = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    fused_s1 = sum(ef[k][0].elapsed_time(ef[k][1]) for k in range(args.steps)) / args.steps
+    fused_run = sum(ef[k][1].elapsed_time(ef[k][2]) for k in range(args.steps)) / args.steps
+    fused_ms = sum(ef[k][0].elapsed_time(ef[k][2]) for k in range(args.steps)) / args.steps
     nnz = int(L.nnz.item())
     fl = flop_counts(w, nnz)
-    res = dict(name=name, tau=tau, corr=corr, ms_per_layer=step_ms, wall_ms_per_layer=wall_ms,
-               stages_ms={"block_stats": st[0], "plan_mask": st[1], "prefill_run": st[2]},
+    # the layer as PrefillLayer runs it (stage 1 as two calls unless fused_stage1 is set)
+    fused = L.fused_stage1
+    res = dict(name=name, tau=tau, corr=corr, ms_per_layer=fused_ms if fused else sep_ms,
+               wall_ms_per_layer=wall_fused if fused else wall_sep,
+               stages_ms={"stage1": fused_s1 if fused else st[0] + st[1],
+                          "prefill_run": fused_run if fused else st[2]},
+               stage1_ms={"fused (fp2_stage1)": fused_s1, "separate (fp2_block_stats + fp2_plan_mask)": st[0] + st[1],
+                          "block_stats": st[0], "plan_mask": st[1]},
+               ms_per_layer_separate_stage1=sep_ms,
                nnz=nnz, density=nnz / fl["causal_pairs"], flops=fl)
     # dense comparison: the same three calls at tau = +inf
     if not args.no_dense:
@@ -167,6 +193,9 @@ def run_workload(name, tau, args, torch, lib, synth, corr=True, stats_cache=Fals
     kbar_bytes = 2 * w.cfg.hkv * w.total_kblocks * w.cfg.d * 4
     res["stats_gbs"] = (kv_bytes + kbar_bytes) / (st[0] * 1e-3) / 1e9
     res["plan_gbs"] = (w.q.nbytes + kbar_bytes / 2) / (st[1] * 1e-3) / 1e9
+    # fused stage 1: K, V and Q read once, kbar / vbar / qbar written (the selection pass reads L2-resident means)
+    qbar_bytes = w.cfg.hkv * w.total_qblocks * w.cfg.d * 4
+    res["stage1_fused_gbs"] = (kv_bytes + w.q.nbytes + kbar_bytes + qbar_bytes) / (fused_s1 * 1e-3) / 1e9
     del L, batch, q, kv
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -244,8 +273,11 @@ def time_layer(L, tau, corr, steps, warmup, torch):
     e = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for k in range(steps):
         e[k][0].record(stream)
-        L.stats()
-        L.plan(tau)
+        if L.fused_stage1:
+            L.stage1(tau)
+        else:
+            L.stats()
+            L.plan(tau)
         e[k][1].record(stream)
         L.attend(corr)
         e[k][2].record(stream)
@@ -425,13 +457,13 @@ def config_runs(args, torch, lib, synth):
            "steps": args.steps, "warmup": args.warmup, "runs": rows}
     if args.configs_out:
         with open(args.configs_out, "w") as f:
-            f.write("| workload | dtype | correction | tau | density | ms/layer | block_stats | plan_mask "
+            f.write("| workload | dtype | correction | tau | density | ms/layer | stage 1 (fp2_stage1) "
                     "| prefill_run | dense-equiv TFLOP/s | MFMA fraction of prefill_run | dense ms/layer "
-                    "| speedup vs dense |\n|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+                    "| speedup vs dense |\n|---|---|---|---|---|---|---|---|---|---|---|---|\n")
             for r in rows:
                 st = r["stages_ms"]
                 f.write(f"| {r['workload']} | {r['dtype']} | {'on' if r['correction'] else 'off'} | {r['tau']} "
-                        f"| {r['density']} | {r['ms_per_layer']} | {st['block_stats']} | {st['plan_mask']} "
+                        f"| {r['density']} | {r['ms_per_layer']} | {st['stage1']} "
                         f"| {st['prefill_run']} | {r['dense_equiv_tflops']} | {r['mfma_frac_run']} "
                         f"| {r['dense_ms_per_layer']} | {r['speedup_vs_dense']} |\n")
             for r in rows:
@@ -602,9 +634,12 @@ def main():
                      "flops_per_launch": attn_flops,
                      "flops_basis": "kept pairs * G*B^2*4d + skipped pairs * G*B*4d"},
         "stages_ms": {k: round(v, 4) for k, v in bf["stages_ms"].items()},
+        "stage1_ms": {k: round(v, 4) for k, v in bf["stage1_ms"].items()},
+        "ms_per_layer_separate_stage1": round(bf["ms_per_layer_separate_stage1"], 4),
         "mfma_frac_computed_layer": round(mfma_frac_layer, 4),
         "stats_hbm_gbs": round(bf["stats_gbs"], 1),
         "plan_hbm_gbs": round(bf["plan_gbs"], 1),
+        "stage1_fused_hbm_gbs": round(bf["stage1_fused_gbs"], 1),
     }
     if "dense_ms_per_layer" in bf:
         out["dense_ms_per_layer"] = round(bf["dense_ms_per_layer"], 3)
@@ -625,6 +660,7 @@ def main():
         out["fp8"] = {"ms_per_layer": round(f8["ms_per_layer"], 4),
                       "dense_equiv_tflops": round(fl8["dense"] / (f8["ms_per_layer"] * 1e-3) / 1e12, 2),
                       "stages_ms": {k: round(v, 4) for k, v in f8["stages_ms"].items()},
+                      "stage1_ms": {k: round(v, 4) for k, v in f8["stage1_ms"].items()},
                       "tau": f8["tau"], "density": round(f8["density"], 5),
                       "mfma_frac_attn": round(busy / t8, 4)}
         if "dense_ms_per_layer" in f8:

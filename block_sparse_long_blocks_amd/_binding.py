@@ -31,7 +31,8 @@ STATUS_NAMES = {0: "FP2_OK", 1: "FP2_ERR_INVALID", 2: "FP2_ERR_UNSUPPORTED", 3: 
 
 SYMBOLS = ("fp2_block_stats", "fp2_block_stats_cache_rows", "fp2_block_stats_cached", "fp2_gather_block_stats",
            "fp2_plan_workspace_bytes", "fp2_plan_max_nnz", "fp2_plan_mask", "fp2_plan_mask_noalloc",
-           "fp2_run_workspace_bytes", "fp2_prefill_run", "fp2_last_error")
+           "fp2_stage1_workspace_bytes", "fp2_stage1", "fp2_run_workspace_bytes", "fp2_prefill_run",
+           "fp2_last_error")
 
 _p = ctypes.c_void_p
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -73,6 +74,11 @@ _lib.fp2_plan_mask.restype = ctypes.c_int
 _lib.fp2_plan_mask_noalloc.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CQ), ctypes.c_int32, _p,
                                        ctypes.c_float, _p, _p, ctypes.c_int64, _p, _p, _p]
 _lib.fp2_plan_mask_noalloc.restype = ctypes.c_int
+_lib.fp2_stage1_workspace_bytes.argtypes = [ctypes.POINTER(CBatch), ctypes.c_int32, ctypes.c_int32]
+_lib.fp2_stage1_workspace_bytes.restype = ctypes.c_size_t
+_lib.fp2_stage1.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CQ), ctypes.POINTER(CKV), ctypes.c_float, _p, _p,
+                            _p, _p, ctypes.c_int64, _p, _p, _p, ctypes.c_size_t, _p]
+_lib.fp2_stage1.restype = ctypes.c_int
 _lib.fp2_run_workspace_bytes.argtypes = [ctypes.POINTER(CBatch), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int]
 _lib.fp2_run_workspace_bytes.restype = ctypes.c_size_t
@@ -253,6 +259,21 @@ def fp2_plan_mask_noalloc(batch: Batch, q: Queries, num_kv_heads: int, kbar: tor
     _check(_lib.fp2_plan_mask_noalloc(ctypes.byref(b), ctypes.byref(qc), num_kv_heads, _ptr(kbar),
                                       ctypes.c_float(tau), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
                                       _ptr(nnz), _ptr(scores), _stream(stream)))
+
+
+def fp2_stage1_workspace_bytes(batch: Batch, num_kv_heads: int, head_dim: int) -> int:
+    b = batch.c
+    return int(_lib.fp2_stage1_workspace_bytes(ctypes.byref(b), num_kv_heads, head_dim))
+
+
+def fp2_stage1(batch: Batch, q: Queries, kv: KVCache, tau: float, kbar: torch.Tensor, vbar: torch.Tensor,
+               row_ptr: torch.Tensor, col_idx: torch.Tensor, nnz: torch.Tensor, workspace: torch.Tensor,
+               scores: Optional[torch.Tensor] = None, stream=None):
+    """Block means, pooled scores, threshold and CSR in one fused pass (fp2_block_stats + fp2_plan_mask)."""
+    b, qc, k = batch.c, q.c, kv.c
+    _check(_lib.fp2_stage1(ctypes.byref(b), ctypes.byref(qc), ctypes.byref(k), ctypes.c_float(tau), _ptr(kbar),
+                           _ptr(vbar), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ptr(nnz), _ptr(scores),
+                           _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def fp2_run_workspace_bytes(batch: Batch, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int) -> int:

@@ -19,6 +19,9 @@ hipError_t launch_plan(const fp2_batch* b, const fp2_q* q, int hkv, const BatchI
                        const float* kbar, float tau, int32_t* row_ptr, int32_t* col_idx,
                        int32_t* nnz, float* scores, void* workspace, hipStream_t stream);
 hipError_t launch_zero_plan(int32_t* row_ptr, int32_t* nnz, hipStream_t stream);
+hipError_t launch_stage1(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, const BatchInfo& info, float tau,
+                         float* kbar, float* vbar, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz, float* scores,
+                         void* workspace, hipStream_t stream);
 hipError_t scratch_address(void** out);
 hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, const BatchInfo& info,
                           const int32_t* row_ptr, const int32_t* col_idx, const float* kbar,
@@ -157,6 +160,34 @@ fp2_status fp2_plan_mask_noalloc(const fp2_batch* batch, const fp2_q* q, int32_t
   return hip_status(launch_plan(batch, q, num_kv_heads, info, kbar, tau, row_ptr, col_idx, nnz,
                                 scores, ws, s),
                     "fp2_plan_mask_noalloc launch");
+}
+
+size_t fp2_stage1_workspace_bytes(const fp2_batch* batch, int32_t num_kv_heads, int32_t head_dim) {
+  BatchInfo info;
+  if (check_batch(batch, &info) != FP2_OK || num_kv_heads < 1 || head_dim < 1) return 0;
+  return stage1_workspace_bytes(info, num_kv_heads, head_dim);
+}
+
+fp2_status fp2_stage1(const fp2_batch* batch, const fp2_q* q, const fp2_kv* kv, float tau, float* kbar, float* vbar,
+                      int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* nnz, float* scores,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  BatchInfo info;
+  fp2_status st = check_batch(batch, &info);
+  if (st != FP2_OK) return st;
+  if ((st = check_kv(kv, batch, info)) != FP2_OK) return st;
+  if ((st = check_plan(batch, q, kv->num_kv_heads, kbar, tau, row_ptr, col_idx, col_capacity, nnz, &info)) != FP2_OK)
+    return st;
+  if (q->dtype != kv->dtype) return fail(FP2_ERR_UNSUPPORTED, "q and kv dtypes differ");
+  if (q->head_dim != kv->head_dim) return fail(FP2_ERR_INVALID, "q and kv head_dim differ");
+  if (info.total_kblocks > 0 && (!kbar || !vbar)) return fail(FP2_ERR_INVALID, "kbar/vbar is NULL");
+  const size_t wneed = stage1_workspace_bytes(info, kv->num_kv_heads, kv->head_dim);
+  if (wneed > 0 && !workspace) return fail(FP2_ERR_INVALID, "workspace is NULL");
+  if (workspace_bytes < wneed)
+    return fail(FP2_ERR_CAPACITY, "stage-1 workspace " + std::to_string(workspace_bytes) + " < " +
+                                      std::to_string(wneed) + " bytes");
+  return hip_status(launch_stage1(batch, q, kv, info, tau, kbar, vbar, row_ptr, col_idx, nnz, scores, workspace,
+                                  (hipStream_t)stream),
+                    "fp2_stage1 launch");
 }
 
 size_t fp2_run_workspace_bytes(const fp2_batch* batch, int32_t num_q_heads, int32_t num_kv_heads,

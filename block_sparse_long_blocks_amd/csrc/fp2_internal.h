@@ -40,6 +40,9 @@ fp2_status check_kv(const fp2_kv* kv, const fp2_batch* b, const BatchInfo& info)
 fp2_status check_index_range(const BatchInfo& info, int num_kv_heads);
 
 size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads);
+// fp2_stage1: the plan workspace followed by the pooled query means
+// (float32 [Hkv, total_qblocks, d])
+size_t stage1_workspace_bytes(const BatchInfo& info, int num_kv_heads, int head_dim);
 // fp2_prefill_run runs the DMA kernel on V^T tiles for d = 128 and query
 // blocks of 128 over KV blocks of 128 or of 64 (two to a tile), bf16 or e4m3,
 // and the register-staged kernel otherwise.

@@ -156,6 +156,12 @@ size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads) {
   return (bytes + 255) & ~size_t(255);
 }
 
+size_t stage1_workspace_bytes(const BatchInfo& info, int num_kv_heads, int head_dim) {
+  const size_t plan = plan_workspace_bytes(info, num_kv_heads);
+  const size_t qbar = ((size_t)info.total_qblocks * num_kv_heads * head_dim * 4 + 255) & ~size_t(255);
+  return plan + qbar;
+}
+
 RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                      int dtype) {
   auto up = [](size_t v) { return (v + 255) & ~size_t(255); };

@@ -24,6 +24,7 @@
 
 #include "fp2_device.h"
 #include "fp2_internal.h"
+#include "pool_device.h"
 
 namespace fp2 {
 
@@ -35,47 +36,28 @@ static __device__ __align__(256) uint8_t scratch[kPlanScratchBytes];
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kPoolThreads;
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-struct PlanArgs {
-  const int32_t* cu_seqlens_q;
-  const int32_t* seqlens_k;
-  const int32_t* cu_qblocks;
-  const int32_t* cu_kblocks;
-  const uint8_t* q;
-  const float* q_scale;
-  const float* kbar;
-  uint32_t* bits;       // [rows, W]
-  int32_t* counts;      // [rows]
-  float* scores_out;    // optional [rows, max_kblocks]
-  float tau, scale;
-  int num_seqs, hq, hkv, d, total_qblocks, total_kblocks, W, max_kblocks;
-  int qblock, kvblock;  // query block and KV block tokens (kvblock divides qblock)
-};
-
-template <int ESZ>
-__device__ __forceinline__ void add_chunk(float* acc, uint4 w, float mul) {
-  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
-  if (ESZ == 2) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += bf16lo(v[i]);
-      acc[2 * i + 1] += bf16hi(v[i]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 f = e4m3x4_to_f32(v[i]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[4 * i + q] += f[q] * mul;
-    }
+// Sum of p over the lpb lanes that share a kbar row (lpb = d/8: 16 or 8),
+// lane 0 of the group holding the tree ((p0 + p8) + (p4 + p12)) + ...: with
+// 16 lanes by DPP row rotations (one vector add each, no LDS traffic), with
+// 8 by cross-lane shuffles in the same order.
+__device__ __forceinline__ float row_sum(float p, int lpb) {
+  if (lpb == 16) {
+    p += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(p), 0x128, 0xf, 0xf, false));  // row_ror:8
+    p += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(p), 0x124, 0xf, 0xf, false));  // row_ror:4
+    p += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(p), 0x122, 0xf, 0xf, false));  // row_ror:2
+    p += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(p), 0x121, 0xf, 0xf, false));  // row_ror:1
+    return p;
   }
+  for (int m = lpb >> 1; m > 0; m >>= 1) p += __shfl_xor(p, m);
+  return p;
 }
 
-template <int ESZ>
+template <int ESZ, bool POOLED>
 __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
   constexpr int N = 16 / ESZ;  // elements per 16-byte chunk
   extern __shared__ float s_scores[];  // [max_kblocks]
@@ -97,50 +79,14 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
   // the diagonal: the KV blocks holding one of the query block's positions
   const int dlo = (P + I * a.qblock) / a.kvblock;
   const int diag = (P + I * a.qblock + ntok - 1) / a.kvblock;  // the last causal KV block
-  const int G = a.hq / a.hkv;
 
-  // ---- pool qbar over ntok tokens x G heads (the group's heads are adjacent)
-  const int row_bytes = G * a.d * ESZ;  // <= 4096: CH <= 256
-  const int CH = row_bytes / 16;
-  const int R = kThreads / CH;
-  const int c = t % CH, r = t / CH;
-  float acc[N];
-#pragma unroll
-  for (int e = 0; e < N; ++e) acc[e] = 0.f;
-  if (r < R) {
-    const int elem0 = c * N;
-    const int h = g * G + elem0 / a.d;  // a chunk stays within one head
-    float mul = 1.f;
-    if (ESZ == 1) mul = a.q_scale[(int64_t)qb * a.hq + h];
-    const uint8_t* base = a.q + ((int64_t)(q0 + I * a.qblock) * a.hq + g * G) * a.d * ESZ + c * 16;
-    const int64_t tok_stride = (int64_t)a.hq * a.d * ESZ;
-    constexpr int U = 8;
-    int tok = r;
-    for (; tok + (U - 1) * R < ntok; tok += U * R) {
-      uint4 w[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const uint4*>(base + (tok + u * R) * tok_stride);
-#pragma unroll
-      for (int u = 0; u < U; ++u) add_chunk<ESZ>(acc, w[u], mul);
-    }
-    for (; tok < ntok; tok += R) add_chunk<ESZ>(acc, *reinterpret_cast<const uint4*>(base + tok * tok_stride), mul);
+  // ---- qbar: pooled here, or (fused stage 1) read back from the pooling pass
+  if constexpr (POOLED) {
+    if (t < a.d) s_qbar[t] = a.qbar[((int64_t)g * a.total_qblocks + qb) * a.d + t];
+    __syncthreads();
+  } else {
+    pool_qbar<ESZ>(a, qb, g, red, s_qbar);
   }
-#pragma unroll
-  for (int e = 0; e < N; ++e) red[t][e] = acc[e];
-  __syncthreads();
-  if (t < a.d) {
-    // element t of qbar: sum over heads hh and token lanes rr of chunk (hh*d + t)/N
-    float sum = 0.f;
-    for (int hh = 0; hh < G; ++hh) {
-      const int el = hh * a.d + t;
-      const int cc = el / N, ee = el % N;
-      float part = 0.f;
-      for (int rr = 0; rr < R; ++rr) part += red[rr * CH + cc][ee];
-      sum += part;
-    }
-    s_qbar[t] = sum / (float)(G * ntok);
-  }
-  __syncthreads();
 
   // ---- scores for J = 0..diag: float32 dot(qbar, kbar_J) * scale.  LPB =
   // d/8 lanes share a kbar row (8 floats each, so a wave's loads cover
@@ -176,11 +122,10 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
         p0 = fmaf(qv[e], k0[u][e], p0);
         p1 = fmaf(qv[4 + e], k1[u][e], p1);
       }
-      float p = p0 + p1;
-      for (int m = lpb >> 1; m > 0; m >>= 1) p += __shfl_xor(p, m);
-      if (J <= diag) {
+      const float p = row_sum(p0 + p1, lpb);
+      if (J <= diag && sub == 0) {  // the row maximum is the maximum of the stored scores
         const float sc = p * a.scale;
-        if (sub == 0) s_scores[J] = sc;
+        s_scores[J] = sc;
         lmax = fmaxf(lmax, sc);
       }
     }
@@ -217,6 +162,135 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
     int tot = 0;
     for (int w = 0; w < kThreads / 64; ++w) tot += s_wcnt[w];
     a.counts[row] = tot;
+  }
+}
+
+// Fused stage 1, selection pass: the pooled means of up to QT (<= kMaxQT)
+// consecutive query blocks of one KV head, scored against their sequence's
+// kbar rows with each kbar row read once for all of them (the scores of one
+// (query block, KV block) pair are summed exactly as score_select_kernel
+// sums them, so the CSR is the same bit for bit), then each row's maximum,
+// threshold, keep bitmask and count as there.
+#ifndef FP2_MAX_QT
+#define FP2_MAX_QT 8
+#endif
+constexpr int kMaxQT = FP2_MAX_QT;
+__global__ __launch_bounds__(kThreads) void select_tiled_kernel(PlanArgs a, int QT) {
+  extern __shared__ float s_sc[];  // [QT][max_kblocks]
+  __shared__ int s_seq[kMaxQT], s_diag[kMaxQT], s_dlo[kMaxQT];
+  __shared__ float s_q[kMaxQT][128];
+  __shared__ float s_wmax[kMaxQT][kThreads / 64];
+  __shared__ int s_wcnt[kMaxQT][kThreads / 64];
+  const int g = blockIdx.y;
+  const int qb0 = blockIdx.x * QT;
+  const int nrows = min(QT, a.total_qblocks - qb0);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (t < nrows) {
+    const int qb = qb0 + t;
+    const int s = find_seq(a.cu_qblocks, a.num_seqs, qb);
+    const int I = qb - a.cu_qblocks[s];
+    const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
+    const int P = a.seqlens_k[s] - n;
+    const int ntok = min(a.qblock, n - I * a.qblock);
+    s_seq[t] = s;
+    s_dlo[t] = (P + I * a.qblock) / a.kvblock;
+    s_diag[t] = (P + I * a.qblock + ntok - 1) / a.kvblock;
+  }
+  for (int i = t; i < nrows * a.d; i += kThreads)
+    s_q[i / a.d][i % a.d] = a.qbar[((int64_t)g * a.total_qblocks + qb0 + i / a.d) * a.d + i % a.d];
+  __syncthreads();
+
+  const int lpb = a.d / 8;  // lanes sharing a kbar row, 8 floats each
+  const int bpw = 64 / lpb;
+  const int sub = lane % lpb;
+  constexpr int UJ = 4;
+  const int jstep = (kThreads / 64) * bpw;
+  // runs of rows from one sequence (a tile crosses a sequence boundary rarely)
+  for (int i0 = 0; i0 < nrows;) {
+    const int s = s_seq[i0];
+    int i1 = i0, jmax = 0;
+    while (i1 < nrows && s_seq[i1] == s) jmax = max(jmax, s_diag[i1++]);
+    float qv[kMaxQT][8];
+#pragma unroll
+    for (int i = 0; i < kMaxQT; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[i][e] = i0 + i < i1 ? s_q[i0 + i][8 * sub + e] : 0.f;
+    const float* kb = a.kbar + ((int64_t)g * a.total_kblocks + a.cu_kblocks[s]) * a.d;
+    for (int J0 = wave * bpw; J0 <= jmax; J0 += UJ * jstep) {
+      f32x4 k0[UJ], k1[UJ];
+#pragma unroll
+      for (int u = 0; u < UJ; ++u) {
+        const int J = J0 + u * jstep + lane / lpb;
+        k0[u] = k1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (J <= jmax) {
+          const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (int64_t)J * a.d + 8 * sub);
+          k0[u] = kr[0];
+          k1[u] = kr[1];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UJ; ++u) {
+        const int J = J0 + u * jstep + lane / lpb;
+#pragma unroll
+        for (int i = 0; i < kMaxQT; ++i) {
+          if (i0 + i >= i1) break;
+          float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p0 = fmaf(qv[i][e], k0[u][e], p0);
+            p1 = fmaf(qv[i][4 + e], k1[u][e], p1);
+          }
+          const float p = row_sum(p0 + p1, lpb);
+          if (sub == 0 && J <= s_diag[i0 + i]) s_sc[(i0 + i) * a.max_kblocks + J] = p * a.scale;
+        }
+      }
+    }
+    i0 = i1;
+  }
+  __syncthreads();
+
+  // per row: maximum, threshold, keep bitmask (forced: block 0 and the
+  // diagonal run), kept count; all waves on each row in turn
+  for (int i = 0; i < nrows; ++i) {
+    const int diag = s_diag[i];
+    const float* sc = s_sc + i * a.max_kblocks;
+    float lmax = -INFINITY;
+    for (int J = t; J <= diag; J += kThreads) lmax = fmaxf(lmax, sc[J]);
+    lmax = wave_max(lmax);
+    if (lane == 0) s_wmax[i][wave] = lmax;
+  }
+  __syncthreads();
+  for (int i = 0; i < nrows; ++i) {
+    const int diag = s_diag[i], dlo = s_dlo[i];
+    const float* sc = s_sc + i * a.max_kblocks;
+    float rmax = s_wmax[i][0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) rmax = fmaxf(rmax, s_wmax[i][w]);
+    const float thr = rmax - a.tau;
+    const int row = g * a.total_qblocks + qb0 + i;
+    int cnt = 0;
+    for (int w = t; w < a.W; w += kThreads) {
+      uint32_t word = 0;
+      const int j0 = w * 32;
+      for (int b = 0; b < 32; ++b) {
+        const int J = j0 + b;
+        if (J <= diag && (sc[J] >= thr || J == 0 || J >= dlo)) word |= 1u << b;
+      }
+      a.bits[(int64_t)row * a.W + w] = word;
+      cnt += __popc(word);
+    }
+    if (a.scores_out) {
+      float* so = a.scores_out + (int64_t)row * a.max_kblocks;
+      for (int J = t; J < a.max_kblocks; J += kThreads) so[J] = J <= diag ? sc[J] : -INFINITY;
+    }
+    cnt = wave_sum_i(cnt);
+    if (lane == 0) s_wcnt[i][wave] = cnt;
+  }
+  __syncthreads();
+  if (t < nrows) {
+    int tot = 0;
+    for (int w = 0; w < kThreads / 64; ++w) tot += s_wcnt[t][w];
+    a.counts[g * a.total_qblocks + qb0 + t] = tot;
   }
 }
 
@@ -288,6 +362,30 @@ __global__ __launch_bounds__(kThreads) void fill_cols_kernel(const uint32_t* __r
   }
 }
 
+// Fused stage 1, first pass: every K, V and Q byte of the batch read once in
+// one launch.  Workgroups [0, total_kblocks) write the KV block means (as
+// fp2_block_stats), the rest one pooled query mean each (query block qb,
+// KV head g: as fp2_plan_mask's pooling phase) into a.qbar, which the
+// select pass then scores against kbar from L2.
+template <int ESZ>
+__global__ __launch_bounds__(kThreads) void pool_kernel(StatsArgs sa, PlanArgs a) {
+  constexpr int N = 16 / ESZ;
+  __shared__ float red_k[kThreads][N + 1];
+  __shared__ float red_v[kThreads][N + 1];
+  __shared__ float s_qbar[128];
+  __shared__ int s_pg[kPoolMaxPages];
+  const int b = blockIdx.x;
+  if (b < sa.total_kblocks) {
+    kv_block_stats<ESZ>(sa, b, red_k, red_v, s_pg);
+    return;
+  }
+  const int idx = b - sa.total_kblocks;
+  const int qb = idx / a.hkv, g = idx % a.hkv;
+  pool_qbar<ESZ>(a, qb, g, red_k, s_qbar);
+  const int t = threadIdx.x;
+  if (t < a.d) a.qbar[((int64_t)g * a.total_qblocks + qb) * a.d + t] = s_qbar[t];
+}
+
 // An empty plan: row_ptr = {0}, nnz = 0 (a kernel, not a memset, so that the
 // call can be captured into a HIP graph).
 __global__ void zero_plan_kernel(int32_t* row_ptr, int32_t* nnz) {
@@ -321,15 +419,11 @@ hipError_t scratch_address(void** out) {
   return hipSuccess;
 }
 
-hipError_t launch_plan(const fp2_batch* b, const fp2_q* q, int hkv, const BatchInfo& info,
-                       const float* kbar, float tau, int32_t* row_ptr, int32_t* col_idx,
-                       int32_t* nnz, float* scores, void* workspace, hipStream_t stream) {
+namespace {
+PlanArgs plan_args(const fp2_batch* b, const fp2_q* q, int hkv, const BatchInfo& info, const float* kbar, float tau,
+                   float* scores, void* workspace) {
   const int rows = (int)(info.total_qblocks * hkv);
   const int W = plan_words(info);
-  uint32_t* bits = static_cast<uint32_t*>(workspace);
-  size_t off = ((size_t)rows * W * 4 + 255) & ~size_t(255);
-  int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + off);
-
   PlanArgs a;
   a.cu_seqlens_q = b->cu_seqlens_q;
   a.seqlens_k = b->seqlens_k;
@@ -338,9 +432,10 @@ hipError_t launch_plan(const fp2_batch* b, const fp2_q* q, int hkv, const BatchI
   a.q = static_cast<const uint8_t*>(q->q);
   a.q_scale = q->q_scale;
   a.kbar = kbar;
-  a.bits = bits;
-  a.counts = counts;
+  a.bits = static_cast<uint32_t*>(workspace);
+  a.counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + (((size_t)rows * W * 4 + 255) & ~size_t(255)));
   a.scores_out = scores;
+  a.qbar = nullptr;
   a.tau = tau;
   a.scale = 1.0f / sqrtf((float)q->head_dim);
   a.num_seqs = b->num_seqs;
@@ -353,20 +448,63 @@ hipError_t launch_plan(const fp2_batch* b, const fp2_q* q, int hkv, const BatchI
   a.total_kblocks = (int)info.total_kblocks;
   a.W = W;
   a.max_kblocks = (int)info.max_kblocks;
-  const size_t lds = (size_t)info.max_kblocks * sizeof(float);
-  dim3 grid((unsigned)info.total_qblocks, (unsigned)hkv);
-  if (q->dtype == FP2_BF16)
-    hipLaunchKernelGGL(score_select_kernel<2>, grid, dim3(kThreads), lds, stream, a);
-  else
-    hipLaunchKernelGGL(score_select_kernel<1>, grid, dim3(kThreads), lds, stream, a);
+  return a;
+}
+
+// score / select (pooling Q itself, or reading the fused pass's qbar), then
+// the scan and the column fill
+hipError_t launch_select(const PlanArgs& a, int dtype, bool pooled, int32_t* row_ptr, int32_t* col_idx,
+                         int32_t* nnz, hipStream_t stream) {
+  const int rows = a.total_qblocks * a.hkv;
+  const size_t lds = (size_t)a.max_kblocks * sizeof(float);
+  dim3 grid((unsigned)a.total_qblocks, (unsigned)a.hkv);
+  if (pooled) {
+    // query blocks per workgroup: score rows of QT x max_kblocks floats in LDS (<= 64 KB)
+    int QT = kMaxQT;
+    while (QT > 1 && (size_t)QT * lds > (size_t)(64 << 10)) QT >>= 1;
+    const dim3 tgrid((unsigned)((a.total_qblocks + QT - 1) / QT), (unsigned)a.hkv);
+    hipLaunchKernelGGL(select_tiled_kernel, tgrid, dim3(kThreads), (size_t)QT * lds, stream, a, QT);
+  } else if (dtype == FP2_BF16) {
+    hipLaunchKernelGGL((score_select_kernel<2, false>), grid, dim3(kThreads), lds, stream, a);
+  } else {
+    hipLaunchKernelGGL((score_select_kernel<1, false>), grid, dim3(kThreads), lds, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(1024), 0, stream, counts, rows, row_ptr, nnz);
+  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(1024), 0, stream, a.counts, rows, row_ptr, nnz);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fill_cols_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, bits, W,
-                     row_ptr, col_idx);
+  hipLaunchKernelGGL(fill_cols_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, a.bits, a.W, row_ptr,
+                     col_idx);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_plan(const fp2_batch* b, const fp2_q* q, int hkv, const BatchInfo& info,
+                       const float* kbar, float tau, int32_t* row_ptr, int32_t* col_idx,
+                       int32_t* nnz, float* scores, void* workspace, hipStream_t stream) {
+  const PlanArgs a = plan_args(b, q, hkv, info, kbar, tau, scores, workspace);
+  return launch_select(a, q->dtype, false, row_ptr, col_idx, nnz, stream);
+}
+
+hipError_t launch_stage1(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, const BatchInfo& info, float tau,
+                         float* kbar, float* vbar, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz, float* scores,
+                         void* workspace, hipStream_t stream) {
+  const int hkv = kv->num_kv_heads;
+  PlanArgs a = plan_args(b, q, hkv, info, kbar, tau, scores, workspace);
+  a.qbar = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan_workspace_bytes(info, hkv));
+  const StatsArgs sa = stats_args(b, kv, info, kbar, vbar);
+  const int64_t nwg = info.total_kblocks + info.total_qblocks * hkv;
+  if (nwg > 0) {
+    if (kv->dtype == FP2_BF16)
+      hipLaunchKernelGGL(pool_kernel<2>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, sa, a);
+    else
+      hipLaunchKernelGGL(pool_kernel<1>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, sa, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (info.total_qblocks == 0) return launch_zero_plan(row_ptr, nnz, stream);
+  return launch_select(a, q->dtype, true, row_ptr, col_idx, nnz, stream);
 }
 
 }  // namespace fp2

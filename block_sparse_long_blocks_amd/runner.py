@@ -11,12 +11,13 @@ import numpy as np
 import torch
 
 from ._binding import (Batch, KVCache, Queries, fp2_block_stats, fp2_plan_mask, fp2_plan_max_nnz,
-                       fp2_plan_workspace_bytes, fp2_prefill_run, fp2_run_workspace_bytes)
+                       fp2_plan_workspace_bytes, fp2_prefill_run, fp2_run_workspace_bytes, fp2_stage1,
+                       fp2_stage1_workspace_bytes)
 
 
 class PrefillLayer:
     def __init__(self, batch: Batch, q: Queries, kv: KVCache, with_scores: bool = False,
-                 out_dtype: torch.dtype = torch.bfloat16):
+                 out_dtype: torch.dtype = torch.bfloat16, fused_stage1: bool = False):
         self.batch, self.q, self.kv = batch, q, kv
         dev = q.q.device
         hkv, d = kv.num_kv_heads, q.q.shape[2]
@@ -29,6 +30,9 @@ class PrefillLayer:
         self.col_idx = torch.empty(max(1, fp2_plan_max_nnz(batch, hkv)), **i32)
         self.nnz = torch.zeros(1, **i32)
         self.plan_ws = torch.empty(max(1, fp2_plan_workspace_bytes(batch, hkv)), dtype=torch.uint8, device=dev)
+        self.stage1_ws = torch.empty(max(1, fp2_stage1_workspace_bytes(batch, hkv, d)), dtype=torch.uint8, device=dev)
+        # __call__: fp2_block_stats then fp2_plan_mask (the faster at 128K), or fp2_stage1
+        self.fused_stage1 = fused_stage1
         self.run_ws = torch.empty(max(1, fp2_run_workspace_bytes(batch, q.q.shape[1], hkv, d, kv.dtype)), dtype=torch.uint8, device=dev)
         self.out = torch.empty((max(1, batch.total_q), q.q.shape[1], d), dtype=out_dtype, device=dev)
         self.scores = torch.empty((rows, max(1, batch.max_kblocks)), **f32) if with_scores else None
@@ -41,13 +45,20 @@ class PrefillLayer:
         fp2_plan_mask(self.batch, self.q, self.kv.num_kv_heads, self.kbar, tau, self.row_ptr, self.col_idx,
                       self.nnz, self.plan_ws, self.scores, stream)
 
+    def stage1(self, tau: float, stream=None):
+        fp2_stage1(self.batch, self.q, self.kv, tau, self.kbar, self.vbar, self.row_ptr, self.col_idx, self.nnz,
+                   self.stage1_ws, self.scores, stream)
+
     def attend(self, correction: bool, stream=None, softmax_scale: Optional[float] = None):
         fp2_prefill_run(self.batch, self.q, self.kv, self.row_ptr, self.col_idx, self.kbar, self.vbar,
                         correction, self.out, self.run_ws, softmax_scale, stream, self.max_chunk_tiles)
 
     def __call__(self, tau: float, correction: bool, stream=None):
-        self.stats(stream)
-        self.plan(tau, stream)
+        if self.fused_stage1:
+            self.stage1(tau, stream)
+        else:
+            self.stats(stream)
+            self.plan(tau, stream)
         self.attend(correction, stream)
         return self.out
 

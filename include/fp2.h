@@ -204,6 +204,25 @@ fp2_status fp2_plan_mask_noalloc(const fp2_batch *batch, const fp2_q *q, int32_t
                                  int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
                                  int32_t *nnz, float *scores, void *stream);
 
+/* Stage 1 in one fused pass (Figure 3: Stage 1 packs the query heads of a KV
+ * head with PackGQA, pools block-mean statistics and emits the CSR index of
+ * selected blocks in a single fused pass): the outputs of fp2_block_stats
+ * (kbar, vbar) and of fp2_plan_mask (row_ptr, col_idx, nnz, scores), bit for
+ * bit, from one launch that reads every K, V and Q byte once and writes the
+ * block means and the pooled query means, then a selection pass that scores
+ * the pooled means against kbar (both held in L2) and compacts the CSR.
+ *   kbar, vbar   device float32 [Hkv, total_kblocks, d] (outputs)
+ *   workspace    device scratch of fp2_stage1_workspace_bytes() bytes: the
+ *                plan workspace followed by the pooled query means
+ * Other arguments, limits and errors as fp2_block_stats and fp2_plan_mask
+ * (the query and KV dtypes and head sizes must agree). */
+size_t fp2_stage1_workspace_bytes(const fp2_batch *batch, int32_t num_kv_heads, int32_t head_dim);
+fp2_status fp2_stage1(const fp2_batch *batch, const fp2_q *q, const fp2_kv *kv, float tau,
+                      float *kbar, float *vbar,
+                      int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
+                      int32_t *nnz, float *scores,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Workspace bytes fp2_prefill_run needs for this batch, head size and KV
  * dtype (0 if the batch is empty or malformed).  For d = 128 with B = 128
  * over KB = 128 or KB = 64 (bf16 or e4m3), it holds V^T tiles of every KV block

@@ -75,6 +75,30 @@ def test_sizes_and_counts():
     assert lib.fp2_run_workspace_bytes(b, 12, 3, 64, lib.FP2_FP8_E4M3) >= 2 * 3 * (8 + 2) * 64 * 2
 
 
+def test_stage1_sizes_and_checks():
+    """fp2_stage1: its workspace is the plan workspace plus float32 pooled query means
+    [Hkv, total_qblocks, d] (256-byte aligned); its checks are those of the two calls it fuses."""
+    b = _batch([1000, 256], [1000, 128])
+    plan = lib.fp2_plan_workspace_bytes(b, 3)
+    qbar = 3 * (8 + 1) * 128 * 4
+    assert lib.fp2_stage1_workspace_bytes(b, 3, 128) == plan + ((qbar + 255) & ~255)
+    f32 = torch.zeros(16)
+    i32 = torch.zeros(64, dtype=torch.int32)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    bb = _batch([256], [256])
+    kv = _kv()
+    _expect(lib.FP2_ERR_CAPACITY, lib.fp2_stage1, bb, _q(256), kv, 1.0, f32, f32, i32, i32, i32, ws[:8],
+            match="stage-1 workspace")
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_stage1, bb, lib.Queries(torch.zeros((256, 4, 128), dtype=torch.uint8),
+            f32), kv, 1.0, f32, f32, i32, i32, i32, ws, match="dtypes differ")
+    _expect(lib.FP2_ERR_INVALID, lib.fp2_stage1, bb, _q(256), kv, math.nan, f32, f32, i32, i32, i32, ws,
+            match="NaN")
+    _expect(lib.FP2_ERR_CAPACITY, lib.fp2_stage1, bb, _q(256), kv, 1.0, f32, f32, i32, i32[:5], i32, ws)
+    _expect(lib.FP2_ERR_INVALID, lib.fp2_stage1, bb, _q(256), kv, 1.0, None, f32, i32, i32, i32, ws, match="NULL")
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_stage1, _batch([256], [256], 32), _q(256), kv, 1.0, f32, f32, i32,
+            i32, i32, ws, match="block")
+
+
 def test_decoupled_blocks_sizes_and_counts():
     """128-token query blocks over 64-token KV blocks: the causal count is that of the blocks
     holding a visible key (counted here from positions); workspace layouts per path."""

@@ -152,6 +152,35 @@ def test_plan_parity(name):
                                                              w.cfg.block, kv_block(w))]) * w.cfg.hkv
 
 
+@pytest.mark.parametrize("name", list(SMALL))
+def test_stage1_fused_matches_separate_calls(name):
+    """fp2_stage1 (one pass over K, V and Q, then the selection) gives fp2_block_stats' block means and
+    fp2_plan_mask's CSR, nnz and float32 scores bit for bit, at every threshold (so the oracle parity
+    of the separate calls carries over)."""
+    w, _ = workload(name)
+    L = layer(w, with_scores=True)
+    for tau in TAUS[name] + (math.inf, -1.0):
+        L.stats()
+        L.plan(tau)
+        torch.cuda.synchronize()
+        ref = [x.clone() for x in (L.kbar, L.vbar, L.row_ptr, L.nnz, L.scores)]
+        n = int(L.nnz.item())
+        ref_ci = L.col_idx[:n].clone()
+        for x in (L.kbar, L.vbar, L.scores):
+            x.fill_(float("nan"))
+        L.row_ptr.fill_(-5)
+        L.col_idx.fill_(-5)
+        L.nnz.fill_(-5)
+        L.stage1(tau)
+        torch.cuda.synchronize()
+        got = (L.kbar, L.vbar, L.row_ptr, L.nnz, L.scores)
+        for a, b in zip(got[:2], ref[:2]):
+            assert torch.equal(a[:, :w.total_kblocks], b[:, :w.total_kblocks])
+        assert torch.equal(got[2], ref[2]) and torch.equal(got[3], ref[3])
+        assert torch.equal(L.col_idx[:n], ref_ci)
+        assert torch.equal(torch.nan_to_num(got[4], nan=7.0), torch.nan_to_num(ref[4], nan=7.0))
+
+
 def _attention_case(name, tau, corr, pad_fill="zero", out_dtype="bf16", max_chunk_tiles=0):
     w, seqs = workload(name, pad_fill)
     L = layer(w, out_dtype=out_dtype)
