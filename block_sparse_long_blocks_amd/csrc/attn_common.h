@@ -37,6 +37,11 @@ struct AttnArgs {
                            // (items kernel scratch)
   int32_t* counters;       // d128 kernel: [0] work items, [1] split rows
   float* part;             // d128 kernel: partial O, reference max and row sum of split-row chunks
+  int32_t* info;           // d128 kernel: per work item, the values its workgroup starts from [items, kInfoInts]
+  uint32_t* skip;          // d128 kernel with correction: skipped-block bitmask per CSR row [rows, wskip]
+  int32_t* mlist;          // d128 kernel with correction: first mean token of each mean tile per CSR row [rows, mtmax]
+  int32_t* mcount;         // d128 kernel with correction: mean tiles per CSR row [rows]
+  int wskip, mtmax;
   int extra_cap, chunk_cap, ncu;
   void* out;               // bf16 or f32 [total_q, Hq, D]
   float scale_log2;        // softmax_scale * log2(e)

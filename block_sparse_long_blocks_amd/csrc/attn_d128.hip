@@ -260,16 +260,6 @@ __global__ __launch_bounds__(256) void vt_mean_kernel(PrepArgs a) {
 // Attention
 // ---------------------------------------------------------------------------
 
-// bits of the 32 mean tokens [32*w, 32*w + 32) that are skipped blocks, i.e.
-// in [1, diag) and not kept
-__device__ __forceinline__ uint32_t skipped_word(const uint32_t* kept, int w, int diag) {
-  const int j0 = 32 * w;
-  if (j0 >= diag) return 0u;
-  uint32_t m = ~kept[w];
-  if (j0 + 32 > diag) m &= (1u << (diag - j0)) - 1u;
-  if (w == 0) m &= ~1u;
-  return m;
-}
 
 // bf16 pair (1, 1): the dot product with it sums two probabilities
 typedef __bf16 bf16x2e __attribute__((ext_vector_type(2)));
@@ -565,7 +555,7 @@ struct Wave {
           const int lim = (TWO ? (j < NS / 2 ? tq : tq2) - 32 * (j % (NS / 2)) : tq - 32 * j) - 4 * hf;
           M[j] = lim >= 31 ? ~0u : lim < 0 ? 0u : (2u << lim) - 1u;
         } else {
-          M[j] = skipped_word(kept, (J0 >> 5) + j, diag) >> (4 * hf);
+          M[j] = kept[(J0 >> 5) + j] >> (4 * hf);  // skipped-block bits of the mean tokens
         }
       }
     } else {
@@ -613,7 +603,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t V1[kTileLds];
   __shared__ uint32_t kept[kMaxKBlocks / 32];
   __shared__ int mtile[kMaxKBlocks / kBlk + 1];
-  __shared__ int s_nmean;
 
   // ---- tile decode: 8 consecutive work items form a group, the slices of
   // one item share blockIdx % 8 (one XCD); the items are in launch order,
@@ -626,19 +615,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   const int rem = b % per_grp;
   const int slice = rem / 8;
   const int pos = grp * 8 + (rem % 8);
-  if (pos >= ld_uniform(a.counters, 0)) return;
-  const int32_t* item = reinterpret_cast<const int32_t*>(a.items + pos);
-  const int rank = ld_uniform(item, 0);
-  const int tile0 = ld_uniform(item, 1), tile1 = ld_uniform(item, 2), pslot = ld_uniform(item, 3);
-  const int qb = a.total_qblocks - 1 - rank / a.hkv;
-  const int g = rank % a.hkv;
+  if (pos >= a.rows + a.extra_cap) return;
+  // the item's record (item_info_kernel): one load round trip for everything
+  // the first two tiles need
+  const int32_t* rec = a.info + (int64_t)pos * kInfoInts;
+  const int rank = ld_uniform(rec, 0);
+  if (rank < 0) return;
+  const int tile0 = ld_uniform(rec, 1), tile1 = ld_uniform(rec, 2), pslot = ld_uniform(rec, 3);
+  const int qb = ld_uniform(rec, 4);
+  const int g = ld_uniform(rec, 5);
   const int row = g * a.total_qblocks + qb;
-
-  const int s = find_seq(a.cu_qblocks, a.num_seqs, qb);
-  const int I = qb - a.cu_qblocks[s];
-  const int q0 = a.cu_seqlens_q[s];
-  const int n = a.cu_seqlens_q[s + 1] - q0;
-  const int T = a.seqlens_k[s];
+  const int s = ld_uniform(rec, 6);
+  const int I = ld_uniform(rec, 7);
+  const int q0 = ld_uniform(rec, 8);
+  const int n = ld_uniform(rec, 9);
+  const int T = ld_uniform(rec, 10);
   // the diagonal: KV blocks dlo .. diag hold the query block's own positions
   // (one block of 128 tokens; two of 64, one for a short last query block)
   const int qpos0 = T - n + I * kBlk;  // position of the block's first query
@@ -646,7 +637,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   const int dlo = PAIR ? qpos0 / KB : diag;
   const int G = a.hq / a.hkv;
   const int32_t* pt = a.page_table + (int64_t)s * a.max_pages;
-  const int kb0 = a.cu_kblocks[s];
+  const int kb0 = ld_uniform(rec, 11);
   const int64_t mrow0 = (int64_t)g * a.total_kblocks + kb0;
 
   const int t = threadIdx.x;
@@ -661,16 +652,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
 
   // uniform values: later loads indexed by them become scalar loads, which
   // do not share the vector-memory counter with the tile DMA
-  const int rbeg = ld_uniform(a.row_ptr, row);
-  const int rend = ld_uniform(a.row_ptr, row + 1);
+  const int rbeg = ld_uniform(rec, 12);
+  const int rend = ld_uniform(rec, 13);
   // this item's exact tiles (CSR entries kbeg .. kend-1; with 64-token KV
   // blocks tile i of a row holds its entries 2i and 2i+1, the last perhaps
   // alone); the mean tiles go with the row's last item
   const int kbeg = rbeg + (PAIR ? 2 * tile0 : tile0);
   const int kend = PAIR ? min(rbeg + 2 * tile1, rend) : rbeg + tile1;
   const int nexact = PAIR ? tile1 - tile0 : kend - kbeg;
-  const bool last_item = kend == rend;
   const int ne = kend - kbeg;
+  // mean-token tiles that hold at least one skipped block (the last item of
+  // a row, correction on): their skipped-block words and first mean tokens
+  // into LDS, read first so that their loads land before the Q and DMA ones
+  const int nmean = ld_uniform(rec, 14);
+  if (nmean > 0) {
+    const int ncand = (dlo + kBlk - 1) / kBlk, nw = (dlo + 31) >> 5;
+    const uint32_t* sk = a.skip + (int64_t)row * a.wskip;
+    for (int w = (int)threadIdx.x; w < ncand * (kBlk / 32); w += kThreads) kept[w] = w < nw ? sk[w] : 0u;
+    const int32_t* ml = a.mlist + (int64_t)row * a.mtmax;
+    for (int k = (int)threadIdx.x; k < nmean; k += kThreads) mtile[k] = ml[k];
+  }
   // PAIR: the two block indices of tile i packed as ja | jb << 16 (a lone
   // last entry goes with itself: its second half is masked)
   auto pack = [&](int ja, int jb, int i) { return ja | ((2 * i + 1 < ne ? jb : ja) << 16); };
@@ -911,21 +912,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   // tile i+2 and the page entries of tile i+1 arrived with the last barrier,
   // the loads of tile i+3's block index and tile i+2's page entries are in
   // flight.
-  // A barrier for LDS data only: the DMA and the loads in flight are not
-  // waited for (the compiler barriers keep LDS accesses on their side).
-  auto lds_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
   // Tile 0 is an exact block (the CSR holds block 0): its DMA, the first
   // page and block-index loads go out before the mean-token setup below.
-  int j0 = 0, j1 = 0, j2v = 0, j2vb = 0, pgv[kDmaHalves] = {};
-  if (0 < nexact) {
-    if constexpr (PAIR) j0 = pack(ld_uniform(a.col_idx, kbeg), ld_uniform(a.col_idx, min(kbeg + 1, kend - 1)), 0);
-    else j0 = ld_uniform(a.col_idx, kbeg);
-  }
+  int j0 = ld_uniform(rec, 16), j1 = ld_uniform(rec, 17), j2v = ld_uniform(rec, 18), j2vb = ld_uniform(rec, 19);
+  int pgv[kDmaHalves] = {};
   // e4m3: the K scale of exact tile i (one page per block) arrives with the
   // barrier before tile i (ksv); the page entry of tile i+1 one tile earlier
   // (pgbv)
@@ -933,17 +923,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)a.k_scale, (short)0, 0x7fffffff, kBufferFlags);
   int ksv = 0, pgbv = 0, ksvb = 0, pgbvb = 0;  // PAIR: the second block's
   if constexpr (FP8) {
-    if (0 < nexact) {
-      ksv = __builtin_amdgcn_raw_buffer_load_b32(rks, (ld_uniform(pt, half_of(j0, 0)) * a.hkv + g) * 4, 0, 0);
-      if constexpr (PAIR)
-        ksvb = __builtin_amdgcn_raw_buffer_load_b32(rks, (ld_uniform(pt, half_of(j0, 1)) * a.hkv + g) * 4, 0, 0);
-    }
+    ksv = ld_uniform(rec, 20);
+    ksvb = ld_uniform(rec, 21);
+    pgbv = ld_uniform(rec, 22);
+    pgbvb = ld_uniform(rec, 23);
   }
   if (0 < nexact) {
     int pg0[kDmaHalves] = {};
     if (dma_wave) {
 #pragma unroll
-      for (int hh = 0; hh < kDmaHalves; ++hh) pg0[hh] = __builtin_amdgcn_readfirstlane(page_of(j0, hh));
+      for (int hh = 0; hh < kDmaHalves; ++hh) pg0[hh] = ld_uniform(rec, 24 + 2 * wave + hh);
     }
     const DmaPlan pl = plan(0, j0, pg0, K0, V0);
     if (pl.fast) {
@@ -952,40 +941,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     }
   }
 
-  // ---- mean-token tiles that hold at least one skipped block
-  int nmean = 0;
-  if (a.correction && dlo > 1 && last_item) {
-    const int nw = (diag + 32) >> 5;
-    for (int w = t; w < nw; w += kThreads) kept[w] = 0u;
-    lds_barrier();
-    for (int i = rbeg + t; i < rend; i += kThreads) {
-      const int j = a.col_idx[i];
-      atomicOr(&kept[j >> 5], 1u << (j & 31));
-    }
-    lds_barrier();
-    if (wave == 0) {
-      const int ncand = (dlo + kBlk - 1) / kBlk;
-      int base = 0;
-      for (int m0 = 0; m0 < ncand; m0 += 64) {
-        const int mt = m0 + lane;
-        bool flag = false;
-        if (mt < ncand) {
-#pragma unroll
-          for (int w = 0; w < kBlk / 32; ++w) flag |= skipped_word(kept, mt * (kBlk / 32) + w, dlo) != 0u;
-        }
-        const uint64_t bal = __ballot(flag);
-        if (flag) mtile[base + __popcll(bal & ((1ull << lane) - 1ull))] = mt * kBlk;
-        base += __popcll(bal);
-      }
-      if (lane == 0) s_nmean = base;
-    }
-    lds_barrier();
-    nmean = s_nmean;
-  }
   const int ntiles = nexact + nmean;
   auto mean_of = [&](int idx) -> int { return idx < ntiles ? mtile[idx - nexact] : 0; };
-  if (nexact == 0 && ntiles > 0) {  // (not produced by fp2_plan_mask: every row holds block 0)
-    j0 = mean_of(0);
+  if (nexact == 0 && ntiles > 0) {  // (not produced by fp2_plan_mask: every row holds block 0; j0 is mean tile 0)
     const int pg0[kDmaHalves] = {};
     const DmaPlan pl = plan(0, j0, pg0, K0, V0);
     if (pl.fast) {
@@ -993,29 +951,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
       for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, V0);
     }
   }
-  if (1 < nexact) {
-    if constexpr (PAIR) j1 = pack(ld_uniform(a.col_idx, kbeg + 2), ld_uniform(a.col_idx, min(kbeg + 3, kend - 1)), 1);
-    else j1 = ld_uniform(a.col_idx, kbeg + 1);
-  } else if (1 < ntiles) {
-    j1 = mean_of(1);
-  }
-  if (2 < nexact) {
-    if constexpr (PAIR) {
-      j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 4 * 4, 0, 0);
-      j2vb = __builtin_amdgcn_raw_buffer_load_b32(rcol, 5 * 4, 0, 0);
-    } else {
-      j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, 2 * 4, 0, 0);
-    }
-  }
-  if constexpr (FP8) {
-    if (1 < nexact) {
-      pgbv = __builtin_amdgcn_raw_buffer_load_b32(rpt, half_of(j1, 0) * 4, 0, 0);
-      if constexpr (PAIR) pgbvb = __builtin_amdgcn_raw_buffer_load_b32(rpt, half_of(j1, 1) * 4, 0, 0);
-    }
-  }
   if (1 < nexact && dma_wave) {
 #pragma unroll
-    for (int hh = 0; hh < kDmaHalves; ++hh) pgv[hh] = page_of(j1, hh);
+    for (int hh = 0; hh < kDmaHalves; ++hh) pgv[hh] = ld_uniform(rec, 32 + 2 * wave + hh);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
@@ -1211,13 +1149,55 @@ __device__ void rank_tiles(const AttnArgs& a, int r, int& nexact, int& nmean) {
   const int row = (r % a.hkv) * a.total_qblocks + qb;
   nexact = max(a.row_ptr[row + 1] - a.row_ptr[row], 0);
   if (a.pair) nexact = (nexact + 1) >> 1;  // 64-token KV blocks, two a tile
-  nmean = 0;
-  if (a.correction) {
-    const int s = find_seq(a.cu_qblocks, a.num_seqs, qb);
-    const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
-    // first KV block of the diagonal: its mean tokens come before it
-    const int dlo = (a.seqlens_k[s] - n + (qb - a.cu_qblocks[s]) * kBlk) / (a.pair ? 64 : kBlk);
-    nmean = (dlo + kBlk - 1) / kBlk;
+  nmean = a.correction ? a.mcount[row] : 0;  // (mean_prep_kernel has run)
+}
+
+// Per CSR row (correction on): the bitmask of its skipped blocks (KV blocks
+// in [1, dlo) that are not kept; dlo = the row's first diagonal block) and
+// the list of its mean tiles (128 consecutive mean tokens holding at least
+// one skipped block, by first mean token), so that a workgroup starting the
+// row reads them instead of building them.
+__global__ __launch_bounds__(256) void mean_prep_kernel(AttnArgs a) {
+  __shared__ uint32_t kw[kMaxKBlocks / 32];
+  const int row = blockIdx.x;
+  const int qb = row % a.total_qblocks;
+  const int s = find_seq(a.cu_qblocks, a.num_seqs, qb);
+  const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
+  const int dlo = (a.seqlens_k[s] - n + (qb - a.cu_qblocks[s]) * kBlk) / (a.pair ? 64 : kBlk);
+  const int nw = (dlo + 31) >> 5;
+  const int t = threadIdx.x;
+  for (int w = t; w < nw; w += 256) kw[w] = 0u;
+  __syncthreads();
+  const int rbeg = a.row_ptr[row], rend = a.row_ptr[row + 1];
+  for (int i = rbeg + t; i < rend; i += 256) {
+    const int j = a.col_idx[i];
+    if (j < dlo) atomicOr(&kw[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  for (int w = t; w < nw; w += 256) {
+    uint32_t m = ~kw[w];
+    const int j0 = 32 * w;
+    if (j0 + 32 > dlo) m &= (1u << (dlo - j0)) - 1u;
+    if (w == 0) m &= ~1u;
+    kw[w] = m;
+    a.skip[(int64_t)row * a.wskip + w] = m;
+  }
+  __syncthreads();
+  if (t < 64) {
+    const int ncand = (dlo + kBlk - 1) / kBlk;
+    int base = 0;
+    for (int m0 = 0; m0 < ncand; m0 += 64) {
+      const int mt = m0 + t;
+      bool flag = false;
+      if (mt < ncand) {
+#pragma unroll
+        for (int w = 0; w < kBlk / 32; ++w) flag |= (4 * mt + w < nw) && kw[4 * mt + w] != 0u;
+      }
+      const uint64_t bal = __ballot(flag);
+      if (flag) a.mlist[(int64_t)row * a.mtmax + base + __popcll(bal & ((1ull << t) - 1ull))] = mt * kBlk;
+      base += __popcll(bal);
+    }
+    if (t == 0) a.mcount[row] = base;
   }
 }
 
@@ -1343,6 +1323,121 @@ __global__ __launch_bounds__(kItemsThreads) void items_kernel(AttnArgs a, int nb
     a.counters[0] = s_cnt[0];
     a.counters[1] = s_cnt[2];
   }
+}
+
+// The values the workgroups of work item pos start from, so that they read
+// one record instead of walking a chain of dependent loads (item -> CSR row
+// bounds -> first columns -> page entries -> DMA): int32 [kInfoInts]
+//   0 rank (-1: no item), 1 first and 2 end exact tile, 3 partial slot,
+//   4 query block, 5 KV head, 6 sequence, 7 query block in the sequence,
+//   8 first query token, 9 new tokens, 10 keys, 11 first KV block of the
+//   sequence, 12 13 CSR row bounds, 14 mean tiles of the item, 16 17 the
+//   block (PAIR: block pair) of tiles 0 and 1, 18 19 the raw CSR entries of
+//   tile 2, e4m3: 20 21 the K scales of tile 0's blocks, 22 23 the pages
+//   of tile 1's blocks, 24-31 and 32-39 the page of each 16 rows that DMA
+//   wave w (w < 4) moves of tiles 0 and 1 (entry 2 w + half).
+template <bool FP8, bool PAIR>
+__global__ __launch_bounds__(256) void item_info_kernel(AttnArgs a) {
+  constexpr int KB = PAIR ? 64 : kBlk;
+  const int pos = blockIdx.x * 256 + threadIdx.x;
+  if (pos >= a.rows + a.extra_cap) return;
+  int32_t* rec = a.info + (int64_t)pos * kInfoInts;
+  if (pos >= a.counters[0]) {
+    rec[0] = -1;
+    return;
+  }
+  const int4 it = a.items[pos];
+  const int rank = it.x, tile0 = it.y, tile1 = it.z;
+  const int qb = a.total_qblocks - 1 - rank / a.hkv;
+  const int g = rank % a.hkv;
+  const int row = g * a.total_qblocks + qb;
+  const int s = find_seq(a.cu_qblocks, a.num_seqs, qb);
+  const int I = qb - a.cu_qblocks[s];
+  const int q0 = a.cu_seqlens_q[s];
+  const int n = a.cu_seqlens_q[s + 1] - q0;
+  const int T = a.seqlens_k[s];
+  const int kb0 = a.cu_kblocks[s];
+  const int32_t* pt = a.page_table + (int64_t)s * a.max_pages;
+  const int qpos0 = T - n + I * kBlk;
+  const int diag = PAIR ? (qpos0 + min(kBlk, n - I * kBlk) - 1) / KB : (T - n) / kBlk + I;
+  const int dlo = PAIR ? qpos0 / KB : diag;
+  const int rbeg = a.row_ptr[row], rend = a.row_ptr[row + 1];
+  const int kbeg = rbeg + (PAIR ? 2 * tile0 : tile0);
+  const int kend = PAIR ? min(rbeg + 2 * tile1, rend) : rbeg + tile1;
+  const int nexact = PAIR ? tile1 - tile0 : kend - kbeg;
+  const int ne = kend - kbeg;
+  const int nmean = (a.correction && dlo > 1 && kend == rend) ? a.mcount[row] : 0;
+  const int ntiles = nexact + nmean;
+  const int32_t* ml = a.mlist + (int64_t)row * a.mtmax;
+  auto mean_of = [&](int idx) -> int { return idx < ntiles ? ml[idx - nexact] : 0; };
+  auto pack = [&](int ja, int jb, int i) { return ja | ((2 * i + 1 < ne ? jb : ja) << 16); };
+  auto half_of = [](int J, int h) { return h ? J >> 16 : J & 0xFFFF; };
+  int j0 = 0, j1 = 0, j2v = 0, j2vb = 0;
+  if (0 < nexact) {
+    if constexpr (PAIR) j0 = pack(a.col_idx[kbeg], a.col_idx[min(kbeg + 1, kend - 1)], 0);
+    else j0 = a.col_idx[kbeg];
+  } else if (0 < ntiles) {
+    j0 = mean_of(0);
+  }
+  if (1 < nexact) {
+    if constexpr (PAIR) j1 = pack(a.col_idx[kbeg + 2], a.col_idx[min(kbeg + 3, kend - 1)], 1);
+    else j1 = a.col_idx[kbeg + 1];
+  } else if (1 < ntiles) {
+    j1 = mean_of(1);
+  }
+  if (2 < nexact) {
+    if constexpr (PAIR) {
+      j2v = a.col_idx[kbeg + 4];
+      j2vb = kbeg + 5 < kend ? a.col_idx[kbeg + 5] : 0;
+    } else {
+      j2v = a.col_idx[kbeg + 2];
+    }
+  }
+  // the page of rows r0 + 16 hh .. of exact tile J that DMA wave w moves (as
+  // the attention kernel's page_of)
+  auto page = [&](int J, int w, int hh) {
+    const int r0 = PAIR ? half_of(J, w >= kDmaWaves / 2) * KB + kDmaRows * (w % (kDmaWaves / 2))
+                        : J * kBlk + kDmaRows * w;
+    int pi, slot;
+    a.pm.split(min(r0 + 16 * hh, T - 1), pi, slot);
+    return pt[pi];
+  };
+  int v[kInfoInts] = {};
+  v[0] = rank;
+  v[1] = tile0;
+  v[2] = tile1;
+  v[3] = it.w;
+  v[4] = qb;
+  v[5] = g;
+  v[6] = s;
+  v[7] = I;
+  v[8] = q0;
+  v[9] = n;
+  v[10] = T;
+  v[11] = kb0;
+  v[12] = rbeg;
+  v[13] = rend;
+  v[14] = nmean;
+  v[16] = j0;
+  v[17] = j1;
+  v[18] = j2v;
+  v[19] = j2vb;
+  if constexpr (FP8) {
+    if (0 < nexact) {
+      v[20] = __float_as_int(a.k_scale[(int64_t)pt[half_of(j0, 0)] * a.hkv + g]);
+      if constexpr (PAIR) v[21] = __float_as_int(a.k_scale[(int64_t)pt[half_of(j0, 1)] * a.hkv + g]);
+    }
+    if (1 < nexact) {
+      v[22] = pt[half_of(j1, 0)];
+      if constexpr (PAIR) v[23] = pt[half_of(j1, 1)];
+    }
+  }
+  for (int w = 0; w < kDmaWaves; ++w)
+    for (int hh = 0; hh < kDmaHalves; ++hh) {
+      if (0 < nexact) v[24 + 2 * w + hh] = page(j0, w, hh);
+      if (1 < nexact) v[32 + 2 * w + hh] = page(j1, w, hh);
+    }
+  for (int i = 0; i < kInfoInts; i += 4) *reinterpret_cast<int4*>(rec + i) = make_int4(v[i], v[i + 1], v[i + 2], v[i + 3]);
 }
 
 // Merges the chunks of each split row: O = sum_c 2^(m_c - M) O_c over
@@ -1472,12 +1567,27 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0) a.ncu = ncu;
   }
   const int nbins = min(max_kblocks + (max_kblocks + kBlk - 1) / kBlk + 1, kItemsMaxBins);
+  if (a.correction) {
+    hipLaunchKernelGGL(mean_prep_kernel, dim3((unsigned)a.rows), dim3(256), 0, stream, a);
+    if (hipError_t e0 = hipGetLastError(); e0 != hipSuccess) return e0;
+  }
   hipLaunchKernelGGL(rank_tiles_kernel, dim3((unsigned)((a.rows + 255) / 256)), dim3(256), 0, stream, a);
   if (hipError_t e0 = hipGetLastError(); e0 != hipSuccess) return e0;
   hipLaunchKernelGGL(items_kernel, dim3(1), dim3(kItemsThreads), (size_t)nbins * sizeof(int), stream, a, nbins);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int items_cap = a.rows + a.extra_cap;
+  const dim3 info_grid((unsigned)((items_cap + 255) / 256));
+  if (fp8 && a.pair)
+    hipLaunchKernelGGL((item_info_kernel<true, true>), info_grid, dim3(256), 0, stream, a);
+  else if (fp8)
+    hipLaunchKernelGGL((item_info_kernel<true, false>), info_grid, dim3(256), 0, stream, a);
+  else if (a.pair)
+    hipLaunchKernelGGL((item_info_kernel<false, true>), info_grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((item_info_kernel<false, false>), info_grid, dim3(256), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(((items_cap + 7) / 8) * 8 * a.slices);
   if (fp8 && a.pair)
     hipLaunchKernelGGL((attn_d128_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream, a);

@@ -62,6 +62,11 @@ struct RunLayout {
   size_t rank_slot = 0;  // V^T path: per row {exact tiles, mean tiles, first partial slot, 0}, int4 [rows]
   size_t counters = 0;   // V^T path: item and split-row counts, int32 [4]
   size_t part = 0;       // V^T path: partial results of the chunks of split rows
+  size_t info = 0;       // V^T path: per work item, the values its workgroup starts from, int32 [items, kInfoInts]
+  size_t skip = 0;       // V^T path with correction: per CSR row, the skipped-block bitmask, u32 [rows, wskip]
+  size_t mlist = 0;      // V^T path with correction: per CSR row, the first mean token of each mean tile, [rows, mtmax]
+  size_t mcount = 0;     // V^T path with correction: per CSR row, its number of mean tiles, int32 [rows]
+  int wskip = 0, mtmax = 0;
   int64_t extra_cap = 0;  // most work items beyond one per row (chunks of split rows)
   size_t total = 0;
   int64_t mt_cap = 0;  // vbar^T tiles per KV head (V^T path)
@@ -76,6 +81,7 @@ constexpr int64_t kMaxExtraItems = 256;
 // Size of the device array that serves as fp2_plan_mask_noalloc's workspace.
 constexpr size_t kPlanScratchBytes = FP2_PLAN_NOALLOC_MAX_BYTES;
 constexpr int64_t kPartFloatsPerWave = 64 * 64 + 2 * 64;
+constexpr int kInfoInts = 48;  // a work item's record: see item_info_kernel
 inline int plan_words(const BatchInfo& info) { return int((info.max_kblocks + 31) / 32); }
 
 }  // namespace fp2

@@ -193,7 +193,13 @@ RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int n
     L.rank_slot = L.splits + up((size_t)L.extra_cap * 16 + 16);
     L.counters = L.rank_slot + up(nrows * 16);
     L.part = L.counters + 256;
-    L.total = L.part + up(2 * (size_t)L.extra_cap * slices * 8 * (size_t)kPartFloatsPerWave * 4);
+    L.info = L.part + up(2 * (size_t)L.extra_cap * slices * 8 * (size_t)kPartFloatsPerWave * 4);
+    L.wskip = (int)((info.max_kblocks + 31) / 32);
+    L.mtmax = (int)((info.max_kblocks + 127) / 128);
+    L.skip = L.info + up((nrows + (size_t)L.extra_cap) * kInfoInts * 4);
+    L.mlist = L.skip + up(nrows * (size_t)L.wskip * 4);
+    L.mcount = L.mlist + up(nrows * (size_t)L.mtmax * 4);
+    L.total = L.mcount + up(nrows * 4);
   } else {
     L.total = L.v16 + rows;
   }

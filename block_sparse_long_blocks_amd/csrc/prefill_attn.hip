@@ -611,6 +611,12 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.rank_slot = reinterpret_cast<int4*>(wsb + L.rank_slot);
   a.counters = reinterpret_cast<int32_t*>(wsb + L.counters);
   a.part = reinterpret_cast<float*>(wsb + L.part);
+  a.info = reinterpret_cast<int32_t*>(wsb + L.info);
+  a.skip = reinterpret_cast<uint32_t*>(wsb + L.skip);
+  a.mlist = reinterpret_cast<int32_t*>(wsb + L.mlist);
+  a.mcount = reinterpret_cast<int32_t*>(wsb + L.mcount);
+  a.wskip = L.wskip;
+  a.mtmax = L.mtmax;
   a.extra_cap = (int)L.extra_cap;
   // max_chunk_tiles > 0 caps the exact tiles of one work item below the
   // batch's own choice, < 0 turns the splitting of rows off
