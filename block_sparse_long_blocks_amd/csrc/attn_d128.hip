@@ -261,13 +261,12 @@ __global__ __launch_bounds__(256) void vt_mean_kernel(PrepArgs a) {
 // ---------------------------------------------------------------------------
 
 
-// bf16 pair (1, 1): the dot product with it sums two probabilities
-typedef __bf16 bf16x2e __attribute__((ext_vector_type(2)));
+// bf16 pair (1, 1)
 constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;
-// a step whose probabilities (per lane: 16 of them) sum to this or more
-// refreshes the reference max; probabilities stay below 2^64, so P (bf16),
-// l and O (float32) cannot overflow
-constexpr float kPmax = 18446744073709551616.0f;  // 2^64
+// a step with a probability of 2^kXmax or more (an exponent, log2 units, of
+// kXmax or more) refreshes the reference max; probabilities stay below 2^64,
+// so P (bf16), the row sums and O (float32) cannot overflow
+constexpr float kXmax = 64.0f;
 
 // Per-wave state and the work of one tile (32-key steps, see the header).
 //
@@ -275,48 +274,69 @@ constexpr float kPmax = 18446744073709551616.0f;  // 2^64
 // 8(i/4) + 4(l/32) + i%4 of its step.  A masked score is -inf; a mean token's
 // score carries log2(B)/scale extra, so that its probability carries the
 // block weight B.
+//
+// The row sums run on the matrix core beside PV, on exactly the rounded
+// probabilities that PV weighs V with, so that O / l is a convex combination
+// of the values whatever the rounding: a 16x16x32 MFMA takes a step half's
+// B operand of PV (lane l: 8 probabilities of query l%32) as its B, whose
+// column c then holds queries c and c+16 in k-groups {0, 2} and {1, 3}; an A
+// of ones in row 0 at k-groups 0 and 2 and in row 1 at k-groups 1 and 3
+// makes D row 0 the sum of query c and row 1 that of query c+16 (lanes 0-15,
+// elements 0 and 1).
 struct Wave {
   static constexpr int NS = kBlk / 32;  // 32-key steps per tile
   bf16x8 qf[kD / 16];  // bf16 query fragments (e4m3 inputs: the codes widened, for bf16 K tiles)
   i32x8 qf8[kD / 64];  // e4m3 query fragments (e4m3 inputs)
   f32x16 o[kD / 32];
+  f32x4 lsum;    // lanes 0-15: the row sums of queries l and l+16 (see above)
+  bf16x8 lones;  // the A operand of the row-sum MFMA
   float m;    // reference max (log2 units), shared by lanes l and l^32
   float nb;   // -m (0 while m = -inf): exp2(s * scale + nb) is the probability
-  float l;    // this lane's half of the denominator
+
+  __device__ __forceinline__ void init_sums() {
+    const int l = __lane_id();
+    const bool on = (l & 15) == (l >> 4 & 1) && (l & 15) < 2;  // row 0 at k-groups 0, 2; row 1 at 1, 3
+    const uint32_t w = on ? kOnesBf16x2 : 0u;
+    lones = __builtin_bit_cast(bf16x8, make_uint4(w, w, w, w));
+    lsum = f32x4{};
+  }
+  // the row sum of query l%32
+  __device__ __forceinline__ float row_sum() const {
+    const int l = __lane_id();
+    const float a = __shfl(lsum[0], l & 15), b = __shfl(lsum[1], l & 15);
+    return (l & 16) ? b : a;
+  }
 
   __device__ __forceinline__ void rescale(float alpha) {
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    // lanes 0-15 hold the sums of queries l and l+16
+    const float alpha_hi = __shfl(alpha, (__lane_id() & 15) + 16);
+    lsum[0] *= alpha;
+    lsum[1] *= alpha_hi;
   }
 
-  // bf16 probabilities of one step against the reference max; returns the
-  // sum of the rounded probabilities (two independent accumulation chains)
-  __device__ __forceinline__ float probs(const f32x16& s, float scl, bf16x8 (&pf)[2]) const {
-    float acc[2] = {0.f, 0.f};
+  // bf16 probabilities of one step against the reference max
+  __device__ __forceinline__ void probs(const f32x16& s, float scl, bf16x8 (&pf)[2]) const {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       uint32_t w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 4; ++q)
         w[q] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * r + 2 * q], scl, nb)),
                            __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * r + 2 * q + 1], scl, nb)));
-        // the denominator sums the same rounded probabilities that PV uses
-        acc[q & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2e, w[q]),
-                                                     __builtin_bit_cast(bf16x2e, kOnesBf16x2), acc[q & 1], false);
-      }
       // computed here, not sunk into the next step's region
       asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
       pf[r] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
     }
-    return acc[0] + acc[1];
   }
 
-  // Sets the reference max to cover this step's scores, rescales O (which
-  // holds every step before this one) and l_prev (l before this step), and
-  // redoes the step's probabilities.
-  __device__ __forceinline__ void refresh(const f32x16& s, float scl, float l_prev, bf16x8 (&pf)[2]) {
+  // Sets the reference max to cover this step's scores, rescales O and the
+  // row sums (which hold every step before this one), and redoes the step's
+  // probabilities.
+  __device__ __forceinline__ void refresh(const f32x16& s, float scl, bf16x8 (&pf)[2]) {
     float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);  // max3 chain
 #pragma unroll
     for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
@@ -326,82 +346,106 @@ struct Wave {
     m = mnew;
     nb = mnew == -INFINITY ? 0.f : -mnew;
     rescale(alpha);
-    l = l_prev * alpha + probs(s, scl, pf);
+    probs(s, scl, pf);
   }
 
   // ---- tiles on a fixed instruction schedule ----
   //
   // A tile's MFMAs run in a fixed order of ops n: QK(0) | QK(1) | QK(2) with
-  // PV(0) | QK(3) with PV(1) | PV(2) | PV(3), six regions.  bf16 QK (QK8
-  // false): 8 MFMAs 32x32x16 per step, 64 ops, regions of 8, 8, 16, 16, 8, 8
-  // with QK and PV alternating.  e4m3 QK (QK8 true): 2 MFMAs 32x32x64 per
-  // step, 40 ops, regions of 2, 2, 10, 10, 8, 8 with the two QK ops at the
-  // head and the middle of regions 2 and 3.  Each op is one slot closed by a
+  // PV(0), L(0) | QK(3) with PV(1), L(1) | PV(2), L(2) | PV(3), L(3), six
+  // regions, where L(j) are the two row-sum MFMAs of step j (each after the
+  // PV ops of its half of the step, on the same probabilities).  bf16 QK (QK8 false): 8 MFMAs 32x32x16
+  // per step, 72 ops, regions of 8, 8, 18, 18, 10, 10 with QK and PV
+  // alternating.  e4m3 QK (QK8 true): 2 MFMAs 32x32x64 per step, 48 ops,
+  // regions of 2, 2, 12, 12, 10, 10 with the two QK ops at the head and the
+  // middle of the PV ops of regions 2 and 3.  Each op is one slot closed by a
   // scheduling barrier, so this is the issue order: an op's LDS operand (16
-  // bytes, 32 for an e4m3 QK op) is read kLA slots ahead (across regions),
-  // and the softmax of step j runs in region j+1 as a stream of groups
-  // spread over the slots, each value produced a group or more before it is
-  // consumed, so that no vector instruction waits on the one just before it
-  // and the matrix core keeps getting work.  The refresh test of step j
-  // closes region j+1, before PV(j) reads P(j).
+  // bytes, 32 for an e4m3 QK op, none for a row-sum op) is read kLA slots
+  // ahead (across regions), and the softmax of step j runs in region j+1 as
+  // a stream of groups spread over the slots, each value produced a group or
+  // more before it is consumed, so that no vector instruction waits on the
+  // one just before it and the matrix core keeps getting work.  The refresh
+  // test of step j closes region j+1, before PV(j) and L(j) read P(j).
   static constexpr int kLA = 4;
   static constexpr int kGroups = 20;
   static constexpr int kRing = 16;  // operand reads in flight (16-byte registers quads)
 
+  enum : int { kOpQK = 0, kOpPV = 1, kOpL = 2 };
+  static constexpr int kMaxOps = 72;
+  // the schedule: op n's kind, step and index (QK: d-slice kk, 16 wide or 64
+  // wide for e4m3; PV: 4 r + dt; L: r), its operand reads and the ring index
+  // of its first read; start[r] is the first op of region r
+  struct Ops {
+    int n;
+    int start[7];
+    int kind[kMaxOps], step[kMaxOps], idx[kMaxOps], reads[kMaxOps], read0[kMaxOps];
+  };
   template <bool QK8>
-  static constexpr int n_ops() { return QK8 ? 40 : 64; }
-  // first op of region r (r = 0..6)
-  template <bool QK8>
-  static constexpr int region_start(int r) {
-    constexpr int b16[7] = {0, 8, 16, 32, 48, 56, 64};
-    constexpr int b8[7] = {0, 2, 4, 14, 24, 32, 40};
-    return QK8 ? b8[r] : b16[r];
-  }
-  template <bool QK8>
-  static constexpr bool op_qk(int n) {
-    if (QK8) return n < 4 || ((n >= 4 && n < 24) && ((n - 4) % 10 == 0 || (n - 4) % 10 == 5));
-    return n < 16 || (n < 48 && (n & 1) == 0);
-  }
-  template <bool QK8>
-  static constexpr int op_step(int n) {
-    if (QK8) {
-      if (op_qk<QK8>(n)) return n < 2 ? 0 : n < 4 ? 1 : n < 14 ? 2 : 3;
-      return n < 14 ? 0 : n < 24 ? 1 : n < 32 ? 2 : 3;
+  static constexpr Ops make_ops() {
+    Ops t{};
+    int n = 0;
+    auto push = [&](int kind, int j, int i) {
+      t.kind[n] = kind;
+      t.step[n] = j;
+      t.idx[n] = i;
+      t.reads[n] = kind == kOpL ? 0 : (kind == kOpQK && QK8) ? 2 : 1;
+      t.read0[n] = n == 0 ? 0 : t.read0[n - 1] + t.reads[n - 1];
+      ++n;
+    };
+    const int nqk = QK8 ? 2 : 8;
+    for (int j = 0; j < 2; ++j) {  // regions 0, 1: QK(0), QK(1)
+      t.start[j] = n;
+      for (int i = 0; i < nqk; ++i) push(kOpQK, j, i);
     }
-    return op_qk<QK8>(n) ? (n < 8 ? 0 : n < 16 ? 1 : n < 32 ? 2 : 3) : (n < 32 ? 0 : n < 48 ? 1 : n < 56 ? 2 : 3);
-  }
-  // QK: d-slice kk (16 wide, or 64 wide for e4m3); PV: 4 r + dt
-  template <bool QK8>
-  static constexpr int op_idx(int n) {
-    if (QK8) {
-      if (n < 4) return n & 1;
-      if (n < 24) {
-        const int t = (n - 4) % 10;
-        return t == 0 ? 0 : t == 5 ? 1 : t - 1 - (t > 5 ? 1 : 0);
+    for (int j = 0; j < 2; ++j) {  // regions 2, 3: QK(j+2) with PV(j) and L(j)
+      t.start[2 + j] = n;
+      for (int i = 0; i < 8; ++i) {
+        if (QK8 ? i % 4 == 0 : true) push(kOpQK, j + 2, QK8 ? i / 4 : i);
+        push(kOpPV, j, i);
+        if (i % 4 == 3) push(kOpL, j, i / 4);  // after the PV ops of half i/4
       }
-      return n & 7;
     }
-    return n < 16 ? (n & 7) : n < 48 ? ((n & 15) >> 1) : (n & 7);
+    for (int j = 2; j < 4; ++j) {  // regions 4, 5: PV(j) and L(j)
+      t.start[2 + j] = n;
+      for (int i = 0; i < 8; ++i) {
+        push(kOpPV, j, i);
+        if (i % 4 == 3) push(kOpL, j, i / 4);
+      }
+    }
+    t.start[6] = n;
+    t.n = n;
+    return t;
   }
   template <bool QK8>
-  static constexpr int op_reads(int n) { return QK8 && op_qk<QK8>(n) ? 2 : 1; }
+  struct Sched {
+    static constexpr Ops ops = make_ops<QK8>();
+  };
+  template <bool QK8>
+  static constexpr int n_ops() { return Sched<QK8>::ops.n; }
+  template <bool QK8>
+  static constexpr int region_start(int r) { return Sched<QK8>::ops.start[r]; }
+  template <bool QK8>
+  static constexpr int op_kind(int n) { return Sched<QK8>::ops.kind[n]; }
+  template <bool QK8>
+  static constexpr int op_step(int n) { return Sched<QK8>::ops.step[n]; }
+  template <bool QK8>
+  static constexpr int op_idx(int n) { return Sched<QK8>::ops.idx[n]; }
+  template <bool QK8>
+  static constexpr int op_reads(int n) { return Sched<QK8>::ops.reads[n]; }
   // index of op n's first operand read
   template <bool QK8>
-  static constexpr int read0(int n) {
-    int r = 0;
-    for (int k = 0; k < n; ++k) r += op_reads<QK8>(k);
-    return r;
-  }
+  static constexpr int read0(int n) { return Sched<QK8>::ops.read0[n]; }
 
-  // LDS address of read e of op n.  bf16 K / V^T: the swizzled 256-byte-row
-  // layout at the two per-lane bases off0 / off1.  e4m3 K: 128-byte rows,
-  // 1 KB per 8 rows, 16-byte chunk c of row r in slot c ^ (r % 8); off8[2 kk
-  // + e] is lane l's slot of chunk 4 kk + 2 (l/32) + e in row l%32.
+  // LDS address of read e of op n (a QK or PV op).  bf16 K / V^T: the
+  // swizzled 256-byte-row layout at the two per-lane bases off0 / off1.
+  // e4m3 K: 128-byte rows, 1 KB per 8 rows, 16-byte chunk c of row r in slot
+  // c ^ (r % 8); off8[2 kk + e] is lane l's slot of chunk 4 kk + 2 (l/32) + e
+  // in row l%32.
   template <bool QK8>
   __device__ __forceinline__ const uint8_t* op_addr(int n, int e, const uint8_t* Kt, const uint8_t* Vt, int off0,
                                                     int off1, const int (&off8)[4]) const {
     const int j = op_step<QK8>(n), i = op_idx<QK8>(n);
-    if (op_qk<QK8>(n)) {
+    if (op_kind<QK8>(n) == kOpQK) {
       if constexpr (QK8) return Kt + off8[2 * i + e] + 4096 * j;
       return Kt + ((i & 1) ? off1 : off0) + 8 * kGS * j + 64 * (i >> 1);
     }
@@ -409,10 +453,10 @@ struct Wave {
   }
 
   // softmax stream of one step: group g computes x[g] (g < 16), e[g-2]
-  // (2 <= g < 18), the bf16 pair w[(g-4)/2] (even g >= 4) and adds e[g-4]
-  // to the row sum (g >= 4)
+  // (2 <= g < 18), the bf16 pair w[(g-4)/2] (even g >= 4) and takes x[g-2]
+  // and x[g-1] into the step's largest exponent mx (even g, 2 <= g < 18)
   struct Soft {
-    float x[16], e[16], acc[2];
+    float x[16], e[16], mx;
     uint32_t w[8];
   };
   // Masked tiles pass the per-lane bit mask M of the step's allowed keys
@@ -438,11 +482,9 @@ struct Wave {
       st.w[(g - 4) >> 1] = pack_bf16x2(st.e[g - 4], st.e[g - 3]);
       asm volatile("" : "+v"(st.w[(g - 4) >> 1]));
     }
-    if (g >= 4 && g < 20) {
-      // the row sum adds the float32 probabilities (PV takes them rounded to
-      // bf16: O / l then errs by at most 2^-9 max|v| relative to exact P)
-      st.acc[g & 1] += st.e[g - 4];
-      asm volatile("" : "+v"(st.acc[g & 1]));
+    if (g >= 2 && g < 18 && (g & 1) == 0) {
+      st.mx = fmaxf(fmaxf(st.mx, st.x[g - 2]), st.x[g - 1]);
+      asm volatile("" : "+v"(st.mx));
     }
   }
 
@@ -461,7 +503,7 @@ struct Wave {
     for (int t = 0; t < S; ++t) {
       const int n = N0 + t;
       const int r0 = read0<QK8>(n) % kRing;
-      if (op_qk<QK8>(n)) {
+      if (op_kind<QK8>(n) == kOpQK) {
         if constexpr (QK8) {
           const uint4 lo = __builtin_bit_cast(uint4, fr[r0]), hi = __builtin_bit_cast(uint4, fr[(r0 + 1) % kRing]);
           const i32x8 ka = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -469,9 +511,11 @@ struct Wave {
         } else {
           sn = mfma_bf16_32x32x16(fr[r0], qf[op_idx<QK8>(n)], sn);
         }
-      } else {
+      } else if (op_kind<QK8>(n) == kOpPV) {
         const int i = op_idx<QK8>(n);
         o[i & 3] = mfma_bf16_32x32x16(fr[r0], pp[i >> 2], o[i & 3]);
+      } else {
+        lsum = mfma_bf16_16x16x32(lones, pp[op_idx<QK8>(n)], lsum);
       }
       if (n + kLA < n_ops<QK8>()) {
         const int nr = n + kLA;
@@ -489,24 +533,21 @@ struct Wave {
     }
   }
 
-  // closes the softmax of a step: P, l, and the refresh when the step's
-  // probabilities reached kPmax (or it is the first step of the row)
+  // closes the softmax of a step: P, and the refresh when a probability of
+  // the step reached 2^kXmax (or it is the first step of the row)
   template <bool MASKED>
   __device__ __forceinline__ void soft_close(Soft& st, const f32x16& s, float scl, bool force, bf16x8 (&pc)[2],
                                              uint32_t M, float cbs) {
     pc[0] = __builtin_bit_cast(bf16x8, make_uint4(st.w[0], st.w[1], st.w[2], st.w[3]));
     pc[1] = __builtin_bit_cast(bf16x8, make_uint4(st.w[4], st.w[5], st.w[6], st.w[7]));
-    const float step = st.acc[0] + st.acc[1];
-    const float l_prev = l;
-    l += step;
-    if (__any(!(step < kPmax)) || force) {
+    if (__any(!(st.mx < kXmax)) || force) {
       if constexpr (MASKED) {
         f32x16 sm;  // the scores as the stream saw them: + cbs where allowed, -inf elsewhere
 #pragma unroll
         for (int i = 0; i < 16; ++i) sm[i] = (M >> (8 * (i >> 2) + (i & 3))) & 1u ? s[i] + cbs : -INFINITY;
-        refresh(sm, scl, l_prev, pc);
+        refresh(sm, scl, pc);
       } else {
-        refresh(s, scl, l_prev, pc);
+        refresh(s, scl, pc);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -568,7 +609,7 @@ struct Wave {
     for (int j = 0; j < NS; ++j) {
       s = sn;
       sn = f32x16{};
-      st.acc[0] = st.acc[1] = 0.f;
+      st.mx = -INFINITY;
       // region j+1: QK(j+1) (j < 3), PV(j-1) (j > 0), softmax(j)
       if (j == 0) region<1, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[0], dma);
       if (j == 1) region<2, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[1], dma);
@@ -686,7 +727,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   Wave ws;
   ws.m = -INFINITY;
   ws.nb = 0.f;
-  ws.l = 0.f;
+  ws.init_sums();
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt) ws.o[dt] = f32x16{};
   float qs = 1.f;  // e4m3: the query block's scale
@@ -1079,7 +1120,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
         for (int q4 = 0; q4 < 4; ++q4)
           *reinterpret_cast<f32x4*>(po + ((dt * 4 + q4) * 64 + lane) * 4) =
               f32x4{ws.o[dt][4 * q4 + 0], ws.o[dt][4 * q4 + 1], ws.o[dt][4 * q4 + 2], ws.o[dt][4 * q4 + 3]};
-      const float lsum = sum_halves(ws.l);
+      const float lsum = ws.row_sum();
       *reinterpret_cast<float2*>(po + 64 * 64 + 2 * lane) = make_float2(ws.m, lsum);
     }
   } else if (!a.out_f32) {
@@ -1090,7 +1131,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     // instructions of 32 scattered pieces each, whose draining held the
     // workgroup's slot for several microseconds.
     if (wave_active) {
-      const float inv = 1.0f / sum_halves(ws.l);  // rows past the sequence end are never stored
+      const float inv = 1.0f / ws.row_sum();  // rows past the sequence end are never stored
       uint8_t* stg = (wave < 4 ? K0 : V0) + (wave & 3) * kStageBytes;
       const int r = lane & 31;
 #pragma unroll
@@ -1115,7 +1156,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
       }
     }
   } else if (q_valid) {
-    const float inv = 1.0f / sum_halves(ws.l);
+    const float inv = 1.0f / ws.row_sum();
     const int64_t obase = ((int64_t)(q0 + I * kBlk + tq) * a.hq + h) * kD;
     if (a.out_f32) {
       float* orow = static_cast<float*>(a.out) + obase;

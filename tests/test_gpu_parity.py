@@ -362,11 +362,10 @@ def test_reference_max_refresh_in_every_tile_kind(dtype, kvb):
     run per query block I): the running reference max must be raised after the first
     step inside exact tiles, diagonal tiles and mean-token tiles (the high span
     skipped, its mean tokens on top), and the result must still match the oracle on
-    the same mask.  Here one or two keys carry each row, so the kernel's one
-    systematic error shows whole: PV takes the probabilities rounded to bf16 while
-    the row sum adds them in float32, which moves O by at most 2^-9 max|v|; the
-    bound adds that term, and the measured worst error is printed beside the 1e-2
-    bar.  e4m3: one scale per KV block and head (query block and
+    the same mask.  One or two keys carry each row here, so a row sum that did not
+    add exactly the bf16-rounded probabilities PV weighs V with would show whole
+    (up to 2^-9 max|v|); the bar is the plain 1e-2 (4e-2 for e4m3), and the
+    measured worst error is printed.  e4m3: one scale per KV block and head (query block and
     head for Q).  kvb = 64: 64-token KV blocks under 128-token query blocks, two to a
     tile, each half with its own K scale; rows of three or four entries give full and
     lone-entry pair tiles."""
@@ -410,6 +409,5 @@ def test_reference_max_refresh_in_every_tile_kind(dtype, kvb):
         torch.cuda.synchronize()
         got = L.out[:T].cpu().numpy().astype(np.float64)
         ref = O.run_batch([tuple(dec)], B, 0.0, corr, keeps=[keep], BK=kvb)["out"]
-        worst = check_out(got, ref, TOL[dtype], "f32", extra=2.0 ** -9 * float(np.abs(dec[2]).max()))
-        print(f"\nrefresh stress {dtype} kvb={kvb} correction={corr}: max abs err {worst:.4f} "
-              f"(bar {TOL[dtype]}, bound {TOL[dtype] + 2.0 ** -9 * float(np.abs(dec[2]).max()):.4f})")
+        worst = check_out(got, ref, TOL[dtype], "f32")
+        print(f"\nrefresh stress {dtype} kvb={kvb} correction={corr}: max abs err {worst:.4f} (bar {TOL[dtype]})")
