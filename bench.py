@@ -183,7 +183,7 @@ def run_workload(name, tau, args, torch, lib, synth, corr=True, stats_cache=Fals
         e1.record(stream)
         torch.cuda.synchronize()
         res["dense_ms_per_layer"] = e0.elapsed_time(e1) / args.dense_steps
-        res["speedup_vs_dense"] = res["dense_ms_per_layer"] / step_ms
+        res["speedup_vs_dense"] = res["dense_ms_per_layer"] / res["ms_per_layer"]
         L(tau, corr)  # leave the sparse plan in place
         torch.cuda.synchronize()
     if stats_cache:
