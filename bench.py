@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 (e4m3) 128K run")
     ap.add_argument("--no-dense", action="store_true", help="skip the tau=+inf comparison run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=96, help="(q-block, KV head) rows timed on the CPU")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="(q-block, KV head) rows timed on the CPU (about 10-15 s)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the 128K line: latency against kept-block density at 64K (bf16 and e4m3), "
                          "with and without mean correction, beside the ideal density x dense line")
@@ -457,7 +457,7 @@ def config_runs(args, torch, lib, synth):
            "steps": args.steps, "warmup": args.warmup, "runs": rows}
     if args.configs_out:
         with open(args.configs_out, "w") as f:
-            f.write("| workload | dtype | correction | tau | density | ms/layer | stage 1 (fp2_stage1) "
+            f.write("| workload | dtype | correction | tau | density | ms/layer | stage 1 (fp2_block_stats + fp2_plan_mask) "
                     "| prefill_run | dense-equiv TFLOP/s | MFMA fraction of prefill_run | dense ms/layer "
                     "| speedup vs dense |\n|---|---|---|---|---|---|---|---|---|---|---|---|\n")
             for r in rows:
@@ -627,8 +627,8 @@ def main():
         "config": {"workload": "c128k_bf16: 1 seq L=131072, 32 q / 8 kv heads, d=128, block 128, band + 16 "
                                "sink columns, tau for 5% kept blocks, mean correction on",
                    "tau": bf["tau"], "density": round(bf["density"], 5), "nnz": bf["nnz"]},
-        "roofline": {"bound": "mfma", "kernel": "attn_d128_kernel<false, false> (fp2_prefill_run: plus its V^T preparation "
-                               "kernels, ~1% of the call)", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "attn_d128_kernel<false, false> (timed as fp2_prefill_run, which also launches "
+                               "the V^T, mean-token and work-item preparation kernels: ~0.19 ms, ~2.3% of the call)", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
                      "flops_per_launch": attn_flops,
