@@ -29,15 +29,16 @@
 //    read is a conflict-free ds_read_b128 at a per-lane base plus an
 //    immediate offset.
 //  * S^T = K Q^T on the bf16 32x32x16 MFMA or the e4m3 32x32x64 MFMA (a lane
-//    holds the keys of one query, so row sums are in-lane plus one lane^32
+//    holds keys of one query, so row maxima are in-lane plus one lane^32
 //    exchange); O^T = V^T P^T on the bf16 MFMA with P straight from the
-//    score registers.
+//    score registers, and the row sums on the matrix core from the same P
+//    (a 16x16x32 MFMA per 16-key half of a step, see Wave).
 //  * Each tile runs in 32-key steps on a fixed instruction schedule: every
 //    MFMA is a slot closed by a scheduling barrier, the QK^T MFMAs of step
 //    j+1 and the PV MFMAs of step j-1 share a region with the softmax of
 //    step j, operand reads run a few slots ahead and the softmax values are
 //    consumed a group or more after they are produced.  Masks are applied
-//    to the exponent; the reference max is refreshed only when probabilities
+//    to the exponent; the reference max is refreshed only when a probability
 //    would reach 2^64.  The younger wave of each SIMD takes the higher issue
 //    priority for the first half of a tile (the arbiter otherwise serves the
 //    older one first).
