@@ -32,7 +32,7 @@ STATUS_NAMES = {0: "FP2_OK", 1: "FP2_ERR_INVALID", 2: "FP2_ERR_UNSUPPORTED", 3: 
 SYMBOLS = ("fp2_block_stats", "fp2_block_stats_cache_rows", "fp2_block_stats_cached", "fp2_gather_block_stats",
            "fp2_plan_workspace_bytes", "fp2_plan_max_nnz", "fp2_plan_mask", "fp2_plan_mask_noalloc",
            "fp2_stage1_workspace_bytes", "fp2_stage1", "fp2_run_workspace_bytes", "fp2_prefill_run",
-           "fp2_last_error")
+           "fp2_debug_bounds_word", "fp2_last_error")
 
 _p = ctypes.c_void_p
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -86,6 +86,8 @@ _lib.fp2_prefill_run.argtypes = [ctypes.POINTER(CBatch), ctypes.POINTER(CQ), cty
                                  _p, _p, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _p, ctypes.c_int32, _p,
                                  ctypes.c_size_t, _p]
 _lib.fp2_prefill_run.restype = ctypes.c_int
+_lib.fp2_debug_bounds_word.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
+_lib.fp2_debug_bounds_word.restype = ctypes.c_int
 _lib.fp2_last_error.argtypes = []
 _lib.fp2_last_error.restype = ctypes.c_char_p
 
@@ -295,6 +297,14 @@ def fp2_prefill_run(batch: Batch, q: Queries, kv: KVCache, row_ptr: torch.Tensor
                                 _ptr(col_idx), _ptr(kbar), _ptr(vbar), int(bool(mean_correction)),
                                 ctypes.c_float(softmax_scale), out_dtype, _ptr(out), int(max_chunk_tiles),
                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def fp2_debug_bounds_word() -> int:
+    """The device error word of a FP2_DEBUG_BOUNDS build (read and cleared; waits for the device).  The
+    package's own libfp2.so is a release build: Fp2Error(FP2_ERR_UNSUPPORTED)."""
+    w = ctypes.c_uint32(0)
+    _check(_lib.fp2_debug_bounds_word(ctypes.byref(w)))
+    return int(w.value)
 
 
 def library_path() -> str:

@@ -1,7 +1,11 @@
 """Build libfp2.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-Usage: python block_sparse_long_blocks_amd/build.py [--debug]   (from the repository root; running it as a
-module would import the package, which needs the library first)
+Usage: python block_sparse_long_blocks_amd/build.py [--debug] [--debug-bounds]   (from the repository root;
+running it as a module would import the package, which needs the library first)
+
+--debug-bounds builds libfp2_bounds.so beside libfp2.so: the same sources with FP2_DEBUG_BOUNDS, whose calls
+check page ids and the CSR on the device (fp2_debug_bounds_word in include/fp2.h).  The package always loads
+libfp2.so; tests load the bounds build by path.
 
 build_sanitized() links a second library for host-side checking only: the C-ABI host code (argument checks,
 launch set-up) built with AddressSanitizer and UndefinedBehaviorSanitizer by the host compiler, beside the
@@ -17,10 +21,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp2.so")
+LIB_BOUNDS = os.path.join(PKG, "libfp2_bounds.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["fp2_api.cpp", "fp2_validate.cpp", "block_stats.hip", "plan_mask.hip", "prefill_attn.hip",
-           "attn_d128.hip"]
+           "attn_d128.hip", "debug_bounds.hip"]
 HOST_SOURCES = ["fp2_api.cpp", "fp2_validate.cpp"]  # plain host C++ (HIP runtime API only)
 CLANGXX = "/opt/rocm/llvm/bin/clang++"
 SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
@@ -34,30 +39,35 @@ DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-pa
 EXTRA = {"attn_d128.hip": ["-fno-honor-nans"]}
 
 
-def _compile(src, opt):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, *EXTRA.get(src, []), opt, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, opt, out_dir=BUILD, defines=()):
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, *EXTRA.get(src, []), *defines, opt, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj, [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
 
 
-def build(debug: bool = False, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(debug: bool = False, verbose: bool = True, bounds: bool = False) -> str:
+    """libfp2.so, or with bounds=True libfp2_bounds.so (FP2_DEBUG_BOUNDS); returns its path."""
+    out_dir = os.path.join(BUILD, "bounds") if bounds else BUILD
+    lib = LIB_BOUNDS if bounds else LIB
+    defines = ("-DFP2_DEBUG_BOUNDS",) if bounds else ()
+    os.makedirs(out_dir, exist_ok=True)
     opt = "-O1" if debug else "-O3"
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(lambda s: _compile(s, opt), SOURCES))
+        results = list(ex.map(lambda s: _compile(s, opt, out_dir, defines), SOURCES))
     for _, warn in results:
         if verbose and warn:
             print("\n".join(warn), file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def asan_runtime() -> str:
@@ -100,4 +110,4 @@ def build_sanitized(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(debug="--debug" in sys.argv))
+    print(build(debug="--debug" in sys.argv, bounds="--debug-bounds" in sys.argv))

@@ -12,6 +12,7 @@ namespace fp2 {
 constexpr float kLazy = 8.0f;
 
 struct AttnArgs {
+  const uint32_t* dbg;  // bounds-checking builds: the error word (see fp2_device.h), else nullptr
   const int32_t* cu_seqlens_q;
   const int32_t* seqlens_k;
   const int32_t* cu_qblocks;

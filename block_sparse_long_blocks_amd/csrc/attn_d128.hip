@@ -100,6 +100,7 @@ __device__ __forceinline__ constexpr int key_of_pos(int p) {
 // Operand preparation
 // ---------------------------------------------------------------------------
 struct PrepArgs {
+  const uint32_t* dbg;  // bounds-checking builds: the error word, else nullptr
   const int32_t* cu_kblocks;
   const int32_t* cu_seqlens_q;
   const int32_t* seqlens_k;
@@ -141,6 +142,7 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
 // block (rows of 128 bytes), two blocks per workgroup.
 template <bool FP8, bool HALF>
 __global__ __launch_bounds__(256) void vt_exact_kernel(PrepArgs a) {
+  FP2_BOUNDS_GUARD(a.dbg);
   constexpr int KB = HALF ? 64 : kBlk;  // keys of a block
   const int t = threadIdx.x;
   const int kb = HALF ? 2 * blockIdx.x + (t >> 7) : blockIdx.x, g = blockIdx.y;
@@ -184,6 +186,7 @@ __global__ __launch_bounds__(256) void vt_exact_kernel(PrepArgs a) {
 // kept block beside a diagonal one.
 template <bool HALF>
 __global__ __launch_bounds__(256) void kd_kernel(PrepArgs a) {
+  FP2_BOUNDS_GUARD(a.dbg);
   constexpr int KB = HALF ? 64 : kBlk;
   const int kb = blockIdx.x, g = blockIdx.y;
   const int s = find_seq(a.cu_kblocks, a.num_seqs, kb);
@@ -216,6 +219,7 @@ __global__ __launch_bounds__(256) void kd_kernel(PrepArgs a) {
 // cu_kblocks[s]/128 + s + mt never collides across sequences and stays
 // below mt_cap = total_kblocks/128 + num_seqs + 1.
 __global__ __launch_bounds__(256) void vt_mean_kernel(PrepArgs a) {
+  FP2_BOUNDS_GUARD(a.dbg);
   const int mt = blockIdx.x, s = blockIdx.y, g = blockIdx.z;
   const int kb0 = a.cu_kblocks[s];
   const int nkb = a.cu_kblocks[s + 1] - kb0;
@@ -645,6 +649,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t V1[kTileLds];
   __shared__ uint32_t kept[kMaxKBlocks / 32];
   __shared__ int mtile[kMaxKBlocks / kBlk + 1];
+  FP2_BOUNDS_GUARD(a.dbg);
 
   // ---- tile decode: 8 consecutive work items form a group, the slices of
   // one item share blockIdx % 8 (one XCD); the items are in launch order,
@@ -1200,6 +1205,7 @@ __device__ void rank_tiles(const AttnArgs& a, int r, int& nexact, int& nmean) {
 // one skipped block, by first mean token), so that a workgroup starting the
 // row reads them instead of building them.
 __global__ __launch_bounds__(256) void mean_prep_kernel(AttnArgs a) {
+  FP2_BOUNDS_GUARD(a.dbg);
   __shared__ uint32_t kw[kMaxKBlocks / 32];
   const int row = blockIdx.x;
   const int qb = row % a.total_qblocks;
@@ -1247,6 +1253,7 @@ __global__ __launch_bounds__(256) void mean_prep_kernel(AttnArgs a) {
 // items_kernel: {exact tiles, mean tiles (an upper bound), first partial slot
 // (-1 until items_kernel splits the row), 0}.
 __global__ __launch_bounds__(256) void rank_tiles_kernel(AttnArgs a) {
+  FP2_BOUNDS_GUARD(a.dbg);
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= a.rows) return;
   int ne, nm;
@@ -1270,6 +1277,7 @@ constexpr int kMinChunkTiles = 16;
 constexpr int kItemsPerCuShare = 4;
 constexpr int kRankCache = 8;  // rank records a thread keeps in registers (8192 ranks with 1024 threads)
 __global__ __launch_bounds__(kItemsThreads) void items_kernel(AttnArgs a, int nbins) {
+  FP2_BOUNDS_GUARD(a.dbg);
   extern __shared__ int hist[];  // [nbins]
   __shared__ int part[kItemsThreads];
   __shared__ int s_tot[2], s_cnt[3];
@@ -1380,6 +1388,7 @@ __global__ __launch_bounds__(kItemsThreads) void items_kernel(AttnArgs a, int nb
 //   wave w (w < 4) moves of tiles 0 and 1 (entry 2 w + half).
 template <bool FP8, bool PAIR>
 __global__ __launch_bounds__(256) void item_info_kernel(AttnArgs a) {
+  FP2_BOUNDS_GUARD(a.dbg);
   constexpr int KB = PAIR ? 64 : kBlk;
   const int pos = blockIdx.x * 256 + threadIdx.x;
   if (pos >= a.rows + a.extra_cap) return;
@@ -1487,6 +1496,7 @@ __global__ __launch_bounds__(256) void item_info_kernel(AttnArgs a) {
 // units), then the same O / l store as the attention epilogue.  One
 // workgroup per (split row, slice), the attention kernel's lane layout.
 __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
+  FP2_BOUNDS_GUARD(a.dbg);
   if ((int)blockIdx.x >= ld_uniform(a.counters, 1)) return;
   const int32_t* sp = reinterpret_cast<const int32_t*>(a.splits + blockIdx.x);
   const int rank = ld_uniform(sp, 0), slot0 = ld_uniform(sp, 1), nch = ld_uniform(sp, 2);
@@ -1550,6 +1560,7 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
                        hipStream_t stream) {
   AttnArgs a = a_in;
   PrepArgs p;
+  p.dbg = a.dbg;
   p.cu_kblocks = a.cu_kblocks;
   p.cu_seqlens_q = a.cu_seqlens_q;
   p.seqlens_k = a.seqlens_k;

@@ -30,12 +30,14 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(StatsArgs a) {
   __shared__ float red_k[kThreads][N + 1];
   __shared__ float red_v[kThreads][N + 1];
   __shared__ int s_pg[kPoolMaxPages];
+  FP2_BOUNDS_GUARD(a.dbg);
   kv_block_stats<ESZ>(a, blockIdx.x, red_k, red_v, s_pg);
 }
 
 // kbar / vbar [g, kb, :] <- the cache rows of block kb (one workgroup per
 // global KV block, float4 copies).
 __global__ __launch_bounds__(kThreads) void gather_stats_kernel(StatsArgs a, const float* kc, const float* vc) {
+  FP2_BOUNDS_GUARD(a.dbg);
   const int kb = blockIdx.x;
   const int s = find_seq(a.cu_kblocks, a.num_seqs, kb);
   const int J = kb - a.cu_kblocks[s];

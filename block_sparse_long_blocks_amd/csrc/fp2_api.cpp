@@ -45,6 +45,8 @@ fp2_status fp2_block_stats(const fp2_batch* batch, const fp2_kv* kv, float* kbar
   if (st != FP2_OK) return st;
   if ((st = check_kv(kv, batch, info)) != FP2_OK) return st;
   if (info.total_kblocks > 0 && (!kbar || !vbar)) return fail(FP2_ERR_INVALID, "kbar/vbar is NULL");
+  if (hipError_t e = launch_check_pages(batch, kv, (hipStream_t)stream); e != hipSuccess)
+    return hip_status(e, "fp2_block_stats bounds check");
   return hip_status(launch_block_stats(batch, kv, info, kbar, vbar, (hipStream_t)stream),
                     "fp2_block_stats launch");
 }
@@ -68,6 +70,8 @@ fp2_status fp2_block_stats_cached(const fp2_batch* batch, const fp2_kv* kv, floa
   if (refresh_prefix != 0 && refresh_prefix != 1) return fail(FP2_ERR_INVALID, "refresh_prefix must be 0 or 1");
   if (info.total_kblocks > 0 && (!kbar_cache || !vbar_cache))
     return fail(FP2_ERR_INVALID, "kbar_cache/vbar_cache is NULL");
+  if (hipError_t e = launch_check_pages(batch, kv, (hipStream_t)stream); e != hipSuccess)
+    return hip_status(e, "fp2_block_stats_cached bounds check");
   return hip_status(launch_block_stats_cached(batch, kv, info, kbar_cache, vbar_cache, refresh_prefix,
                                               (hipStream_t)stream),
                     "fp2_block_stats_cached launch");
@@ -83,6 +87,8 @@ fp2_status fp2_gather_block_stats(const fp2_batch* batch, const fp2_kv* kv, cons
     return fail(FP2_ERR_UNSUPPORTED, "the block stats cache needs page_size and the KV block to divide one another");
   if (info.total_kblocks > 0 && (!kbar_cache || !vbar_cache || !kbar || !vbar))
     return fail(FP2_ERR_INVALID, "a cache or output pointer is NULL");
+  if (hipError_t e = launch_check_pages(batch, kv, (hipStream_t)stream); e != hipSuccess)
+    return hip_status(e, "fp2_gather_block_stats bounds check");
   return hip_status(launch_gather_stats(batch, kv, info, kbar_cache, vbar_cache, kbar, vbar, (hipStream_t)stream),
                     "fp2_gather_block_stats launch");
 }
@@ -185,6 +191,8 @@ fp2_status fp2_stage1(const fp2_batch* batch, const fp2_q* q, const fp2_kv* kv, 
   if (workspace_bytes < wneed)
     return fail(FP2_ERR_CAPACITY, "stage-1 workspace " + std::to_string(workspace_bytes) + " < " +
                                       std::to_string(wneed) + " bytes");
+  if (hipError_t e = launch_check_pages(batch, kv, (hipStream_t)stream); e != hipSuccess)
+    return hip_status(e, "fp2_stage1 bounds check");
   return hip_status(launch_stage1(batch, q, kv, info, tau, kbar, vbar, row_ptr, col_idx, nnz, scores, workspace,
                                   (hipStream_t)stream),
                     "fp2_stage1 launch");
@@ -227,10 +235,20 @@ fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv*
       return fail(FP2_ERR_CAPACITY, "run workspace " + std::to_string(workspace_bytes) + " < " +
                                         std::to_string(wneed) + " bytes");
   }
+  if (hipError_t e = launch_check_pages(batch, kv, (hipStream_t)stream); e != hipSuccess)
+    return hip_status(e, "fp2_prefill_run bounds check");
+  if (hipError_t e = launch_check_csr(batch, info, kv->num_kv_heads, row_ptr, col_idx, (hipStream_t)stream);
+      e != hipSuccess)
+    return hip_status(e, "fp2_prefill_run bounds check");
   return hip_status(launch_prefill(batch, q, kv, info, row_ptr, col_idx, kbar, vbar,
                                    mean_correction, softmax_scale, out_dtype == FP2_OUT_F32, out, max_chunk_tiles,
                                    workspace, (hipStream_t)stream),
                     "fp2_prefill_run launch");
+}
+
+fp2_status fp2_debug_bounds_word(uint32_t* word) {
+  if (!word) return fail(FP2_ERR_INVALID, "word is NULL");
+  return read_bounds_word(word);
 }
 
 const char* fp2_last_error(void) { return fp2::last_error(); }

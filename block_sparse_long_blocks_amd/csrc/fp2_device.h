@@ -7,6 +7,23 @@
 
 namespace fp2 {
 
+// Bounds-checking builds (FP2_DEBUG_BOUNDS): each call that reads page ids or
+// a CSR first runs a check kernel that sets bits of an error word (1: a page
+// id outside [0, num_pages); 2: a CSR entry outside its row's blocks or out of
+// order; 4: CSR row pointers out of order or past the causal count), and every
+// kernel that reads them returns at once while the word is set, so that a bad
+// input is reported instead of read past.  Release builds pass a null word and
+// the guard compiles to nothing.
+#ifdef FP2_DEBUG_BOUNDS
+#define FP2_BOUNDS_GUARD(word) \
+  do {                                                                                    \
+    if ((word) != nullptr && *reinterpret_cast<const volatile uint32_t*>(word) != 0u) return; \
+  } while (0)
+#else
+#define FP2_BOUNDS_GUARD(word) ((void)(word))
+#endif
+
+
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;

@@ -7,6 +7,8 @@
 #include <cstdint>
 #include <string>
 
+#include <hip/hip_runtime_api.h>
+
 #include "fp2.h"
 
 namespace fp2 {
@@ -83,5 +85,15 @@ constexpr size_t kPlanScratchBytes = FP2_PLAN_NOALLOC_MAX_BYTES;
 constexpr int64_t kPartFloatsPerWave = 64 * 64 + 2 * 64;
 constexpr int kInfoInts = 48;  // a work item's record: see item_info_kernel
 inline int plan_words(const BatchInfo& info) { return int((info.max_kblocks + 31) / 32); }
+
+// Bounds-checking builds (FP2_DEBUG_BOUNDS, see fp2_device.h; csrc/debug_bounds.hip):
+// the device address of the error word on the current device (nullptr in
+// release builds), the check kernels (no-ops in release builds), and the
+// word's read-and-clear (FP2_ERR_UNSUPPORTED in release builds).
+const uint32_t* bounds_word();
+hipError_t launch_check_pages(const fp2_batch* b, const fp2_kv* kv, hipStream_t stream);
+hipError_t launch_check_csr(const fp2_batch* b, const BatchInfo& info, int num_kv_heads, const int32_t* row_ptr,
+                            const int32_t* col_idx, hipStream_t stream);
+fp2_status read_bounds_word(uint32_t* word);
 
 }  // namespace fp2

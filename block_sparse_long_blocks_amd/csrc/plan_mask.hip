@@ -374,6 +374,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(StatsArgs sa, PlanArgs a
   __shared__ float red_v[kThreads][N + 1];
   __shared__ float s_qbar[128];
   __shared__ int s_pg[kPoolMaxPages];
+  FP2_BOUNDS_GUARD(sa.dbg);
   const int b = blockIdx.x;
   if (b < sa.total_kblocks) {
     kv_block_stats<ESZ>(sa, b, red_k, red_v, s_pg);

@@ -47,6 +47,7 @@ struct Chunk<1> {
 };
 
 struct StatsArgs {
+  const uint32_t* dbg;  // bounds-checking builds: the error word (see fp2_device.h), else nullptr
   const int32_t* cu_kblocks;
   const int32_t* seqlens_k;
   const int32_t* page_table;
@@ -189,6 +190,7 @@ __device__ __forceinline__ void kv_block_stats(const StatsArgs& a, int kb, float
 
 inline StatsArgs stats_args(const fp2_batch* b, const fp2_kv* kv, const BatchInfo& info, float* kbar, float* vbar) {
   StatsArgs a;
+  a.dbg = bounds_word();
   a.cu_kblocks = b->cu_kblocks;
   a.seqlens_k = b->seqlens_k;
   a.cu_seqlens_q = b->cu_seqlens_q;

@@ -360,6 +360,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t Kl[TL::KLDS];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * TL::VS];
   __shared__ uint32_t kept[kMaxKBlocks / 32];
+  FP2_BOUNDS_GUARD(a.dbg);
 
   // ---- tile decode: 8 consecutive CSR ranks form a group; the slices of one
   // rank land on one XCD (blockIdx % 8); latest query blocks (most causal
@@ -588,6 +589,7 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
     if (e != hipSuccess) return e;
   }
   AttnArgs a;
+  a.dbg = bounds_word();
   a.cu_seqlens_q = b->cu_seqlens_q;
   a.seqlens_k = b->seqlens_k;
   a.cu_qblocks = b->cu_qblocks;

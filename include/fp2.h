@@ -44,7 +44,8 @@
  *    (fp2_last_error() gives a message, per calling thread).
  *  - Page ids and device-side descriptor arrays are trusted: out-of-range
  *    page ids, or device arrays that disagree with their host mirrors, are
- *    undefined behaviour.
+ *    undefined behaviour (a FP2_DEBUG_BOUNDS build checks page ids and the
+ *    CSR on the device: fp2_debug_bounds_word()).
  *  - Layouts are row-major (C order).  "bf16" is bfloat16; "e4m3" is OCP
  *    FP8 E4M3 (bias 7, max 448, no infinities).
  */
@@ -269,6 +270,24 @@ fp2_status fp2_prefill_run(const fp2_batch *batch, const fp2_q *q, const fp2_kv 
                            int32_t mean_correction, float softmax_scale,
                            fp2_out_dtype out_dtype, void *out, int32_t max_chunk_tiles,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Debug aid for the device data the host checks cannot see (page ids, the
+ * CSR handed to fp2_prefill_run).  A library built with FP2_DEBUG_BOUNDS
+ * (block_sparse_long_blocks_amd/build.py --debug-bounds) runs a check kernel
+ * ahead of every call that reads them and keeps a device error word: bit 1, a
+ * page id a sequence uses lies outside [0, num_pages) (fp2_block_stats,
+ * fp2_block_stats_cached, fp2_gather_block_stats, fp2_stage1,
+ * fp2_prefill_run); bit 2, a CSR row is not strictly ascending from block 0
+ * through the row's last diagonal block; bit 4, the row pointers are out of
+ * order or past the causal pair count (fp2_prefill_run).  While the word is
+ * set, the kernels that read those data return at once, so later outputs of
+ * that device are left unwritten instead of being read past buffers.
+ *   word  host out: the error word (0 if every checked call was clean); the
+ *         device word is cleared.
+ * Reads the current device's word with a synchronous copy (it waits for the
+ * device).  FP2_ERR_UNSUPPORTED from a release build, which trusts these data
+ * (see the top of this file). */
+fp2_status fp2_debug_bounds_word(uint32_t *word);
 
 /* Message for the last non-OK status returned on the calling thread. */
 const char *fp2_last_error(void);

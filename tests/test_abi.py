@@ -256,6 +256,23 @@ def test_validation_rejects_before_launch():
     _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_plan_mask, b, _q(256, hq=64), 2, f32, 1.0, i32, i32, i32, ws)
 
 
+def test_release_build_has_no_bounds_word():
+    """Without FP2_DEBUG_BOUNDS the library trusts page ids and the CSR, and says so instead of
+    reporting a word it does not keep (no HIP call is made)."""
+    _expect(lib.FP2_ERR_UNSUPPORTED, lib.fp2_debug_bounds_word, match="FP2_DEBUG_BOUNDS")
+
+
+def test_bounds_build_is_built():
+    """build() also builds libfp2_bounds.so (FP2_DEBUG_BOUNDS) beside libfp2.so; it exports the same
+    functions."""
+    import ctypes
+    path = os.path.join(ROOT, "block_sparse_long_blocks_amd", "libfp2_bounds.so")
+    assert os.path.exists(path), "build it: python block_sparse_long_blocks_amd/build.py --debug-bounds"
+    so = ctypes.CDLL(path)
+    for n in declared_functions():
+        assert hasattr(so, n), n
+
+
 def test_no_fallback_without_library(tmp_path, monkeypatch):
     """The binding refuses to import when libfp2.so is absent (no CPU path)."""
     import importlib.util
@@ -282,8 +299,9 @@ def test_build_entry_builds_before_importing_the_package(tmp_path):
     (pkg / "build.py").write_text(
         "import os, shutil\n"
         f"SRC = {lib.library_path()!r}\n"
-        "def build(debug=False):\n"
-        "    dst = os.path.join(os.path.dirname(os.path.abspath(__file__)), 'libfp2.so')\n"
+        "def build(debug=False, bounds=False):\n"
+        "    name = 'libfp2_bounds.so' if bounds else 'libfp2.so'\n"
+        "    dst = os.path.join(os.path.dirname(os.path.abspath(__file__)), name)\n"
         "    shutil.copy(SRC, dst)\n"
         "    return dst\n")
     assert not (pkg / "libfp2.so").exists()
