@@ -666,6 +666,19 @@ def main():
         if "dense_ms_per_layer" in f8:
             out["fp8"]["dense_ms_per_layer"] = round(f8["dense_ms_per_layer"], 3)
             out["fp8"]["speedup_vs_dense"] = round(f8["speedup_vs_dense"], 2)
+    # context for the stage-1 HBM figures: a plain device copy of 1 GiB (read + write) on this machine
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    out["copy_hbm_gbs"] = round(2 * (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)
+    del src, dst
     if args.copy_calibration:
         # an elementwise kernel that reads and writes exactly 1 GiB each
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
