@@ -37,9 +37,10 @@
 //    MFMA is a slot closed by a scheduling barrier, the QK^T MFMAs of step
 //    j+1 and the PV MFMAs of step j-1 share a region with the softmax of
 //    step j, operand reads run a few slots ahead and the softmax values are
-//    consumed a group or more after they are produced.  Masks are applied
-//    to the exponent; the reference max is refreshed only when a probability
-//    would reach 2^64.  The younger wave of each SIMD takes the higher issue
+//    consumed a group or more after they are produced.  Diagonal masks are
+//    applied to the exponent; bf16 mean-token tiles take their weight and
+//    mask from one more MFMA per step on the plain schedule; the reference
+//    max is refreshed only when a probability would reach 2^64.  The younger wave of each SIMD takes the higher issue
 //    priority for the first half of a tile (the arbiter otherwise serves the
 //    older one first).
 //  * 64-token KV blocks: a tile holds two kept blocks (CSR entries 2i and
@@ -581,16 +582,41 @@ struct Wave {
   // diagonal tq is the query's position minus the first block's first key,
   // tq2 the same for the second block (very negative when the tile holds one
   // block).
-  template <bool MASKED, bool QK8, bool TWO = false, class Dma>
+  //
+  // AUG (plain schedule, bf16 mean-token tiles): the tokens' weight and mask
+  // enter the scores through one more MFMA per step, at the head of the
+  // step's QK chain, instead of a bit test and a select per score.  Its A
+  // holds for key l of the step (lane l < 32, k = 0 and 1) cbs split into two
+  // bf16 halves when the token's block is skipped, -inf and 0 when it is not;
+  // its B holds ones at k = 0 and 1 of every column; every other A element
+  // is finite and meets a zero of B.  So the product adds cbs, or -inf, to
+  // each score of the key's row, and the rest of the tile is the plain one.
+  template <bool MASKED, bool QK8, bool TWO = false, bool AUG = false, class Dma>
   __device__ __forceinline__ void tile(bf16x8 (&fr)[kRing], bool first, const uint8_t* Kt, const uint8_t* Vt,
                                        int off0, int off1, const int (&off8)[4], float scl, float scl2, Dma&& dma,
                                        int mode,
                                        int tq, int tq2, int hf, float lb, float cbs, int J0, int diag,
                                        const uint32_t* kept) {
+    static_assert(!(MASKED && AUG), "the weight MFMA is the plain schedule's mask");
     bf16x8 pp[2] = {qf[0], qf[0]}, pc[2];
     f32x16 s = f32x16{}, sn = f32x16{};
     Soft st;
     uint32_t M[NS] = {};
+    uint32_t abit = 0u, hl = 0u;  // AUG: bit j = key l%32 of step j is a skipped block's token
+    auto weight = [&](int j) {
+      const uint32_t ka = (abit >> j) & 1u ? hl : (hf ? 0u : 0xff80u);  // bf16 -inf at k = 0 (lanes < 32)
+      const bf16x8 wa = __builtin_bit_cast(bf16x8, make_uint4(ka, 0u, 0u, 0u));
+      const bf16x8 wb = __builtin_bit_cast(bf16x8, make_uint4(hf ? 0u : kOnesBf16x2, 0u, 0u, 0u));
+      return mfma_bf16_32x32x16(wa, wb, f32x16{});
+    };
+    if constexpr (AUG) {
+      const uint32_t hi = pack_bf16x2(cbs, 0.f) & 0xffffu;
+      hl = pack_bf16x2(cbs, cbs - bf16lo(hi));  // cbs ~ bf16 hi + bf16 lo
+      const int l = __lane_id() & 31;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) abit |= ((kept[(J0 >> 5) + j] >> l) & 1u) << j;  // skipped-block words
+      sn = weight(0);
+    }
     if constexpr (MASKED) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
@@ -614,6 +640,9 @@ struct Wave {
     for (int j = 0; j < NS; ++j) {
       s = sn;
       sn = f32x16{};
+      if constexpr (AUG) {
+        if (j + 1 < NS) sn = weight(j + 1);
+      }
       st.mx = -INFINITY;
       // region j+1: QK(j+1) (j < 3), PV(j-1) (j > 0), softmax(j)
       if (j == 0) region<1, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[0], dma);
@@ -637,6 +666,9 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* dst) {
 
 // PAIR: 64-token KV blocks under 128-token query blocks, two blocks (two CSR
 // entries) to a 128-key tile.
+// tile code paths of the attention kernel's loops
+enum : int { kPathPlain = 0, kPathMasked = 1, kPathMean = 2 };
+
 template <bool FP8, bool PAIR>
 __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   constexpr int KB = PAIR ? 64 : kBlk;  // tokens of a KV block
@@ -1005,10 +1037,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   const float scl = a.scale_log2 * qs;  // logit scale of mean tiles (and of every bf16 tile)
+  // bf16: mean tiles take the plain schedule with the weight MFMA (see
+  // Wave::tile); e4m3 keeps them on the masked one (its plain tiles are e4m3)
+  constexpr bool kMeanPlain = !FP8;
 
-  // MASKED_C: std::integral_constant<bool, ...>, the tile code path (see below)
-  auto iter = [&](auto masked_c, int idx, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
-    constexpr bool MASKED = decltype(masked_c)::value;
+  // PATH_C: std::integral_constant<int, ...>, the tile code path (see below)
+  auto iter = [&](auto path_c, int idx, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn)
+                  __attribute__((always_inline)) {
+    constexpr int PATH = decltype(path_c)::value;
+    constexpr bool MASKED = PATH != kPathPlain;  // bf16 tiles (e4m3 inputs: the codes widened)
     // the tile's first operand reads go out before the bookkeeping below
     bf16x8 fr[Wave::kRing];
     if (wave_active) ws.first_reads<FP8 && !MASKED>(fr, Kc, Vc, off0, off1, off8);
@@ -1067,9 +1104,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, Vn);
       }
-    } else if constexpr (!MASKED) {
+    } else if constexpr (PATH == kPathPlain) {
       ws.tile<false, FP8, PAIR>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, 0, tq, 0, hf, 0.f, 0.f, 0,
                                 dlo, kept);
+    } else if constexpr (PATH == kPathMean) {
+      // bf16 mean tiles: the plain schedule with the weight MFMA (cbs: log2 B in score units)
+      ws.tile<false, false, PAIR, true>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, 2, tq, 0, hf, 0.f,
+                                        a.log2_block / sclt, j0, dlo, kept);
     } else {
       // mean tiles: weight of a KV block, its log2 in the exponent (cbs in score units)
       const float lbm = mode == 2 ? a.log2_block : 0.f;
@@ -1096,9 +1137,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   // exact tiles off the diagonal, which the ascending CSR puts ahead of the
   // diagonal block (e4m3: on the e4m3 MFMA), then the diagonal and the mean
   // tiles on the masked bf16 path (e4m3: the diagonal block's codes widened
-  // to bf16).
-  const std::integral_constant<bool, false> plain_c;
-  const std::integral_constant<bool, true> masked_c;
+  // to bf16); bf16 mean tiles branch from there to the plain schedule with
+  // the weight MFMA.
+  const std::integral_constant<int, kPathPlain> plain_c;
+  const std::integral_constant<int, kPathMasked> masked_c;
+  const std::integral_constant<int, kPathMean> mean_c;
   int idx = 0;
   while (idx < nexact && !masked_exact(j0, idx)) {
     iter(plain_c, idx, K0, V0, K1, V1);
@@ -1107,14 +1150,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     iter(plain_c, idx, K1, V1, K0, V0);
     ++idx;
   }
-  if (idx < ntiles && (idx & 1)) {
-    iter(masked_c, idx, K1, V1, K0, V0);
-    ++idx;
-  }
-  for (; idx < ntiles; idx += 2) {
-    iter(masked_c, idx, K0, V0, K1, V1);
-    if (idx + 1 < ntiles) iter(masked_c, idx + 1, K1, V1, K0, V0);
-  }
+  // (tile idx sits in buffers idx % 2)
+  auto run = [&](auto path_c, int end) __attribute__((always_inline)) {
+    if (idx < end && (idx & 1)) {
+      iter(path_c, idx, K1, V1, K0, V0);
+      ++idx;
+    }
+    while (idx < end) {
+      iter(path_c, idx, K0, V0, K1, V1);
+      ++idx;
+      if (idx >= end) break;
+      iter(path_c, idx, K1, V1, K0, V0);
+      ++idx;
+    }
+  };
+  run(masked_c, kMeanPlain ? nexact : ntiles);
+  if constexpr (kMeanPlain) run(mean_c, ntiles);
 
   // ---- epilogue: O / l, or the chunk's partial result in register layout
   if (pslot >= 0) {
