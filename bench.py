@@ -196,6 +196,9 @@ def run_workload(name, tau, args, torch, lib, synth, corr=True, stats_cache=Fals
     # fused stage 1: K, V and Q read once, kbar / vbar / qbar written (the selection pass reads L2-resident means)
     qbar_bytes = w.cfg.hkv * w.total_qblocks * w.cfg.d * 4
     res["stage1_fused_gbs"] = (kv_bytes + w.q.nbytes + kbar_bytes + qbar_bytes) / (fused_s1 * 1e-3) / 1e9
+    # device memory of fp2_prefill_run's workspace against the paged K and V it serves
+    res["run_workspace_mb"] = L.run_ws.numel() / 1e6
+    res["kv_cache_mb"] = kv_bytes / 1e6
     del L, batch, q, kv
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -521,7 +524,7 @@ def tile_study(args, torch, lib, synth):
         dense = L.out
         diff = (sparse - dense).abs()
         fl = flop_counts(w, nnz)
-        if dt == "fp8":  # QK^T of plain tiles on e4m3 MFMA, PV and the masked tiles on bf16 MFMA
+        if dt == "fp8":  # QK^T of exact tiles on e4m3 MFMA, PV and the mean tiles on bf16 MFMA
             busy = fl["kept"] / 2 / (PEAK_TFLOPS["fp8"] * 1e12) + (fl["kept"] / 2 + fl["corr"]) / (PEAK_TFLOPS["bf16"] * 1e12)
         else:
             busy = (fl["kept"] + fl["corr"]) / (PEAK_TFLOPS["bf16"] * 1e12)
@@ -662,7 +665,8 @@ def main():
                       "stages_ms": {k: round(v, 4) for k, v in f8["stages_ms"].items()},
                       "stage1_ms": {k: round(v, 4) for k, v in f8["stage1_ms"].items()},
                       "tau": f8["tau"], "density": round(f8["density"], 5),
-                      "mfma_frac_attn": round(busy / t8, 4)}
+                      "mfma_frac_attn": round(busy / t8, 4),
+                      "run_workspace_mb": round(f8["run_workspace_mb"], 1), "kv_cache_mb": round(f8["kv_cache_mb"], 1)}
         if "dense_ms_per_layer" in f8:
             out["fp8"]["dense_ms_per_layer"] = round(f8["dense_ms_per_layer"], 3)
             out["fp8"]["speedup_vs_dense"] = round(f8["speedup_vs_dense"], 2)

@@ -30,7 +30,6 @@ struct AttnArgs {
   const uint16_t* vbar16;  // fp16 [Hkv, total_kblocks, D] (register-staged kernel)
   const uint8_t* vt;       // V^T tiles of every KV block (bf16 d128 kernel)
   const uint8_t* vbt;      // vbar^T tiles of the mean tokens (bf16 d128 kernel)
-  const uint8_t* kd;       // e4m3 d128 kernel: K codes as bf16 rows of the diagonal-capable blocks
   int4* items;             // d128 kernel: work items {rank, first tile, end tile, partial slot or -1},
                            // heaviest first, [rows + extra_cap]
   int4* splits;            // d128 kernel: split rows {rank, first slot, chunks, 0}, [extra_cap]
@@ -56,8 +55,7 @@ struct AttnArgs {
 
 
 // Transposes V (and vbar, and rounds kbar) into the workspace parts that
-// a.vt, a.vbt and a.kbar16 point to (e4m3: V dequantized, and the K codes of
-// the blocks that can be diagonal widened to bf16 rows at a.kd), builds the
+// a.vt, a.vbt and a.kbar16 point to (e4m3: V dequantized), builds the
 // work items (the exact tiles of heavy rows split into chunks, heaviest item
 // first), runs the d=128 B=128 kernel and merges the chunks of split rows.
 hipError_t launch_attn_d128(const AttnArgs& a, bool fp8, const float* kbar, const float* vbar, int max_kblocks,

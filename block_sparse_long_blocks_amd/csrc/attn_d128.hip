@@ -16,8 +16,7 @@
 //  * V is first transposed into V^T tiles (one 128 d x 128 key tile per KV
 //    block and head, keys in the order the PV MFMA consumes them; e4m3 V
 //    dequantized), and the vbar of the mean tokens likewise; kbar is rounded
-//    to bf16 rows; e4m3 K codes of the blocks that can be diagonal are
-//    widened to bf16 rows.
+//    to bf16 rows.  e4m3 K tiles stay e4m3 codes, read from the pages.
 //  * Tiles stream global -> LDS by DMA (global_load_lds, 16 bytes a lane)
 //    into two LDS buffers: the next tile's DMA runs while the current tile is
 //    computed; one barrier per tile.  No staging registers; the waves write
@@ -38,19 +37,18 @@
 //    j+1 and the PV MFMAs of step j-1 share a region with the softmax of
 //    step j, operand reads run a few slots ahead and the softmax values are
 //    consumed a group or more after they are produced.  Diagonal masks are
-//    applied to the exponent; bf16 mean-token tiles take their weight and
-//    mask from one more MFMA per step on the plain schedule; the reference
-//    max is refreshed only when a probability would reach 2^64.  The younger wave of each SIMD takes the higher issue
-//    priority for the first half of a tile (the arbiter otherwise serves the
-//    older one first).
+//    applied to the exponent; mean-token tiles take their weight and mask
+//    from one more MFMA per step on the plain schedule; the reference max is
+//    refreshed only when a probability would reach 2^64.  The younger wave
+//    of each SIMD takes the higher issue priority for the first half of a
+//    tile (the arbiter otherwise serves the older one first).
 //  * 64-token KV blocks: a tile holds two kept blocks (CSR entries 2i and
 //    2i+1 of the row), waves 0-1 moving the first block's K rows and 2-3 the
 //    second's; V^T is kept as half tiles (128 d x 64 keys) and each lane
 //    takes its 16-byte chunk from the half its key positions belong to.  A
 //    row's last entry may be alone (second half masked); the diagonal mask
 //    is by position and the logit scale (e4m3: the block's K scale) per
-//    half; e4m3 K codes of every block are widened to bf16 rows, since a
-//    masked tile can hold any kept block beside a diagonal one.
+//    half.
 //  * The workgroups run work items built on the device (items_kernel):
 //    heaviest first, with the exact tiles of rows much heavier than the rest
 //    cut into chunks whose float32 partials combine_kernel merges.
@@ -114,7 +112,6 @@ struct PrepArgs {
   uint16_t* kbar16;  // bf16 [Hkv, total_kblocks, D]
   uint8_t* vt;       // V^T tiles [Hkv, total_kblocks]
   uint8_t* vbt;      // vbar^T tiles [Hkv, mt_cap]
-  uint8_t* kd;       // e4m3: K codes as bf16 rows [Hkv, total_kblocks, B, D]
   PageMap pm;
   int num_seqs, hkv, max_pages, page_size, total_kblocks, mt_cap;
 };
@@ -178,40 +175,6 @@ __global__ __launch_bounds__(256) void vt_exact_kernel(PrepArgs a) {
   uint8_t* dst = a.vt + ((int64_t)g * a.total_kblocks + kb) * (KB * kRowBytes) + c * 16;
 #pragma unroll
   for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dst + (8 * dc + e) * (2 * KB)) = out[e];
-}
-
-// e4m3 K codes of every block that is some query block's diagonal (the
-// blocks from the sequence's cached prefix length / B on), widened to bf16
-// rows (exact; the scale stays apart), zero past the sequence end.  HALF
-// (64-token KV blocks): every block, since a masked pair tile can hold any
-// kept block beside a diagonal one.
-template <bool HALF>
-__global__ __launch_bounds__(256) void kd_kernel(PrepArgs a) {
-  FP2_BOUNDS_GUARD(a.dbg);
-  constexpr int KB = HALF ? 64 : kBlk;
-  const int kb = blockIdx.x, g = blockIdx.y;
-  const int s = find_seq(a.cu_kblocks, a.num_seqs, kb);
-  const int J = kb - a.cu_kblocks[s];
-  const int T = a.seqlens_k[s];
-  const int P = T - (a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s]);
-  if (!HALF && J < P / kBlk) return;
-  const int32_t* pt = a.page_table + (int64_t)s * a.max_pages;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < KB / 16; ++u) {
-    const int id = t + 256 * u;
-    const int r = id >> 4, ch = id & 15;  // row, 8-wide d chunk
-    const int pos = J * KB + r;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (pos < T) {
-      const uint2 c8 = *reinterpret_cast<const uint2*>(
-          a.k_pages + (((int64_t)pt[J] * KB + r) * a.hkv + g) * kD + ch * 8);  // one page per block
-      const f32x4 lo = e4m3x4_to_f32(c8.x), hi = e4m3x4_to_f32(c8.y);
-      v = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
-                     pack_bf16x2(hi[2], hi[3]));
-    }
-    *reinterpret_cast<uint4*>(a.kd + (((int64_t)g * a.total_kblocks + kb) * KB + r) * kRowBytes + ch * 16) = v;
-  }
 }
 
 // Mean tokens: tile mt of sequence s holds mean tokens [128 mt, 128 mt + 128)
@@ -291,7 +254,7 @@ constexpr float kXmax = 64.0f;
 // elements 0 and 1).
 struct Wave {
   static constexpr int NS = kBlk / 32;  // 32-key steps per tile
-  bf16x8 qf[kD / 16];  // bf16 query fragments (e4m3 inputs: the codes widened, for bf16 K tiles)
+  bf16x8 qf[kD / 16];  // bf16 query fragments (e4m3 inputs: the codes widened, for the bf16 kbar rows)
   i32x8 qf8[kD / 64];  // e4m3 query fragments (e4m3 inputs)
   f32x16 o[kD / 32];
   f32x4 lsum;    // lanes 0-15: the row sums of queries l and l+16 (see above)
@@ -466,13 +429,12 @@ struct Wave {
     uint32_t w[8];
   };
   // Masked tiles pass the per-lane bit mask M of the step's allowed keys
-  // (bit 8(i/4) + i%4 for element i) and nbm = nb + log2(B) on mean tiles:
-  // a masked element's exponent is -inf.
+  // (bit 8(i/4) + i%4 for element i): a masked element's exponent is -inf.
   template <bool MASKED>
-  __device__ __forceinline__ void soft_group(int g, Soft& st, const f32x16& s, float scl, float nbm,
+  __device__ __forceinline__ void soft_group(int g, Soft& st, const f32x16& s, float scl, float nb,
                                              uint32_t M) const {
     if (g < 16) {
-      float x = __builtin_fmaf(s[g], scl, nbm);
+      float x = __builtin_fmaf(s[g], scl, nb);
       if constexpr (MASKED) {
         const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)M, 8 * (g >> 2) + (g & 3), 1);
         x = __uint_as_float((sel & __float_as_uint(x)) | (~sel & 0xff800000u));
@@ -500,7 +462,7 @@ struct Wave {
   template <int R, bool SOFT, bool MASKED, bool QK8, class Dma>
   __device__ __forceinline__ void region(bf16x8 (&fr)[kRing], f32x16& sn, const bf16x8 (&pp)[2], Soft& st,
                                          const f32x16& s, const uint8_t* Kt, const uint8_t* Vt, int off0, int off1,
-                                         const int (&off8)[4], float scl, float nbm, uint32_t M, Dma& dma) {
+                                         const int (&off8)[4], float scl, float nb, uint32_t M, Dma& dma) {
     constexpr int N0 = region_start<QK8>(R), S = region_start<QK8>(R + 1) - N0;
     constexpr int kDma0 = QK8 ? 4 : 8;
     // the younger wave's issue priority ends half way (see the tile loop)
@@ -533,7 +495,7 @@ struct Wave {
       if (n >= kDma0 && n < kDma0 + 16) dma(n - kDma0);
       if constexpr (SOFT) {
 #pragma unroll
-        for (int g = t * kGroups / S; g < (t + 1) * kGroups / S; ++g) soft_group<MASKED>(g, st, s, scl, nbm, M);
+        for (int g = t * kGroups / S; g < (t + 1) * kGroups / S; ++g) soft_group<MASKED>(g, st, s, scl, nb, M);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -543,14 +505,14 @@ struct Wave {
   // the step reached 2^kXmax (or it is the first step of the row)
   template <bool MASKED>
   __device__ __forceinline__ void soft_close(Soft& st, const f32x16& s, float scl, bool force, bf16x8 (&pc)[2],
-                                             uint32_t M, float cbs) {
+                                             uint32_t M) {
     pc[0] = __builtin_bit_cast(bf16x8, make_uint4(st.w[0], st.w[1], st.w[2], st.w[3]));
     pc[1] = __builtin_bit_cast(bf16x8, make_uint4(st.w[4], st.w[5], st.w[6], st.w[7]));
     if (__any(!(st.mx < kXmax)) || force) {
       if constexpr (MASKED) {
-        f32x16 sm;  // the scores as the stream saw them: + cbs where allowed, -inf elsewhere
+        f32x16 sm;  // the scores as the stream saw them: -inf where masked
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm[i] = (M >> (8 * (i >> 2) + (i & 3))) & 1u ? s[i] + cbs : -INFINITY;
+        for (int i = 0; i < 16; ++i) sm[i] = (M >> (8 * (i >> 2) + (i & 3))) & 1u ? s[i] : -INFINITY;
         refresh(sm, scl, pc);
       } else {
         refresh(s, scl, pc);
@@ -560,11 +522,8 @@ struct Wave {
   }
 
   // One tile; scl is its logit scale (log2 units, input scales folded in).
-  // MASKED: mode 1 diagonal block (key > query masked), mode 2 mean-token
-  // tile starting at mean token J0 (only skipped blocks' tokens count, each
-  // with weight B: lb = log2 B added to the exponent, cbs = lb / scl in
-  // score units); mode 0 passes whole.  QK8: e4m3 K tile and QK on the
-  // 32x32x64 e4m3 MFMA.
+  // MASKED: mode 1 diagonal block (key > query masked), mode 0 passes
+  // whole.  QK8: e4m3 K tile and QK on the 32x32x64 e4m3 MFMA.
   // The operand reads of the first kLA ops, issued by the caller as early as
   // it can (see first_reads).
   template <bool QK8>
@@ -583,20 +542,20 @@ struct Wave {
   // tq2 the same for the second block (very negative when the tile holds one
   // block).
   //
-  // AUG (plain schedule, bf16 mean-token tiles): the tokens' weight and mask
-  // enter the scores through one more MFMA per step, at the head of the
-  // step's QK chain, instead of a bit test and a select per score.  Its A
-  // holds for key l of the step (lane l < 32, k = 0 and 1) cbs split into two
-  // bf16 halves when the token's block is skipped, -inf and 0 when it is not;
-  // its B holds ones at k = 0 and 1 of every column; every other A element
-  // is finite and meets a zero of B.  So the product adds cbs, or -inf, to
-  // each score of the key's row, and the rest of the tile is the plain one.
+  // AUG (plain schedule, mean-token tile starting at mean token J0): only
+  // the tokens of skipped blocks count, each with weight B, i.e. cbs =
+  // log2(B) / scl more score.  Weight and mask enter the scores through one
+  // more MFMA per step, at the head of the step's QK chain, instead of a bit
+  // test and a select per score.  Its A holds for key l of the step (lane
+  // l < 32, k = 0 and 1) cbs split into two bf16 halves when the token's
+  // block is skipped, -inf and 0 when it is not; its B holds ones at k = 0
+  // and 1 of every column; every other A element is finite and meets a zero
+  // of B.  So the product adds cbs, or -inf, to each score of the key's row,
+  // and the rest of the tile is the plain one.
   template <bool MASKED, bool QK8, bool TWO = false, bool AUG = false, class Dma>
   __device__ __forceinline__ void tile(bf16x8 (&fr)[kRing], bool first, const uint8_t* Kt, const uint8_t* Vt,
                                        int off0, int off1, const int (&off8)[4], float scl, float scl2, Dma&& dma,
-                                       int mode,
-                                       int tq, int tq2, int hf, float lb, float cbs, int J0, int diag,
-                                       const uint32_t* kept) {
+                                       int mode, int tq, int tq2, int hf, float cbs, int J0, const uint32_t* kept) {
     static_assert(!(MASKED && AUG), "the weight MFMA is the plain schedule's mask");
     bf16x8 pp[2] = {qf[0], qf[0]}, pc[2];
     f32x16 s = f32x16{}, sn = f32x16{};
@@ -622,17 +581,12 @@ struct Wave {
       for (int j = 0; j < NS; ++j) {
         if (mode == 0) {
           M[j] = ~0u;
-        } else if (mode == 1) {
+        } else {
           // element i allowed iff 8(i/4) + i%4 <= lim
           const int lim = (TWO ? (j < NS / 2 ? tq : tq2) - 32 * (j % (NS / 2)) : tq - 32 * j) - 4 * hf;
           M[j] = lim >= 31 ? ~0u : lim < 0 ? 0u : (2u << lim) - 1u;
-        } else {
-          M[j] = kept[(J0 >> 5) + j] >> (4 * hf);  // skipped-block bits of the mean tokens
         }
       }
-    } else {
-      lb = 0.f;
-      cbs = 0.f;
     }
     __builtin_amdgcn_sched_barrier(0);
     region<0, false, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, 0.f, 0u, dma);  // QK(0)
@@ -645,11 +599,11 @@ struct Wave {
       }
       st.mx = -INFINITY;
       // region j+1: QK(j+1) (j < 3), PV(j-1) (j > 0), softmax(j)
-      if (j == 0) region<1, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[0], dma);
-      if (j == 1) region<2, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb + lb, M[1], dma);
-      if (j == 2) region<3, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, TWO ? scl2 : scl, nb + lb, M[2], dma);
-      if (j == 3) region<4, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, TWO ? scl2 : scl, nb + lb, M[3], dma);
-      soft_close<MASKED>(st, s, (TWO && j >= NS / 2) ? scl2 : scl, first && j == 0, pc, M[j], cbs);
+      if (j == 0) region<1, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb, M[0], dma);
+      if (j == 1) region<2, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb, M[1], dma);
+      if (j == 2) region<3, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, TWO ? scl2 : scl, nb, M[2], dma);
+      if (j == 3) region<4, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, TWO ? scl2 : scl, nb, M[3], dma);
+      soft_close<MASKED>(st, s, (TWO && j >= NS / 2) ? scl2 : scl, first && j == 0, pc, M[j]);
       pp[0] = pc[0];
       pp[1] = pc[1];
     }
@@ -779,7 +733,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     }
   } else {
     // e4m3 codes: 32 bytes at d = 64 kk + 32 (l/32) for the 32x32x64 MFMA, and
-    // the 8 at d = 16 kk + 8 (l/32) widened to bf16 (exactly) for bf16 K tiles
+    // the 8 at d = 16 kk + 8 (l/32) widened to bf16 (exactly) for the bf16
+    // kbar rows of mean tiles
     const uint8_t* qrow = a.q + ((int64_t)(q0 + I * kBlk + tq) * a.hq + h) * kD;
 #pragma unroll
     for (int kk = 0; kk < kD / 64; ++kk) {
@@ -884,16 +839,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
       }
       const int r0 = dma_row0(j);
       pl.fast = pages16 && r0 + kDmaRows - 1 < T;
-      if (FP8 && masked_exact(j, idx)) {
-        // the diagonal block's K codes widened to bf16 rows (zero past the end)
-        pl.fast = true;
-        const int64_t kdr = PAIR ? (mrow0 + half_of(j, wave >= kDmaWaves / 2)) * KB + r0 % KB
-                                 : (mrow0 + j) * kBlk + kDmaRows * wave;
-#pragma unroll
-        for (int hh = 0; hh < kDmaHalves; ++hh) pl.kb[hh] = a.kd + (kdr + 16 * hh) * kRowBytes;
-        pl.kstep = 1024;
-        pl.kvo = voff;
-      } else if (FP8) {
+      if (FP8) {
         // e4m3 K rows (one page per block): kDmaRows/8 instructions of 8 rows
         pl.kd = Kd + kDmaRows * wave * kD;
         pl.kds = 1024;
@@ -1037,18 +983,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   const float scl = a.scale_log2 * qs;  // logit scale of mean tiles (and of every bf16 tile)
-  // bf16: mean tiles take the plain schedule with the weight MFMA (see
-  // Wave::tile); e4m3 keeps them on the masked one (its plain tiles are e4m3)
-  constexpr bool kMeanPlain = !FP8;
 
   // PATH_C: std::integral_constant<int, ...>, the tile code path (see below)
   auto iter = [&](auto path_c, int idx, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn)
                   __attribute__((always_inline)) {
     constexpr int PATH = decltype(path_c)::value;
-    constexpr bool MASKED = PATH != kPathPlain;  // bf16 tiles (e4m3 inputs: the codes widened)
+    constexpr bool QK8 = FP8 && PATH != kPathMean;  // e4m3 K tile (mean tiles: bf16 kbar rows)
     // the tile's first operand reads go out before the bookkeeping below
     bf16x8 fr[Wave::kRing];
-    if (wave_active) ws.first_reads<FP8 && !MASKED>(fr, Kc, Vc, off0, off1, off8);
+    if (wave_active) ws.first_reads<QK8>(fr, Kc, Vc, off0, off1, off8);
     __builtin_amdgcn_sched_barrier(0);
     int j2;
     if constexpr (PAIR) j2 = idx + 2 < nexact ? pack(after_barrier(j2v), after_barrier(j2vb), idx + 2) : mean_of(idx + 2);
@@ -1105,26 +1048,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
         for (int i = 0; i < kDmaInstr; ++i) issue(pl, i, Vn);
       }
     } else if constexpr (PATH == kPathPlain) {
-      ws.tile<false, FP8, PAIR>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, 0, tq, 0, hf, 0.f, 0.f, 0,
-                                dlo, kept);
+      ws.tile<false, FP8, PAIR>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, 0, tq, 0, hf, 0.f, 0, kept);
     } else if constexpr (PATH == kPathMean) {
-      // bf16 mean tiles: the plain schedule with the weight MFMA (cbs: log2 B in score units)
-      ws.tile<false, false, PAIR, true>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, 2, tq, 0, hf, 0.f,
-                                        a.log2_block / sclt, j0, dlo, kept);
+      // mean tiles: the plain bf16 schedule with the weight MFMA (cbs: log2 B in score units)
+      ws.tile<false, false, PAIR, true>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, 2, tq, 0, hf,
+                                        a.log2_block / sclt, j0, kept);
+    } else if constexpr (PAIR) {
+      // diagonal offsets of the two blocks (a lone block: its second half masked)
+      const int qd = qpos0 + tq;
+      const int tqa = qd - half_of(j0, 0) * KB;
+      const int tqb = 2 * idx + 1 < ne ? qd - half_of(j0, 1) * KB : -(1 << 20);
+      ws.tile<true, FP8, true>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, mode, tqa, tqb, hf, 0.f, 0,
+                               kept);
     } else {
-      // mean tiles: weight of a KV block, its log2 in the exponent (cbs in score units)
-      const float lbm = mode == 2 ? a.log2_block : 0.f;
-      if constexpr (PAIR) {
-        // diagonal offsets of the two blocks (a lone block: its second half masked)
-        const int qd = qpos0 + tq;
-        const int tqa = qd - half_of(j0, 0) * KB;
-        const int tqb = 2 * idx + 1 < ne ? qd - half_of(j0, 1) * KB : -(1 << 20);
-        ws.tile<true, false, true>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, mode, tqa, tqb, hf, lbm,
-                                   lbm / sclt, j0, dlo, kept);
-      } else {
-        ws.tile<true, false>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt, dma, mode, tq, 0, hf, lbm, lbm / sclt,
-                             j0, dlo, kept);
-      }
+      ws.tile<true, FP8>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt, dma, mode, tq, 0, hf, 0.f, 0, kept);
     }
     __builtin_amdgcn_s_setprio(0);
     j0 = j1;
@@ -1132,12 +1069,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's DMA and loads for later tiles have landed
     __syncthreads();
   };
-  // Two loops, each with one tile code path (one instance of the tile code
+  // Three loops, each with one tile code path (one instance of the tile code
   // per loop keeps the register allocation of each loop separate): first the
   // exact tiles off the diagonal, which the ascending CSR puts ahead of the
-  // diagonal block (e4m3: on the e4m3 MFMA), then the diagonal and the mean
-  // tiles on the masked bf16 path (e4m3: the diagonal block's codes widened
-  // to bf16); bf16 mean tiles branch from there to the plain schedule with
+  // diagonal block, then the diagonal on the masked path (e4m3 inputs: both
+  // on the e4m3 MFMA), then the mean tiles on the plain bf16 schedule with
   // the weight MFMA.
   const std::integral_constant<int, kPathPlain> plain_c;
   const std::integral_constant<int, kPathMasked> masked_c;
@@ -1164,8 +1100,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
       ++idx;
     }
   };
-  run(masked_c, kMeanPlain ? nexact : ntiles);
-  if constexpr (kMeanPlain) run(mean_c, ntiles);
+  run(masked_c, nexact);
+  run(mean_c, ntiles);
 
   // ---- epilogue: O / l, or the chunk's partial result in register layout
   if (pslot >= 0) {
@@ -1624,7 +1560,6 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
   p.kbar16 = const_cast<uint16_t*>(a.kbar16);
   p.vt = const_cast<uint8_t*>(a.vt);
   p.vbt = const_cast<uint8_t*>(a.vbt);
-  p.kd = const_cast<uint8_t*>(a.kd);
   p.pm = a.pm;
   p.num_seqs = a.num_seqs;
   p.hkv = a.hkv;
@@ -1637,14 +1572,8 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
     const dim3 per_pair((unsigned)((a.total_kblocks + 1) / 2), (unsigned)a.hkv);
     if (fp8 && a.pair) {
       hipLaunchKernelGGL((vt_exact_kernel<true, true>), per_pair, dim3(256), 0, stream, p);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kd_kernel<true>, per_block, dim3(256), 0, stream, p);
     } else if (fp8) {
       hipLaunchKernelGGL((vt_exact_kernel<true, false>), per_block, dim3(256), 0, stream, p);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kd_kernel<false>, per_block, dim3(256), 0, stream, p);
     } else if (a.pair) {
       hipLaunchKernelGGL((vt_exact_kernel<false, true>), dim3((unsigned)((a.total_kblocks + 1) / 2), (unsigned)a.hkv),
                          dim3(256), 0, stream, p);

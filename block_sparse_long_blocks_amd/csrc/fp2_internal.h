@@ -58,7 +58,6 @@ struct RunLayout {
   size_t k16 = 0;      // bf16 kbar rows [Hkv, total_kblocks, d]
   size_t v16 = 0;      // fp16 vbar rows (register-staged path) or vbar^T tiles (V^T path)
   size_t vt = 0;       // V^T tiles of every KV block (V^T path; 64 keys a tile with 64-token blocks)
-  size_t kd = 0;       // e4m3 V^T path: K codes as bf16 rows, [Hkv, total_kblocks, B, d]
   size_t items = 0;    // V^T path: work items in launch order, int4 [rows + extra_cap]
   size_t splits = 0;   // V^T path: rows split into chunks, int4 [extra_cap]
   size_t rank_slot = 0;  // V^T path: per row {exact tiles, mean tiles, first partial slot, 0}, int4 [rows]

@@ -177,10 +177,6 @@ RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int n
     L.mt_cap = (int64_t)(tkb / 128 + (size_t)num_seqs + 1);
     L.vt = L.v16 + hkv * (size_t)L.mt_cap * mtile;
     L.total = L.vt + hkv * tkb * tile;
-    if (dtype == FP2_FP8_E4M3) {
-      L.kd = L.total;
-      L.total = L.kd + hkv * tkb * tile;
-    }
     // work items: one per CSR row plus the extra chunks of split rows (at
     // most one per 4 causal tiles, and kMaxExtraItems); a split row holds at
     // least two chunks, so the partial slots are at most twice the extras

@@ -607,7 +607,6 @@ hipError_t launch_prefill(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, 
   a.vbar16 = v16;
   a.vt = wsb + L.vt;
   a.vbt = wsb + L.v16;
-  a.kd = wsb + L.kd;
   a.items = reinterpret_cast<int4*>(wsb + L.items);
   a.splits = reinterpret_cast<int4*>(wsb + L.splits);
   a.rank_slot = reinterpret_cast<int4*>(wsb + L.rank_slot);

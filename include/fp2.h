@@ -228,9 +228,8 @@ fp2_status fp2_stage1(const fp2_batch *batch, const fp2_q *q, const fp2_kv *kv, 
  * dtype (0 if the batch is empty or malformed).  For d = 128 with B = 128
  * over KB = 128 or KB = 64 (bf16 or e4m3), it holds V^T tiles of every KV block
  * (one bf16 128 x KB tile per block and KV head, e4m3 V dequantized: about
- * the size of bf16 V), bf16 kbar rows and
- * vbar^T tiles of the mean tokens, for e4m3 also the K codes of every
- * block widened to bf16 rows (another tile per block and head), and the
+ * the size of bf16 V, i.e. of the e4m3 K and V together), bf16 kbar rows and
+ * vbar^T tiles of the mean tokens, and the
  * work items in launch order (one per CSR row plus up to 256 chunks of
  * rows split for balance, heaviest first) with the float32 partial results
  * of split rows (about 132 KB per chunk and 256 packed query rows, so it
