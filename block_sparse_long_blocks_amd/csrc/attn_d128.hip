@@ -52,6 +52,7 @@
 //  * The workgroups run work items built on the device (items_kernel):
 //    heaviest first, with the exact tiles of rows much heavier than the rest
 //    cut into chunks whose float32 partials combine_kernel merges.
+#include <mutex>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -1543,6 +1544,87 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
     }
 }
 
+// The V^T preparation does not depend on the work-item kernels, so it runs
+// on a second stream of the library's (one per device, created on first use,
+// default priority) while the caller's stream builds the work items; the two
+// meet before the attention kernel.  Each device's fork and join events are
+// shared by all calls, so one call's record / wait pairs are enqueued under a
+// host lock.
+struct SidePath {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SidePath g_side[kMaxDevices];
+
+// (g_side_mu held)
+hipError_t side_path(int dev, SidePath*& out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SidePath& sp = g_side[dev];
+  if (!sp.stream) {
+    SidePath n;
+    hipError_t e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.stream) (void)hipStreamDestroy(n.stream);
+      return e;
+    }
+    sp = n;
+  }
+  out = &sp;
+  return hipSuccess;
+}
+
+// V^T tiles of every KV block and head, and the mean tokens' vbar^T tiles
+// and bf16 kbar rows
+hipError_t launch_prep(const PrepArgs& p, const AttnArgs& a, bool fp8, int max_kblocks, hipStream_t stream) {
+  const dim3 per_block((unsigned)a.total_kblocks, (unsigned)a.hkv);
+  const dim3 per_pair((unsigned)((a.total_kblocks + 1) / 2), (unsigned)a.hkv);
+  if (fp8 && a.pair)
+    hipLaunchKernelGGL((vt_exact_kernel<true, true>), per_pair, dim3(256), 0, stream, p);
+  else if (fp8)
+    hipLaunchKernelGGL((vt_exact_kernel<true, false>), per_block, dim3(256), 0, stream, p);
+  else if (a.pair)
+    hipLaunchKernelGGL((vt_exact_kernel<false, true>), per_pair, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((vt_exact_kernel<false, false>), per_block, dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.correction) return e;
+  hipLaunchKernelGGL(vt_mean_kernel, dim3((unsigned)((max_kblocks + kBlk - 1) / kBlk), (unsigned)a.num_seqs,
+                                          (unsigned)a.hkv),
+                     dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+// mean-tile lists, tile counts, work items and their records
+hipError_t launch_items(const AttnArgs& a, bool fp8, int max_kblocks, hipStream_t stream) {
+  const int nbins = min(max_kblocks + (max_kblocks + kBlk - 1) / kBlk + 1, kItemsMaxBins);
+  if (a.correction) {
+    hipLaunchKernelGGL(mean_prep_kernel, dim3((unsigned)a.rows), dim3(256), 0, stream, a);
+    if (hipError_t e0 = hipGetLastError(); e0 != hipSuccess) return e0;
+  }
+  hipLaunchKernelGGL(rank_tiles_kernel, dim3((unsigned)((a.rows + 255) / 256)), dim3(256), 0, stream, a);
+  if (hipError_t e0 = hipGetLastError(); e0 != hipSuccess) return e0;
+  hipLaunchKernelGGL(items_kernel, dim3(1), dim3(kItemsThreads), (size_t)nbins * sizeof(int), stream, a, nbins);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int items_cap = a.rows + a.extra_cap;
+  const dim3 info_grid((unsigned)((items_cap + 255) / 256));
+  if (fp8 && a.pair)
+    hipLaunchKernelGGL((item_info_kernel<true, true>), info_grid, dim3(256), 0, stream, a);
+  else if (fp8)
+    hipLaunchKernelGGL((item_info_kernel<true, false>), info_grid, dim3(256), 0, stream, a);
+  else if (a.pair)
+    hipLaunchKernelGGL((item_info_kernel<false, true>), info_grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((item_info_kernel<false, false>), info_grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const float* vbar, int max_kblocks,
                        hipStream_t stream) {
   AttnArgs a = a_in;
@@ -1567,60 +1649,33 @@ hipError_t launch_impl(const AttnArgs& a_in, bool fp8, const float* kbar, const 
   p.page_size = a.page_size;
   p.total_kblocks = a.total_kblocks;
   p.mt_cap = a.mt_cap;
-  if (a.total_kblocks > 0) {
-    const dim3 per_block((unsigned)a.total_kblocks, (unsigned)a.hkv);
-    const dim3 per_pair((unsigned)((a.total_kblocks + 1) / 2), (unsigned)a.hkv);
-    if (fp8 && a.pair) {
-      hipLaunchKernelGGL((vt_exact_kernel<true, true>), per_pair, dim3(256), 0, stream, p);
-    } else if (fp8) {
-      hipLaunchKernelGGL((vt_exact_kernel<true, false>), per_block, dim3(256), 0, stream, p);
-    } else if (a.pair) {
-      hipLaunchKernelGGL((vt_exact_kernel<false, true>), dim3((unsigned)((a.total_kblocks + 1) / 2), (unsigned)a.hkv),
-                         dim3(256), 0, stream, p);
-    } else {
-      hipLaunchKernelGGL((vt_exact_kernel<false, false>), per_block, dim3(256), 0, stream, p);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.correction) {
-      hipLaunchKernelGGL(vt_mean_kernel,
-                         dim3((unsigned)((max_kblocks + kBlk - 1) / kBlk), (unsigned)a.num_seqs, (unsigned)a.hkv),
-                         dim3(256), 0, stream, p);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
-  if (a.rows <= 0) return hipSuccess;
+  if (a.rows <= 0) return a.total_kblocks > 0 ? launch_prep(p, a, fp8, max_kblocks, stream) : hipSuccess;
   const int G = a.hq / a.hkv;
   a.slices = (G * kBlk + kWGRows - 1) / kWGRows;
   int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
   a.ncu = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int ncu = 0;
-    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0) a.ncu = ncu;
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0) a.ncu = ncu;
+  if (a.total_kblocks > 0) {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    SidePath* sp = nullptr;
+    e = side_path(dev, sp);
+    if (e == hipSuccess) e = hipEventRecord(sp->fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(sp->stream, sp->fork, 0);
+    if (e != hipSuccess) return e;
+    // from here on the caller's stream waits for the side stream's work, also on an error
+    e = launch_prep(p, a, fp8, max_kblocks, sp->stream);
+    hipError_t ej = hipEventRecord(sp->join, sp->stream);
+    if (e == hipSuccess && ej == hipSuccess) e = launch_items(a, fp8, max_kblocks, stream);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(stream, sp->join, 0);
+    if (e == hipSuccess) e = ej;
+  } else {
+    e = launch_items(a, fp8, max_kblocks, stream);
   }
-  const int nbins = min(max_kblocks + (max_kblocks + kBlk - 1) / kBlk + 1, kItemsMaxBins);
-  if (a.correction) {
-    hipLaunchKernelGGL(mean_prep_kernel, dim3((unsigned)a.rows), dim3(256), 0, stream, a);
-    if (hipError_t e0 = hipGetLastError(); e0 != hipSuccess) return e0;
-  }
-  hipLaunchKernelGGL(rank_tiles_kernel, dim3((unsigned)((a.rows + 255) / 256)), dim3(256), 0, stream, a);
-  if (hipError_t e0 = hipGetLastError(); e0 != hipSuccess) return e0;
-  hipLaunchKernelGGL(items_kernel, dim3(1), dim3(kItemsThreads), (size_t)nbins * sizeof(int), stream, a, nbins);
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int items_cap = a.rows + a.extra_cap;
-  const dim3 info_grid((unsigned)((items_cap + 255) / 256));
-  if (fp8 && a.pair)
-    hipLaunchKernelGGL((item_info_kernel<true, true>), info_grid, dim3(256), 0, stream, a);
-  else if (fp8)
-    hipLaunchKernelGGL((item_info_kernel<true, false>), info_grid, dim3(256), 0, stream, a);
-  else if (a.pair)
-    hipLaunchKernelGGL((item_info_kernel<false, true>), info_grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((item_info_kernel<false, false>), info_grid, dim3(256), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(((items_cap + 7) / 8) * 8 * a.slices);
   if (fp8 && a.pair)
     hipLaunchKernelGGL((attn_d128_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
