@@ -304,6 +304,40 @@ def test_repeat_runs_bit_identical():
     np.testing.assert_array_equal(ci_a, ci_b)
 
 
+def test_concurrent_calls_on_two_streams():
+    """fp2_prefill_run runs its V^T preparation on a second stream of the library's, forked from and
+    joined to the caller's stream by events that all calls on a device share (under a host lock): two
+    host threads driving two layers on two streams at once get, every time, what each layer gives alone."""
+    import threading
+    layers = [layer(workload(n)[0]) for n in ("varlen_p64", "fp8_varlen")]
+    ref = [L(0.5, True).clone() for L in layers]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in layers]
+    outs = [[] for _ in layers]
+    errors = []
+
+    def drive(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(16):
+                    outs[i].append(layers[i](0.5, True).clone())
+            streams[i].synchronize()
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=drive, args=(i,)) for i in range(len(layers))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(len(layers)):
+        assert len(outs[i]) == 16
+        for o in outs[i]:
+            assert torch.equal(o, ref[i])
+
+
 def test_page_shuffle_and_varlen_metamorphic():
     """Shuffled pages == identity pages (bit-identical); a varlen batch == each sequence alone."""
     cfg = SMALL["varlen_p64"]
