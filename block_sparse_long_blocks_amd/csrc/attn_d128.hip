@@ -552,11 +552,14 @@ struct Wave {
   // block is skipped, -inf and 0 when it is not; its B holds ones at k = 0
   // and 1 of every column; every other A element is finite and meets a zero
   // of B.  So the product adds cbs, or -inf, to each score of the key's row,
-  // and the rest of the tile is the plain one.
+  // and the rest of the tile is the plain one.  nsteps: the steps that hold
+  // a token below the diagonal (a row's last mean tile may end early); the
+  // PV work of later steps (regions 4 and 5) is skipped.
   template <bool MASKED, bool QK8, bool TWO = false, bool AUG = false, class Dma>
   __device__ __forceinline__ void tile(bf16x8 (&fr)[kRing], bool first, const uint8_t* Kt, const uint8_t* Vt,
                                        int off0, int off1, const int (&off8)[4], float scl, float scl2, Dma&& dma,
-                                       int mode, int tq, int tq2, int hf, float cbs, int J0, const uint32_t* kept) {
+                                       int mode, int tq, int tq2, int hf, float cbs, int J0, const uint32_t* kept,
+                                       int nsteps = NS) {
     static_assert(!(MASKED && AUG), "the weight MFMA is the plain schedule's mask");
     bf16x8 pp[2] = {qf[0], qf[0]}, pc[2];
     f32x16 s = f32x16{}, sn = f32x16{};
@@ -603,12 +606,16 @@ struct Wave {
       if (j == 0) region<1, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb, M[0], dma);
       if (j == 1) region<2, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, nb, M[1], dma);
       if (j == 2) region<3, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, TWO ? scl2 : scl, nb, M[2], dma);
-      if (j == 3) region<4, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, TWO ? scl2 : scl, nb, M[3], dma);
+      if (j == 3) {
+        if (AUG && nsteps <= 2) break;  // steps 2 and 3 hold no token that counts: PV(2), PV(3) and L go
+        region<4, true, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, TWO ? scl2 : scl, nb, M[3], dma);
+      }
       soft_close<MASKED>(st, s, (TWO && j >= NS / 2) ? scl2 : scl, first && j == 0, pc, M[j]);
       pp[0] = pc[0];
       pp[1] = pc[1];
     }
-    region<5, false, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, 0.f, 0u, dma);  // PV(3)
+    if (!AUG || nsteps > 3)
+      region<5, false, MASKED, QK8>(fr, sn, pp, st, s, Kt, Vt, off0, off1, off8, scl, 0.f, 0u, dma);  // PV(3)
   }
 };
 
@@ -1053,7 +1060,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
     } else if constexpr (PATH == kPathMean) {
       // mean tiles: the plain bf16 schedule with the weight MFMA (cbs: log2 B in score units)
       ws.tile<false, false, PAIR, true>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, 2, tq, 0, hf,
-                                        a.log2_block / sclt, j0, kept);
+                                        a.log2_block / sclt, j0, kept, min(Wave::NS, (dlo - j0 + 31) >> 5));
     } else if constexpr (PAIR) {
       // diagonal offsets of the two blocks (a lone block: its second half masked)
       const int qd = qpos0 + tq;
