@@ -390,6 +390,8 @@ def density_sweep(args, torch, lib, synth):
             row["corr_overhead"] = round(row["ms_run_corr"] / row["ms_run_nocorr"] - 1.0, 4)
             row["speedup_vs_dense_layer"] = round(dense_layer / row["ms_layer_corr"], 2)
             row["corr_flops_share"] = round(fl["corr"] / (fl["kept"] + fl["corr"]), 4)
+            # the overhead if a correction FLOP cost what an exact one does: corr / exact FLOPs
+            row["corr_over_exact_flops"] = round(fl["corr"] / fl["kept"], 4)
             log("sweep:", json.dumps(row))
             table.append(row)
         table.append(dict(dtype=dtype, target=1.0, density=1.0, nnz=fl_dense["causal_pairs"],
@@ -406,14 +408,15 @@ def density_sweep(args, torch, lib, synth):
     if args.sweep_out:
         with open(args.sweep_out, "w") as f:
             f.write("| dtype | density | tau | kept blocks per row (mean / max) | run ms (corr) | run ms (no corr) "
-                    "| ideal ms | no corr / ideal | corr overhead | corr share of FLOPs | layer ms (corr) "
-                    "| layer speedup vs dense |\n")
-            f.write("|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+                    "| ideal ms | no corr / ideal | corr overhead | corr share of FLOPs | corr / exact FLOPs "
+                    "| layer ms (corr) | layer speedup vs dense |\n")
+            f.write("|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
             for r in table:
                 f.write(f"| {r['dtype']} | {r['density']} | {r.get('tau', 'inf')} "
                         f"| {r.get('mean_row_blocks', '-')} / {r.get('max_row_blocks', '-')} | {r.get('ms_run_corr', '-')} "
                         f"| {r['ms_run_nocorr']} | {r['ideal_run_ms']} | {r['run_over_ideal']} "
                         f"| {r.get('corr_overhead', '-')} | {r.get('corr_flops_share', '-')} "
+                        f"| {r.get('corr_over_exact_flops', '-')} "
                         f"| {r.get('ms_layer_corr', r['ms_layer_nocorr'])} | {r.get('speedup_vs_dense_layer', 1.0)} |\n")
             f.write("\nChunked prefill: one 128-token query chunk after a 130944-token cached prefix "
                     "(8 CSR rows), fp2_prefill_run ms with mean correction, rows split into chunks or not:\n\n")
