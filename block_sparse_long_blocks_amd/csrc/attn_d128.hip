@@ -626,10 +626,11 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
-// PAIR: 64-token KV blocks under 128-token query blocks, two blocks (two CSR
-// entries) to a 128-key tile.
 // tile code paths of the attention kernel's loops
 enum : int { kPathPlain = 0, kPathMasked = 1, kPathMean = 2 };
+
+// PAIR: 64-token KV blocks under 128-token query blocks, two blocks (two CSR
+// entries) to a 128-key tile.
 
 template <bool FP8, bool PAIR>
 __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
@@ -1042,7 +1043,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
         j2v = __builtin_amdgcn_raw_buffer_load_b32(rcol, (idx + 3) * 4, 0, 0);
       }
     }
-    const int mode = idx >= nexact ? 2 : (masked_exact(j0, idx) ? 1 : 0);
+    const int mode = idx < nexact && masked_exact(j0, idx) ? 1 : 0;  // the masked path's mask: 1 diagonal
     // The issue arbiter serves the older wave of a SIMD first (waves 0-3,
     // which also issue the DMA): the younger waves 4-7 get the higher issue
     // priority until region 3 so that the two finish a tile closer together.
@@ -1059,7 +1060,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a) {
       ws.tile<false, FP8, PAIR>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, 0, tq, 0, hf, 0.f, 0, kept);
     } else if constexpr (PATH == kPathMean) {
       // mean tiles: the plain bf16 schedule with the weight MFMA (cbs: log2 B in score units)
-      ws.tile<false, false, PAIR, true>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, 2, tq, 0, hf,
+      ws.tile<false, false, PAIR, true>(fr, idx == 0, Kc, Vc, off0, off1, off8, sclt, sclt2, dma, 0, tq, 0, hf,
                                         a.log2_block / sclt, j0, kept, min(Wave::NS, (dlo - j0 + 31) >> 5));
     } else if constexpr (PAIR) {
       // diagonal offsets of the two blocks (a lone block: its second half masked)
