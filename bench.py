@@ -634,7 +634,8 @@ def main():
                                "sink columns, tau for 5% kept blocks, mean correction on",
                    "tau": bf["tau"], "density": round(bf["density"], 5), "nnz": bf["nnz"]},
         "roofline": {"bound": "mfma", "kernel": "attn_d128_kernel<false, false> (timed as fp2_prefill_run, which also launches "
-                               "the V^T, mean-token and work-item preparation kernels: ~0.19 ms, ~2.3% of the call)", "achieved": round(achieved, 2),
+                               "the V^T, mean-token and work-item preparation kernels, the first two beside the others "
+                               "on a second stream: ~0.03-0.07 ms, under 1% of the call)", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
                      "flops_per_launch": attn_flops,
