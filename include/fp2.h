@@ -262,7 +262,14 @@ size_t fp2_run_workspace_bytes(const fp2_batch *batch, int32_t num_q_heads, int3
  *                     holds at most this many exact tiles (still within the
  *                     256 extra items); < 0: rows are never split.  The
  *                     result does not depend on it beyond float32 rounding
- *                     order; other paths ignore it. */
+ *                     order; other paths ignore it.
+ * On the work-item path the V^T and mean-token preparation runs on a second
+ * stream the library keeps per device (created on the first call on that
+ * device, default priority, never destroyed): it starts after the work
+ * enqueued on `stream` before the call and `stream` waits for it before the
+ * attention kernel, so the call keeps the usual stream order.  The fork and
+ * join events are shared per device; a host lock serialises their use, so
+ * concurrent calls from several threads are safe. */
 fp2_status fp2_prefill_run(const fp2_batch *batch, const fp2_q *q, const fp2_kv *kv,
                            const int32_t *row_ptr, const int32_t *col_idx,
                            const float *kbar, const float *vbar,
