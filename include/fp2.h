@@ -269,7 +269,9 @@ size_t fp2_run_workspace_bytes(const fp2_batch *batch, int32_t num_q_heads, int3
  * enqueued on `stream` before the call and `stream` waits for it before the
  * attention kernel, so the call keeps the usual stream order.  The fork and
  * join events are shared per device; a host lock serialises their use, so
- * concurrent calls from several threads are safe. */
+ * concurrent calls from several threads are safe.  A device reset
+ * (hipDeviceReset) invalidates that stream: the library is not meant to be
+ * used across one. */
 fp2_status fp2_prefill_run(const fp2_batch *batch, const fp2_q *q, const fp2_kv *kv,
                            const int32_t *row_ptr, const int32_t *col_idx,
                            const float *kbar, const float *vbar,
