@@ -36,9 +36,12 @@
  *
  * Conventions for every entry point:
  *  - All device buffers are allocated and owned by the caller.  The library
- *    never allocates, frees or synchronises; it only enqueues kernels on the
- *    caller's stream (a hipStream_t passed as void*, NULL = default stream).
- *    Buffers must stay valid until the stream has passed the work.
+ *    never allocates device memory, frees or synchronises; it enqueues
+ *    kernels on the caller's stream (a hipStream_t passed as void*, NULL =
+ *    default stream), and fp2_prefill_run also on a second stream of its own
+ *    that it orders against the caller's (created with two events on the
+ *    first call on a device; see there).  Buffers must stay valid until the
+ *    stream has passed the work.
  *  - Arguments are checked on the host before anything is enqueued; on a
  *    failed check nothing is launched and the status says why
  *    (fp2_last_error() gives a message, per calling thread).
