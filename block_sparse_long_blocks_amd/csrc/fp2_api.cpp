@@ -1,6 +1,7 @@
 // C ABI of the library: host-side checks, then kernel launches on the
-// caller's stream.  No allocation, no synchronisation, no state besides the
-// per-thread error text.
+// caller's stream.  No device allocation and no synchronisation; this layer
+// keeps no state besides the per-thread error text (the prefill path's
+// second stream per device lives beside its kernels).
 #include <hip/hip_runtime_api.h>
 
 #include <cmath>
@@ -32,6 +33,24 @@ static fp2_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return FP2_OK;
   return fail(FP2_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
+
+// Kernels run on the device of the stream they are enqueued on, while the
+// library's per-device state (the prefill call's second stream and events,
+// the allocation-free call's scratch array, the bounds word) is taken for
+// the current device: a stream of another device is refused.  The NULL
+// stream is the current device's.  A handle the runtime cannot place (a
+// special stream handle) is left to the launch itself.
+static fp2_status check_stream(void* stream, const char* what) {
+  if (!stream) return FP2_OK;
+  int cur = 0;
+  hipDevice_t sdev = 0;
+  if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess)
+    return FP2_OK;
+  if (sdev != cur)
+    return fail(FP2_ERR_INVALID, std::string(what) + ": the stream belongs to device " + std::to_string(sdev) +
+                                     " but the current device is " + std::to_string(cur));
+  return FP2_OK;
+}
 }  // namespace fp2
 
 using namespace fp2;
@@ -45,6 +64,7 @@ fp2_status fp2_block_stats(const fp2_batch* batch, const fp2_kv* kv, float* kbar
   if (st != FP2_OK) return st;
   if ((st = check_kv(kv, batch, info)) != FP2_OK) return st;
   if (info.total_kblocks > 0 && (!kbar || !vbar)) return fail(FP2_ERR_INVALID, "kbar/vbar is NULL");
+  if ((st = check_stream(stream, "fp2_block_stats")) != FP2_OK) return st;
   if (hipError_t e = launch_check_pages(batch, kv, (hipStream_t)stream); e != hipSuccess)
     return hip_status(e, "fp2_block_stats bounds check");
   return hip_status(launch_block_stats(batch, kv, info, kbar, vbar, (hipStream_t)stream),
@@ -70,6 +90,7 @@ fp2_status fp2_block_stats_cached(const fp2_batch* batch, const fp2_kv* kv, floa
   if (refresh_prefix != 0 && refresh_prefix != 1) return fail(FP2_ERR_INVALID, "refresh_prefix must be 0 or 1");
   if (info.total_kblocks > 0 && (!kbar_cache || !vbar_cache))
     return fail(FP2_ERR_INVALID, "kbar_cache/vbar_cache is NULL");
+  if ((st = check_stream(stream, "fp2_block_stats_cached")) != FP2_OK) return st;
   if (hipError_t e = launch_check_pages(batch, kv, (hipStream_t)stream); e != hipSuccess)
     return hip_status(e, "fp2_block_stats_cached bounds check");
   return hip_status(launch_block_stats_cached(batch, kv, info, kbar_cache, vbar_cache, refresh_prefix,
@@ -87,6 +108,7 @@ fp2_status fp2_gather_block_stats(const fp2_batch* batch, const fp2_kv* kv, cons
     return fail(FP2_ERR_UNSUPPORTED, "the block stats cache needs page_size and the KV block to divide one another");
   if (info.total_kblocks > 0 && (!kbar_cache || !vbar_cache || !kbar || !vbar))
     return fail(FP2_ERR_INVALID, "a cache or output pointer is NULL");
+  if ((st = check_stream(stream, "fp2_gather_block_stats")) != FP2_OK) return st;
   if (hipError_t e = launch_check_pages(batch, kv, (hipStream_t)stream); e != hipSuccess)
     return hip_status(e, "fp2_gather_block_stats bounds check");
   return hip_status(launch_gather_stats(batch, kv, info, kbar_cache, vbar_cache, kbar, vbar, (hipStream_t)stream),
@@ -140,6 +162,7 @@ fp2_status fp2_plan_mask(const fp2_batch* batch, const fp2_q* q, int32_t num_kv_
   if (workspace_bytes < wneed)
     return fail(FP2_ERR_CAPACITY, "plan workspace " + std::to_string(workspace_bytes) + " < " +
                                       std::to_string(wneed) + " bytes");
+  if ((st = check_stream(stream, "fp2_plan_mask")) != FP2_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (info.total_qblocks == 0) return hip_status(launch_zero_plan(row_ptr, nnz, s), "fp2_plan_mask");
   return hip_status(launch_plan(batch, q, num_kv_heads, info, kbar, tau, row_ptr, col_idx, nnz,
@@ -158,6 +181,7 @@ fp2_status fp2_plan_mask_noalloc(const fp2_batch* batch, const fp2_q* q, int32_t
     return fail(FP2_ERR_CAPACITY, "this batch needs " + std::to_string(wneed) +
                                       " bytes of plan workspace; the allocation-free call holds at most " +
                                       std::to_string(kPlanScratchBytes) + " (use fp2_plan_mask)");
+  if ((st = check_stream(stream, "fp2_plan_mask_noalloc")) != FP2_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (info.total_qblocks == 0) return hip_status(launch_zero_plan(row_ptr, nnz, s), "fp2_plan_mask_noalloc");
   void* ws = nullptr;
@@ -191,6 +215,7 @@ fp2_status fp2_stage1(const fp2_batch* batch, const fp2_q* q, const fp2_kv* kv, 
   if (workspace_bytes < wneed)
     return fail(FP2_ERR_CAPACITY, "stage-1 workspace " + std::to_string(workspace_bytes) + " < " +
                                       std::to_string(wneed) + " bytes");
+  if ((st = check_stream(stream, "fp2_stage1")) != FP2_OK) return st;
   if (hipError_t e = launch_check_pages(batch, kv, (hipStream_t)stream); e != hipSuccess)
     return hip_status(e, "fp2_stage1 bounds check");
   return hip_status(launch_stage1(batch, q, kv, info, tau, kbar, vbar, row_ptr, col_idx, nnz, scores, workspace,
@@ -235,6 +260,7 @@ fp2_status fp2_prefill_run(const fp2_batch* batch, const fp2_q* q, const fp2_kv*
       return fail(FP2_ERR_CAPACITY, "run workspace " + std::to_string(workspace_bytes) + " < " +
                                         std::to_string(wneed) + " bytes");
   }
+  if ((st = check_stream(stream, "fp2_prefill_run")) != FP2_OK) return st;
   if (hipError_t e = launch_check_pages(batch, kv, (hipStream_t)stream); e != hipSuccess)
     return hip_status(e, "fp2_prefill_run bounds check");
   if (hipError_t e = launch_check_csr(batch, info, kv->num_kv_heads, row_ptr, col_idx, (hipStream_t)stream);

@@ -41,7 +41,8 @@
  *    default stream), and fp2_prefill_run also on a second stream of its own
  *    that it orders against the caller's (created with two events on the
  *    first call on a device; see there).  Buffers must stay valid until the
- *    stream has passed the work.
+ *    stream has passed the work.  The stream must belong to the current
+ *    device (FP2_ERR_INVALID otherwise; NULL is the current device's).
  *  - Arguments are checked on the host before anything is enqueued; on a
  *    failed check nothing is launched and the status says why
  *    (fp2_last_error() gives a message, per calling thread).
