@@ -113,7 +113,18 @@ def measured_traffic(workload, launch_flops):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_workload(name, tau, args, torch, lib, synth, corr=True, stats_cache=False):
+def baseline_sample(cfg, nqb, rows_wanted):
+    """The (KV head, query blocks) sample of the CPU-baseline leg: two KV heads, the last query block and
+    seeded random ones of each."""
+    import numpy as np
+    rng = np.random.default_rng(0)
+    heads = [0, cfg.hkv // 2]
+    per_head = max(1, rows_wanted // len(heads))
+    rows = sorted(set([nqb - 1] + rng.choice(nqb, per_head - 1, replace=False).tolist()))
+    return heads, rows
+
+
+def run_workload(name, tau, args, torch, lib, synth, corr=True, stats_cache=False, capture=None):
     log(f"generating {name} (tau={tau:.6g}) ...")
     t0 = time.time()
     w = synth.make(name, tau=tau)
@@ -199,48 +210,109 @@ def run_workload(name, tau, args, torch, lib, synth, corr=True, stats_cache=Fals
     # device memory of fp2_prefill_run's workspace against the paged K and V it serves
     res["run_workspace_mb"] = L.run_ws.numel() / 1e6
     res["kv_cache_mb"] = kv_bytes / 1e6
+    if capture is not None:
+        # the GPU's plan and the output rows of the CPU-baseline sample (capture = (heads, query blocks)),
+        # from the last sparse call, for the parity figures of that leg
+        heads, rows = capture
+        G, B = w.cfg.hq // w.cfg.hkv, w.cfg.block
+        rp, ci = L.csr_host()
+        res["capture"] = {"row_ptr": rp, "col_idx": ci,
+                          "out": {(g, i): L.out[i * B:(i + 1) * B, g * G:(g + 1) * G, :].float().cpu().numpy()
+                                  for g in heads for i in rows}}
     del L, batch, q, kv
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return w, res
 
 
-def cpu_baseline(w, tau, rows_wanted):
-    """The float64 oracle on a bounded sample of the same workload: stage 1 for the
-    sampled KV heads plus attention of the sampled (q-block, KV head) rows."""
-    import numpy as np
+def oracle_sample(w, tau, heads, rows, gpu_keep=None):
+    """The float64 oracle on a sample of a one-sequence workload: stage 1 for the KV heads in
+    heads, then attention with mean correction for the query blocks in rows of each (on the GPU's
+    mask gpu_keep[g] when given, else on the oracle's own).  Returns ({g: (s, thr, keep)},
+    {g: output rows}, dense-equivalent FLOPs of the attended rows)."""
     import oracle as O
     cfg = w.cfg
     B, G, d = cfg.block, cfg.hq // cfg.hkv, cfg.d
-    nqb = int(w.cu_qblocks[1])
-    rng = np.random.default_rng(0)
-    heads = [0, cfg.hkv // 2]
-    per_head = max(1, rows_wanted // len(heads))
-    cores = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    dense_flops = 0
+    masks, outs, dense_flops = {}, {}, 0
     for g in heads:
-        Q = O.decode_bf16(w.q[:, g * G:(g + 1) * G, :]) if cfg.dtype == "bf16" else None
-        K = O.decode_bf16(w.k_seq[0][:, g:g + 1, :])
-        V = O.decode_bf16(w.v_seq[0][:, g:g + 1, :])
+        qs = w.q_scale[:, g * G:(g + 1) * G] if cfg.dtype == "fp8" else None
+        ks = w.k_scale_seq[0][:, g:g + 1] if cfg.dtype == "fp8" else None
+        vs = w.v_scale_seq[0][:, g:g + 1] if cfg.dtype == "fp8" else None
+        Q, K, V = O.decode_sequence(cfg.dtype, B, w.q[:, g * G:(g + 1) * G, :], qs, w.k_seq[0][:, g:g + 1, :], ks,
+                                    w.v_seq[0][:, g:g + 1, :], vs)
         kbar, vbar = O.block_means(K, B), O.block_means(V, B)
         qbar = O.pooled_query_means(Q, B, G)
         s = O.block_scores(qbar, kbar, 0, B, d)
-        keep, _, _ = O.select_blocks(s, 0, B, tau)
-        rows = sorted(set([nqb - 1] + rng.choice(nqb, per_head - 1, replace=False).tolist()))
-        O.attend(Q, K, V, keep, B, True, kbar, vbar, rows=[(0, i) for i in rows])
+        keep, thr, _ = O.select_blocks(s, 0, B, tau)
+        masks[g] = (s[0], thr[0], keep[0])
+        run_keep = keep if gpu_keep is None else gpu_keep[g:g + 1]
+        outs[g], _ = O.attend(Q, K, V, run_keep, B, True, kbar, vbar, rows=[(0, i) for i in rows])
         for i in rows:
             ntok = min(B, Q.shape[0] - i * B)
-            first = i * B
-            dense_flops += 4 * d * G * sum(first + t + 1 for t in range(ntok))
+            dense_flops += 4 * d * G * sum(i * B + t + 1 for t in range(ntok))
         del Q, K, V
+    return masks, outs, dense_flops
+
+
+def parity_figures(w, heads, rows, masks, outs, capture, gpu_keep, tol):
+    """Mask and output parity of a GPU run against oracle_sample's results (see cpu_baseline)."""
+    import numpy as np
+    import oracle as O
+    B = w.cfg.block
+    ties = flips = hard = onnz = gnnz = 0
+    for g in heads:
+        s_g, thr_g, keep_g = masks[g]
+        with np.errstate(invalid="ignore"):
+            tie = np.abs(s_g.astype(np.float64) - thr_g.astype(np.float64)[:, None]) <= O.NEAR_TIE
+        diff = keep_g != gpu_keep[g]
+        ties += int(tie.sum())
+        flips += int(diff.sum())
+        hard += int((diff & ~tie).sum())
+        onnz += int(keep_g.sum())
+        gnnz += int(gpu_keep[g].sum())
+    err = 0.0
+    for g in heads:
+        for i in rows:
+            ref = outs[g][i * B:(i + 1) * B]
+            err = max(err, float(np.abs(capture["out"][(g, i)][:ref.shape[0]] - ref).max()))
+    return {"kv_heads": heads, "csr_rows": len(heads) * masks[heads[0]][2].shape[0], "oracle_nnz": onnz,
+            "gpu_nnz": gnnz, "near_ties": ties, "mask_flips": flips, "flips_off_near_tie": hard,
+            "query_blocks_checked": len(heads) * len(rows), "out_max_abs_err": float(f"{err:.3g}"), "out_tol": tol,
+            "note": "masks over every row of the sampled KV heads (near-tie: |s - threshold| <= 1e-5); "
+                    "bf16 output of the sampled rows against the float64 oracle run on the GPU plan"}
+
+
+def gpu_keep_of(w, capture):
+    import oracle as O
+    return O.keep_from_csr(capture["row_ptr"], capture["col_idx"], w.cfg.hkv, [int(w.cu_qblocks[1])],
+                           [int(w.cu_kblocks[1])])[0]
+
+
+def cpu_baseline(w, tau, rows_wanted, capture=None):
+    """The float64 oracle on a bounded sample of the same workload: stage 1 for the
+    sampled KV heads plus attention of the sampled (q-block, KV head) rows.
+
+    With capture (the GPU's CSR and its output rows of the same sample, from run_workload),
+    attention runs on the GPU's mask (the output bar is against the oracle on the same mask)
+    and the leg also reports, untimed, how the two masks compare over every row of the
+    sampled heads (near-ties within NEAR_TIE of the threshold, flips, flips off a near-tie)
+    and the largest output difference over the sampled rows."""
+    heads, rows = baseline_sample(w.cfg, int(w.cu_qblocks[1]), rows_wanted)
+    gpu_keep = gpu_keep_of(w, capture) if capture is not None else None
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    masks, outs, dense_flops = oracle_sample(w, tau, heads, rows, gpu_keep)
     dt = time.perf_counter() - t0
-    return dict(value=dense_flops / dt / 1e12, unit="TFLOP/s (dense-equivalent)", cores=cores,
-                kind="oracle", seconds=dt,
-                sample=f"float64 numpy oracle, c128k_bf16: block means + pooled scores + threshold for "
-                       f"KV heads {heads}, then attention with mean correction for {per_head} query blocks "
-                       f"per head (incl. the last); dense-equivalent FLOPs of the sampled rows / wall time",
-                blas_threads=os.environ.get("OMP_NUM_THREADS", "default"))
+    res = dict(value=dense_flops / dt / 1e12, unit="TFLOP/s (dense-equivalent)", cores=cores,
+               kind="oracle", seconds=dt,
+               sample=f"float64 numpy oracle, {w.cfg.name}: block means + pooled scores + threshold for "
+                      f"KV heads {heads}, then attention with mean correction for {len(rows)} query blocks "
+                      f"per head (incl. the last){' on the GPU plan' if capture is not None else ''}; "
+                      f"dense-equivalent FLOPs of the sampled rows / wall time",
+               blas_threads=os.environ.get("OMP_NUM_THREADS", "default"))
+    if capture is not None:
+        res["parity_sample"] = parity_figures(w, heads, rows, masks, outs, capture, gpu_keep, 1e-2)
+    return res
 
 
 def sweep_config(dtype):
@@ -609,7 +681,9 @@ def main():
         tile_study(args, torch, lib, synth)
         return
     taus = load_taus()
-    w, bf = run_workload("c128k_bf16", taus["c128k_bf16"]["tau"], args, torch, lib, synth)
+    cfg128 = synth.CONFIGS["c128k_bf16"]
+    sample = None if args.no_cpu else baseline_sample(cfg128, cfg128.seqlens[0] // cfg128.block, args.cpu_rows)
+    w, bf = run_workload("c128k_bf16", taus["c128k_bf16"]["tau"], args, torch, lib, synth, capture=sample)
     fl = bf["flops"]
     t_attn = bf["stages_ms"]["prefill_run"] * 1e-3
     attn_flops = fl["kept"] + fl["corr"]
@@ -653,11 +727,20 @@ def main():
         out["speedup_vs_dense"] = round(bf["speedup_vs_dense"], 2)
     if not args.no_cpu:
         log("timing the CPU oracle on a sample ...")
-        out["cpu_baseline"] = cpu_baseline(w, bf["tau"], args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w, bf["tau"], args.cpu_rows, bf.get("capture"))
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 5)
     del w
     if not args.no_fp8:
-        w8, f8 = run_workload("c128k_fp8", taus["c128k_fp8"]["tau"], args, torch, lib, synth)
+        cfg8 = synth.CONFIGS["c128k_fp8"]
+        sample8 = None if args.no_cpu else baseline_sample(cfg8, cfg8.seqlens[0] // cfg8.block, args.cpu_rows // 8)
+        w8, f8 = run_workload("c128k_fp8", taus["c128k_fp8"]["tau"], args, torch, lib, synth, capture=sample8)
+        parity8 = None
+        if sample8 is not None:
+            # untimed: the same parity figures for the e4m3 workload on a smaller sample
+            log("oracle parity sample of the fp8 workload ...")
+            keep8 = gpu_keep_of(w8, f8["capture"])
+            m8, o8, _ = oracle_sample(w8, f8["tau"], sample8[0], sample8[1], keep8)
+            parity8 = parity_figures(w8, sample8[0], sample8[1], m8, o8, f8["capture"], keep8, 4e-2)
         del w8
         fl8 = f8["flops"]
         t8 = f8["stages_ms"]["prefill_run"] * 1e-3
@@ -671,6 +754,8 @@ def main():
                       "tau": f8["tau"], "density": round(f8["density"], 5),
                       "mfma_frac_attn": round(busy / t8, 4),
                       "run_workspace_mb": round(f8["run_workspace_mb"], 1), "kv_cache_mb": round(f8["kv_cache_mb"], 1)}
+        if parity8 is not None:
+            out["fp8"]["parity_sample"] = parity8
         if "dense_ms_per_layer" in f8:
             out["fp8"]["dense_ms_per_layer"] = round(f8["dense_ms_per_layer"], 3)
             out["fp8"]["speedup_vs_dense"] = round(f8["speedup_vs_dense"], 2)
