@@ -44,6 +44,9 @@ fp2_status check_index_range(const BatchInfo& info, int num_kv_heads);
 size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads);
 // fp2_stage1: the plan workspace followed by the pooled query means
 // (float32 [Hkv, total_qblocks, d])
+// the fused stage 1's workspace: the plan workspace, the pooled query means
+// (256-byte aligned) and the select pass's claim counter (its own 256 bytes)
+constexpr size_t kStage1TicketBytes = 256;
 size_t stage1_workspace_bytes(const BatchInfo& info, int num_kv_heads, int head_dim);
 // fp2_prefill_run runs the DMA kernel on V^T tiles for d = 128 and query
 // blocks of 128 over KV blocks of 128 or of 64 (two to a tile), bf16 or e4m3,

@@ -159,7 +159,7 @@ size_t plan_workspace_bytes(const BatchInfo& info, int num_kv_heads) {
 size_t stage1_workspace_bytes(const BatchInfo& info, int num_kv_heads, int head_dim) {
   const size_t plan = plan_workspace_bytes(info, num_kv_heads);
   const size_t qbar = ((size_t)info.total_qblocks * num_kv_heads * head_dim * 4 + 255) & ~size_t(255);
-  return plan + qbar;
+  return plan + qbar + kStage1TicketBytes;
 }
 
 RunLayout run_layout(const BatchInfo& info, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

@@ -138,24 +138,24 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
   for (int w = 1; w < kThreads / 64; ++w) rmax = fmaxf(rmax, s_wmax[w]);
   const float thr = rmax - a.tau;
 
-  // ---- keep bitmask (forced: block 0 and the diagonal run) and kept count
+  // ---- keep bitmask (forced: block 0 and the diagonal run) and kept count:
+  // one ballot per 64 KV blocks, lane l deciding block J0 + l, lanes 0 and 1
+  // storing the two 32-bit words
   const int row = g * a.total_qblocks + qb;
   int cnt = 0;
-  for (int w = t; w < a.W; w += kThreads) {
-    uint32_t word = 0;
-    const int j0 = w * 32;
-    for (int b = 0; b < 32; ++b) {
-      const int J = j0 + b;
-      if (J <= diag && (s_scores[J] >= thr || J == 0 || J >= dlo)) word |= 1u << b;
-    }
-    a.bits[(int64_t)row * a.W + w] = word;
-    cnt += __popc(word);
+  uint32_t* brow = a.bits + (int64_t)row * a.W;
+  for (int J0 = 64 * (t >> 6); J0 < 32 * a.W; J0 += kThreads) {
+    const int J = J0 + lane;
+    const bool keep = J <= diag && (s_scores[J] >= thr || J == 0 || J >= dlo);
+    const uint64_t m = __ballot(keep);
+    const int w = (J0 >> 5) + lane;
+    if (lane < 2 && w < a.W) brow[w] = (uint32_t)(m >> (32 * lane));
+    cnt += __popcll(m);
   }
   if (a.scores_out) {
     float* so = a.scores_out + (int64_t)row * a.max_kblocks;
     for (int J = t; J < a.max_kblocks; J += kThreads) so[J] = J <= diag ? s_scores[J] : -INFINITY;
   }
-  cnt = wave_sum_i(cnt);
   if ((t & 63) == 0) s_wcnt[t >> 6] = cnt;
   __syncthreads();
   if (t == 0) {
@@ -165,132 +165,149 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(PlanArgs a) {
   }
 }
 
-// Fused stage 1, selection pass: the pooled means of up to QT (<= kMaxQT)
-// consecutive query blocks of one KV head, scored against their sequence's
-// kbar rows with each kbar row read once for all of them (the scores of one
-// (query block, KV block) pair are summed exactly as score_select_kernel
-// sums them, so the CSR is the same bit for bit), then each row's maximum,
-// threshold, keep bitmask and count as there.
+// Fused stage 1, selection pass: work items of up to QT (<= kMaxQT)
+// consecutive query blocks of one KV head, their pooled means scored against
+// the sequence's kbar rows with each kbar row read once for all of them (the
+// scores of one (query block, KV block) pair are summed exactly as
+// score_select_kernel sums them, so the CSR is the same bit for bit), then
+// each row's maximum, threshold, keep bitmask and count as there.  A grid of
+// at most kSelectMaxWorkgroups claims the items, latest query blocks first.
 #ifndef FP2_MAX_QT
 #define FP2_MAX_QT 8
 #endif
 constexpr int kMaxQT = FP2_MAX_QT;
+constexpr int kSelectMaxWorkgroups = 2048;  // 8 per CU of a 256-CU part
 __global__ __launch_bounds__(kThreads) void select_tiled_kernel(PlanArgs a, int QT) {
   extern __shared__ float s_sc[];  // [QT][max_kblocks]
   __shared__ int s_seq[kMaxQT], s_diag[kMaxQT], s_dlo[kMaxQT];
   __shared__ float s_q[kMaxQT][128];
   __shared__ float s_wmax[kMaxQT][kThreads / 64];
   __shared__ int s_wcnt[kMaxQT][kThreads / 64];
-  const int g = blockIdx.y;
-  const int qb0 = blockIdx.x * QT;
-  const int nrows = min(QT, a.total_qblocks - qb0);
+  __shared__ int s_item;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  if (t < nrows) {
-    const int qb = qb0 + t;
-    const int s = find_seq(a.cu_qblocks, a.num_seqs, qb);
-    const int I = qb - a.cu_qblocks[s];
-    const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
-    const int P = a.seqlens_k[s] - n;
-    const int ntok = min(a.qblock, n - I * a.qblock);
-    s_seq[t] = s;
-    s_dlo[t] = (P + I * a.qblock) / a.kvblock;
-    s_diag[t] = (P + I * a.qblock + ntok - 1) / a.kvblock;
-  }
-  for (int i = t; i < nrows * a.d; i += kThreads)
-    s_q[i / a.d][i % a.d] = a.qbar[((int64_t)g * a.total_qblocks + qb0 + i / a.d) * a.d + i % a.d];
-  __syncthreads();
+  // Work items (query tile, KV head) in descending tile order, claimed
+  // through a counter until none is left: rows late in a sequence score many
+  // more KV blocks than early ones, so the heaviest go first and every
+  // workgroup keeps claiming until the list is done, however the hardware
+  // placed the workgroups on the CUs.
+  const int ntiles = (a.total_qblocks + QT - 1) / QT;
+  const int nitems = ntiles * a.hkv;
+  for (;;) {
+    __syncthreads();  // the previous item's LDS reads are done
+    if (t == 0) s_item = atomicAdd(a.ticket, 1);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= nitems) break;
+    const int g = item % a.hkv;
+    const int qb0 = (ntiles - 1 - item / a.hkv) * QT;
+    const int nrows = min(QT, a.total_qblocks - qb0);
+    if (t < nrows) {
+      const int qb = qb0 + t;
+      const int s = find_seq(a.cu_qblocks, a.num_seqs, qb);
+      const int I = qb - a.cu_qblocks[s];
+      const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
+      const int P = a.seqlens_k[s] - n;
+      const int ntok = min(a.qblock, n - I * a.qblock);
+      s_seq[t] = s;
+      s_dlo[t] = (P + I * a.qblock) / a.kvblock;
+      s_diag[t] = (P + I * a.qblock + ntok - 1) / a.kvblock;
+    }
+    for (int i = t; i < nrows * a.d; i += kThreads)
+      s_q[i / a.d][i % a.d] = a.qbar[((int64_t)g * a.total_qblocks + qb0 + i / a.d) * a.d + i % a.d];
+    __syncthreads();
 
-  const int lpb = a.d / 8;  // lanes sharing a kbar row, 8 floats each
-  const int bpw = 64 / lpb;
-  const int sub = lane % lpb;
-  constexpr int UJ = 4;
-  const int jstep = (kThreads / 64) * bpw;
-  // runs of rows from one sequence (a tile crosses a sequence boundary rarely)
-  for (int i0 = 0; i0 < nrows;) {
-    const int s = s_seq[i0];
-    int i1 = i0, jmax = 0;
-    while (i1 < nrows && s_seq[i1] == s) jmax = max(jmax, s_diag[i1++]);
-    float qv[kMaxQT][8];
-#pragma unroll
-    for (int i = 0; i < kMaxQT; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[i][e] = i0 + i < i1 ? s_q[i0 + i][8 * sub + e] : 0.f;
-    const float* kb = a.kbar + ((int64_t)g * a.total_kblocks + a.cu_kblocks[s]) * a.d;
-    for (int J0 = wave * bpw; J0 <= jmax; J0 += UJ * jstep) {
-      f32x4 k0[UJ], k1[UJ];
-#pragma unroll
-      for (int u = 0; u < UJ; ++u) {
-        const int J = J0 + u * jstep + lane / lpb;
-        k0[u] = k1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (J <= jmax) {
-          const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (int64_t)J * a.d + 8 * sub);
-          k0[u] = kr[0];
-          k1[u] = kr[1];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UJ; ++u) {
-        const int J = J0 + u * jstep + lane / lpb;
-#pragma unroll
-        for (int i = 0; i < kMaxQT; ++i) {
-          if (i0 + i >= i1) break;
-          float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p0 = fmaf(qv[i][e], k0[u][e], p0);
-            p1 = fmaf(qv[i][4 + e], k1[u][e], p1);
+    const int lpb = a.d / 8;  // lanes sharing a kbar row, 8 floats each
+    const int bpw = 64 / lpb;
+    const int sub = lane % lpb;
+    constexpr int UJ = 4;
+    const int jstep = (kThreads / 64) * bpw;
+    // runs of rows from one sequence (a tile crosses a sequence boundary rarely)
+    for (int i0 = 0; i0 < nrows;) {
+      const int s = s_seq[i0];
+      int i1 = i0, jmax = 0;
+      while (i1 < nrows && s_seq[i1] == s) jmax = max(jmax, s_diag[i1++]);
+      float qv[kMaxQT][8];
+      #pragma unroll
+      for (int i = 0; i < kMaxQT; ++i)
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) qv[i][e] = i0 + i < i1 ? s_q[i0 + i][8 * sub + e] : 0.f;
+      const float* kb = a.kbar + ((int64_t)g * a.total_kblocks + a.cu_kblocks[s]) * a.d;
+      for (int J0 = wave * bpw; J0 <= jmax; J0 += UJ * jstep) {
+        f32x4 k0[UJ], k1[UJ];
+        #pragma unroll
+        for (int u = 0; u < UJ; ++u) {
+          const int J = J0 + u * jstep + lane / lpb;
+          k0[u] = k1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (J <= jmax) {
+            const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (int64_t)J * a.d + 8 * sub);
+            k0[u] = kr[0];
+            k1[u] = kr[1];
           }
-          const float p = row_sum(p0 + p1, lpb);
-          if (sub == 0 && J <= s_diag[i0 + i]) s_sc[(i0 + i) * a.max_kblocks + J] = p * a.scale;
+        }
+        #pragma unroll
+        for (int u = 0; u < UJ; ++u) {
+          const int J = J0 + u * jstep + lane / lpb;
+          #pragma unroll
+          for (int i = 0; i < kMaxQT; ++i) {
+            if (i0 + i >= i1) break;
+            float p0 = 0.f, p1 = 0.f;
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              p0 = fmaf(qv[i][e], k0[u][e], p0);
+              p1 = fmaf(qv[i][4 + e], k1[u][e], p1);
+            }
+            const float p = row_sum(p0 + p1, lpb);
+            if (sub == 0 && J <= s_diag[i0 + i]) s_sc[(i0 + i) * a.max_kblocks + J] = p * a.scale;
+          }
         }
       }
+      i0 = i1;
     }
-    i0 = i1;
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // per row: maximum, threshold, keep bitmask (forced: block 0 and the
-  // diagonal run), kept count; all waves on each row in turn
-  for (int i = 0; i < nrows; ++i) {
-    const int diag = s_diag[i];
-    const float* sc = s_sc + i * a.max_kblocks;
-    float lmax = -INFINITY;
-    for (int J = t; J <= diag; J += kThreads) lmax = fmaxf(lmax, sc[J]);
-    lmax = wave_max(lmax);
-    if (lane == 0) s_wmax[i][wave] = lmax;
-  }
-  __syncthreads();
-  for (int i = 0; i < nrows; ++i) {
-    const int diag = s_diag[i], dlo = s_dlo[i];
-    const float* sc = s_sc + i * a.max_kblocks;
-    float rmax = s_wmax[i][0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) rmax = fmaxf(rmax, s_wmax[i][w]);
-    const float thr = rmax - a.tau;
-    const int row = g * a.total_qblocks + qb0 + i;
-    int cnt = 0;
-    for (int w = t; w < a.W; w += kThreads) {
-      uint32_t word = 0;
-      const int j0 = w * 32;
-      for (int b = 0; b < 32; ++b) {
-        const int J = j0 + b;
-        if (J <= diag && (sc[J] >= thr || J == 0 || J >= dlo)) word |= 1u << b;
+    // per row: maximum, threshold, keep bitmask (forced: block 0 and the
+    // diagonal run), kept count; all waves on each row in turn
+    for (int i = 0; i < nrows; ++i) {
+      const int diag = s_diag[i];
+      const float* sc = s_sc + i * a.max_kblocks;
+      float lmax = -INFINITY;
+      for (int J = t; J <= diag; J += kThreads) lmax = fmaxf(lmax, sc[J]);
+      lmax = wave_max(lmax);
+      if (lane == 0) s_wmax[i][wave] = lmax;
+    }
+    __syncthreads();
+    for (int i = 0; i < nrows; ++i) {
+      const int diag = s_diag[i], dlo = s_dlo[i];
+      const float* sc = s_sc + i * a.max_kblocks;
+      float rmax = s_wmax[i][0];
+      #pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) rmax = fmaxf(rmax, s_wmax[i][w]);
+      const float thr = rmax - a.tau;
+      const int row = g * a.total_qblocks + qb0 + i;
+      // one ballot per 64 KV blocks: lane l decides block J0 + l, lanes 0 and
+      // 1 store the two 32-bit words
+      int cnt = 0;
+      uint32_t* brow = a.bits + (int64_t)row * a.W;
+      for (int J0 = 64 * wave; J0 < 32 * a.W; J0 += kThreads) {
+        const int J = J0 + lane;
+        const bool keep = J <= diag && (sc[J] >= thr || J == 0 || J >= dlo);
+        const uint64_t m = __ballot(keep);
+        const int w = (J0 >> 5) + lane;
+        if (lane < 2 && w < a.W) brow[w] = (uint32_t)(m >> (32 * lane));
+        cnt += __popcll(m);
       }
-      a.bits[(int64_t)row * a.W + w] = word;
-      cnt += __popc(word);
+      if (a.scores_out) {
+        float* so = a.scores_out + (int64_t)row * a.max_kblocks;
+        for (int J = t; J < a.max_kblocks; J += kThreads) so[J] = J <= diag ? sc[J] : -INFINITY;
+      }
+      if (lane == 0) s_wcnt[i][wave] = cnt;
     }
-    if (a.scores_out) {
-      float* so = a.scores_out + (int64_t)row * a.max_kblocks;
-      for (int J = t; J < a.max_kblocks; J += kThreads) so[J] = J <= diag ? sc[J] : -INFINITY;
+    __syncthreads();
+    if (t < nrows) {
+      int tot = 0;
+      for (int w = 0; w < kThreads / 64; ++w) tot += s_wcnt[t][w];
+      a.counts[g * a.total_qblocks + qb0 + t] = tot;
     }
-    cnt = wave_sum_i(cnt);
-    if (lane == 0) s_wcnt[i][wave] = cnt;
-  }
-  __syncthreads();
-  if (t < nrows) {
-    int tot = 0;
-    for (int w = 0; w < kThreads / 64; ++w) tot += s_wcnt[t][w];
-    a.counts[g * a.total_qblocks + qb0 + t] = tot;
   }
 }
 
@@ -374,6 +391,9 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(StatsArgs sa, PlanArgs a
   __shared__ float red_v[kThreads][N + 1];
   __shared__ float s_qbar[128];
   __shared__ int s_pg[kPoolMaxPages];
+  // the select pass's claim counter (it runs after this launch), cleared
+  // ahead of the bounds guard so that the select pass always runs whole
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.ticket = 0;
   FP2_BOUNDS_GUARD(sa.dbg);
   const int b = blockIdx.x;
   if (b < sa.total_kblocks) {
@@ -437,6 +457,7 @@ PlanArgs plan_args(const fp2_batch* b, const fp2_q* q, int hkv, const BatchInfo&
   a.counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + (((size_t)rows * W * 4 + 255) & ~size_t(255)));
   a.scores_out = scores;
   a.qbar = nullptr;
+  a.ticket = nullptr;
   a.tau = tau;
   a.scale = 1.0f / sqrtf((float)q->head_dim);
   a.num_seqs = b->num_seqs;
@@ -463,7 +484,9 @@ hipError_t launch_select(const PlanArgs& a, int dtype, bool pooled, int32_t* row
     // query blocks per workgroup: score rows of QT x max_kblocks floats in LDS (<= 64 KB)
     int QT = kMaxQT;
     while (QT > 1 && (size_t)QT * lds > (size_t)(64 << 10)) QT >>= 1;
-    const dim3 tgrid((unsigned)((a.total_qblocks + QT - 1) / QT), (unsigned)a.hkv);
+    // enough workgroups to fill the device; each claims items until none is left
+    const int nitems = ((a.total_qblocks + QT - 1) / QT) * a.hkv;
+    const dim3 tgrid((unsigned)std::min(nitems, kSelectMaxWorkgroups));
     hipLaunchKernelGGL(select_tiled_kernel, tgrid, dim3(kThreads), (size_t)QT * lds, stream, a, QT);
   } else if (dtype == FP2_BF16) {
     hipLaunchKernelGGL((score_select_kernel<2, false>), grid, dim3(kThreads), lds, stream, a);
@@ -494,6 +517,8 @@ hipError_t launch_stage1(const fp2_batch* b, const fp2_q* q, const fp2_kv* kv, c
   const int hkv = kv->num_kv_heads;
   PlanArgs a = plan_args(b, q, hkv, info, kbar, tau, scores, workspace);
   a.qbar = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan_workspace_bytes(info, hkv));
+  a.ticket = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + stage1_workspace_bytes(info, hkv, q->head_dim) -
+                                        kStage1TicketBytes);
   const StatsArgs sa = stats_args(b, kv, info, kbar, vbar);
   const int64_t nwg = info.total_kblocks + info.total_qblocks * hkv;
   if (nwg > 0) {

@@ -227,6 +227,7 @@ struct PlanArgs {
   int32_t* counts;      // [rows]
   float* scores_out;    // optional [rows, max_kblocks]
   float* qbar;          // fused stage 1: pooled query means [Hkv, total_qblocks, d]
+  int32_t* ticket;      // fused stage 1: the select pass's work-item claim counter
   float tau, scale;
   int num_seqs, hq, hkv, d, total_qblocks, total_kblocks, W, max_kblocks;
   int qblock, kvblock;  // query block and KV block tokens (kvblock divides qblock)

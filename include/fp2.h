@@ -218,7 +218,8 @@ fp2_status fp2_plan_mask_noalloc(const fp2_batch *batch, const fp2_q *q, int32_t
  * the pooled means against kbar (both held in L2) and compacts the CSR.
  *   kbar, vbar   device float32 [Hkv, total_kblocks, d] (outputs)
  *   workspace    device scratch of fp2_stage1_workspace_bytes() bytes: the
- *                plan workspace followed by the pooled query means
+ *                plan workspace, the pooled query means and 256 bytes for
+ *                the selection pass's work counter (cleared by the call)
  * Other arguments, limits and errors as fp2_block_stats and fp2_plan_mask
  * (the query and KV dtypes and head sizes must agree). */
 size_t fp2_stage1_workspace_bytes(const fp2_batch *batch, int32_t num_kv_heads, int32_t head_dim);

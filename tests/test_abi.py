@@ -79,11 +79,12 @@ def test_sizes_and_counts():
 
 def test_stage1_sizes_and_checks():
     """fp2_stage1: its workspace is the plan workspace plus float32 pooled query means
-    [Hkv, total_qblocks, d] (256-byte aligned); its checks are those of the two calls it fuses."""
+    [Hkv, total_qblocks, d] (256-byte aligned) plus 256 bytes for the selection pass's work
+    counter; its checks are those of the two calls it fuses."""
     b = _batch([1000, 256], [1000, 128])
     plan = lib.fp2_plan_workspace_bytes(b, 3)
     qbar = 3 * (8 + 1) * 128 * 4
-    assert lib.fp2_stage1_workspace_bytes(b, 3, 128) == plan + ((qbar + 255) & ~255)
+    assert lib.fp2_stage1_workspace_bytes(b, 3, 128) == plan + ((qbar + 255) & ~255) + 256
     f32 = torch.zeros(16)
     i32 = torch.zeros(64, dtype=torch.int32)
     ws = torch.zeros(1 << 16, dtype=torch.uint8)
